@@ -1,0 +1,264 @@
+/*
+ * mnb_oracle.c -- plain, slow, obviously-correct CPU oracle for the block-wise
+ * int4 weight-only matmul in the ONNX MatMulNBits layout.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  It shares no code,
+ * header, table or constant with the HIP library under block_wise_int4_amd/,
+ * and the product path never calls it.
+ *
+ * Everything is computed in IEEE-754 binary64, in the order the definitions
+ * state, with no blocking, fusion or reordering.
+ *
+ * Sources (web pages, cited by title and item):
+ *  [FMT]  onnx-runtime-ep-cuda 0.1.0-dev.6, src/kernels/marlin_gemm.rs --
+ *         module doc, section "ONNX MatMulNBits int4 format (input to the
+ *         repack)": Y[M,N] = A[M,K] . dequant(B)^T with
+ *         dequant(B)[n,k] = (code[n,k] - zp[n,k/group]) * scale[n,k/group];
+ *         packed [N, k_blocks, group/2], low nibble for even k; zero points
+ *         [N, ceil(k_blocks/2)], low nibble for even block; default zp 8.
+ *  [DQ]   onnx-runtime-ep-cuda 0.1.0-dev.3, src/kernels/matmul_nbits.rs --
+ *         kernel matmul_nbits_dequant_f32 (the same indexing written as a
+ *         dequantize-to-dense step) and the f64 dequant-and-matmul oracle
+ *         loop of test fp16_gemv_matches_dequant_reference.
+ *  [SILU] ferrox-cuda gpu.rs -- kernel silu_mul_f32: silu(g) * u with
+ *         silu(x) = x / (1 + e^-x); matmul_nbits.rs (dev.3) --
+ *         gate_up_silu_f32 states the same function in a two-branch form.
+ *
+ * Parity pins for every function live in tests/test_oracle.py (worked
+ * examples, exhaustive nibble decode, pack/unpack identity, code==zp gives
+ * zero, exact-rational brute force, integer special case, fp16 decode against
+ * numpy for all 65536 bit patterns, silu against scipy's expit).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* ---- scalar decoding --------------------------------------------------- */
+
+/* IEEE-754 binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction
+ * bits.  Exponent 0 = zero/subnormal (fraction * 2^-24), exponent 31 =
+ * infinity (fraction 0) or NaN. */
+double oracle_f16_to_f64(uint16_t h)
+{
+    const int sign = (h >> 15) & 1;
+    const int expo = (h >> 10) & 31;
+    const int frac = h & 1023;
+    double v;
+    if (expo == 0) {
+        v = ldexp((double)frac, -24);
+    } else if (expo == 31) {
+        v = frac == 0 ? INFINITY : NAN;
+    } else {
+        v = ldexp((double)(1024 + frac), expo - 25);
+    }
+    return sign ? -v : v;
+}
+
+void oracle_decode_f16(const uint16_t* h, int64_t count, double* out)
+{
+    for (int64_t i = 0; i < count; ++i) out[i] = oracle_f16_to_f64(h[i]);
+}
+
+void oracle_decode_f32(const float* f, int64_t count, double* out)
+{
+    for (int64_t i = 0; i < count; ++i) out[i] = (double)f[i];
+}
+
+/* ---- the format [FMT] -------------------------------------------------- */
+
+static int64_t k_blocks_of(int64_t K, int64_t g) { return (K + g - 1) / g; }
+static int64_t zp_row_bytes_of(int64_t kb) { return (kb + 1) / 2; }
+
+/* code[n,k]: byte (n*k_blocks + k/g) * (g/2) + (k mod g)/2, low nibble for
+ * even (k mod g), high nibble for odd. */
+int oracle_code(const uint8_t* packed, int64_t n, int64_t k, int64_t K, int64_t g)
+{
+    const int64_t kb = k_blocks_of(K, g);
+    const int64_t blob = g / 2;
+    const int64_t block = k / g;
+    const int64_t within = k % g;
+    const uint8_t byte = packed[(n * kb + block) * blob + within / 2];
+    return (within % 2 == 0) ? (byte & 15) : (byte >> 4);
+}
+
+/* zp[n,b]: 8 when no zero points are given; otherwise byte n*zrb + b/2, low
+ * nibble for even b, high nibble for odd b. */
+int oracle_zero_point(const uint8_t* zero_points, int64_t n, int64_t b, int64_t kb)
+{
+    if (zero_points == NULL) return 8;
+    const uint8_t byte = zero_points[n * zp_row_bytes_of(kb) + b / 2];
+    return (b % 2 == 0) ? (byte & 15) : (byte >> 4);
+}
+
+/* codes u8[N,K] in plain row-major order. */
+void oracle_unpack_codes(const uint8_t* packed, int64_t N, int64_t K, int64_t g, uint8_t* codes)
+{
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k)
+            codes[n * K + k] = (uint8_t)oracle_code(packed, n, k, K, g);
+}
+
+/* zero points u8[N,kb] in plain row-major order (8 everywhere when absent). */
+void oracle_unpack_zero_points(const uint8_t* zero_points, int64_t N, int64_t kb, uint8_t* z)
+{
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t b = 0; b < kb; ++b)
+            z[n * kb + b] = (uint8_t)oracle_zero_point(zero_points, n, b, kb);
+}
+
+/* dequant(B)[n,k] = (code[n,k] - zp[n,k/g]) * scale[n,k/g], in fp64.  The
+ * scales arrive already decoded to fp64 ([N, k_blocks]).  The product is
+ * exact: a 5-bit integer times a scale of at most 24 significant bits. */
+void oracle_dequant(const uint8_t* packed, const double* scales, const uint8_t* zero_points,
+                    int64_t N, int64_t K, int64_t g, double* w)
+{
+    const int64_t kb = k_blocks_of(K, g);
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            const int64_t b = k / g;
+            const int code = oracle_code(packed, n, k, K, g);
+            const int zp = oracle_zero_point(zero_points, n, b, kb);
+            w[n * K + k] = ((double)code - (double)zp) * scales[n * kb + b];
+        }
+    }
+}
+
+/* Y[m,n] = sum_{k=0}^{K-1} A[m,k] * W[n,k], k ascending, in fp64; alongside,
+ * Bnd[m,n] = sum_k |A[m,k] * W[n,k]| (the magnitude the tolerance scales
+ * with).  Naive loop over output elements; threads > 0 sets the OpenMP team. */
+void oracle_matmul(const double* A, const double* W, int64_t M, int64_t N, int64_t K,
+                   double* Y, double* Bnd, int threads)
+{
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#pragma omp parallel for collapse(2) schedule(static)
+#endif
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const double p = A[m * K + k] * W[n * K + k];
+                acc += p;
+                mag += fabs(p);
+            }
+            Y[m * N + n] = acc;
+            if (Bnd) Bnd[m * N + n] = mag;
+        }
+    }
+}
+
+/* The whole method for a chosen set of output elements (m_i, n_i): each
+ * weight is decoded from the packed bytes on the fly, as in [DQ]'s f32
+ * GEMV, so no dense [N,K] matrix is built.  Used where the full product is
+ * too large for a CPU check. */
+void oracle_matmul_nbits_at(const double* A, const uint8_t* packed, const double* scales,
+                            const uint8_t* zero_points, int64_t N, int64_t K, int64_t g,
+                            const int64_t* ms, const int64_t* ns, int64_t count,
+                            double* Y, double* Bnd, int threads)
+{
+    const int64_t kb = k_blocks_of(K, g);
+    (void)N;
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#pragma omp parallel for schedule(dynamic, 16)
+#endif
+    for (int64_t i = 0; i < count; ++i) {
+        const int64_t m = ms[i], n = ns[i];
+        double acc = 0.0, mag = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            const int64_t b = k / g;
+            const int code = oracle_code(packed, n, k, K, g);
+            const int zp = oracle_zero_point(zero_points, n, b, kb);
+            const double w = ((double)code - (double)zp) * scales[n * kb + b];
+            const double p = A[m * K + k] * w;
+            acc += p;
+            mag += fabs(p);
+        }
+        Y[i] = acc;
+        if (Bnd) Bnd[i] = mag;
+    }
+}
+
+/* All M x N outputs of the method, decoding weights on the fly (no dense
+ * matrix): the CPU baseline times this over a bounded sample of rows. */
+void oracle_matmul_nbits(const double* A, const uint8_t* packed, const double* scales,
+                         const uint8_t* zero_points, int64_t M, int64_t N, int64_t K, int64_t g,
+                         double* Y, double* Bnd, int threads)
+{
+    const int64_t kb = k_blocks_of(K, g);
+#ifdef _OPENMP
+    if (threads > 0) omp_set_num_threads(threads);
+#pragma omp parallel for collapse(2) schedule(static)
+#endif
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0, mag = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                const int64_t b = k / g;
+                const int code = oracle_code(packed, n, k, K, g);
+                const int zp = oracle_zero_point(zero_points, n, b, kb);
+                const double w = ((double)code - (double)zp) * scales[n * kb + b];
+                const double p = A[m * K + k] * w;
+                acc += p;
+                mag += fabs(p);
+            }
+            Y[m * N + n] = acc;
+            if (Bnd) Bnd[m * N + n] = mag;
+        }
+    }
+}
+
+/* [SILU]: S = silu(G) * U with silu(x) = x / (1 + e^-x). */
+void oracle_swiglu(const double* G, const double* U, int64_t count, double* S)
+{
+    for (int64_t i = 0; i < count; ++i) {
+        const double x = G[i];
+        S[i] = (x / (1.0 + exp(-x))) * U[i];
+    }
+}
+
+/* ---- the inverse direction, for fixtures ------------------------------- */
+
+/* Pack codes u8[N,K] (values 0..15) into [N, k_blocks, g/2] per [FMT];
+ * nibbles past K in the last block are written as 0. */
+void oracle_pack_codes(const uint8_t* codes, int64_t N, int64_t K, int64_t g, uint8_t* packed)
+{
+    const int64_t kb = k_blocks_of(K, g);
+    const int64_t blob = g / 2;
+    for (int64_t i = 0; i < N * kb * blob; ++i) packed[i] = 0;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            const int64_t within = k % g;
+            const int64_t at = (n * kb + k / g) * blob + within / 2;
+            const uint8_t c = codes[n * K + k] & 15;
+            packed[at] |= (within % 2 == 0) ? c : (uint8_t)(c << 4);
+        }
+    }
+}
+
+/* Pack zero points u8[N,kb] (0..15) into [N, ceil(kb/2)] per [FMT]; the high
+ * nibble of the last byte of a row with odd kb is written as 0. */
+void oracle_pack_zero_points(const uint8_t* z, int64_t N, int64_t kb, uint8_t* zero_points)
+{
+    const int64_t zrb = zp_row_bytes_of(kb);
+    for (int64_t i = 0; i < N * zrb; ++i) zero_points[i] = 0;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t b = 0; b < kb; ++b) {
+            const uint8_t v = z[n * kb + b] & 15;
+            zero_points[n * zrb + b / 2] |= (b % 2 == 0) ? v : (uint8_t)(v << 4);
+        }
+    }
+}
+
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

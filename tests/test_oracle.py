@@ -1,0 +1,334 @@
+"""Pins for the CPU oracle (no GPU).
+
+Each check ties the oracle to something other than itself: values worked out
+by hand from the format (tests/golden), exhaustive enumeration, exact rational
+brute force, special cases that reduce to a library routine (numpy integer
+matmul, numpy's fp16 decoder, scipy's logistic function), and invariants
+(code == zero point gives exactly zero, linearity, one-hot rows).  A mutation
+test at the end plants plausible mistakes in a copy of the C oracle and checks
+that these pins catch every one of them.
+"""
+import json
+import os
+import shutil
+import subprocess
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import oracle as o
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
+
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)["examples"]
+
+
+def _example_operands(ex):
+    N, K, g = ex["N"], ex["K"], ex["group"]
+    kb = (K + g - 1) // g
+    if "packed_hex" in ex:
+        packed = np.frombuffer(bytes.fromhex(ex["packed_hex"]), dtype=np.uint8).copy()
+    elif "packed_sparse" in ex:
+        packed = np.zeros(ex["packed_len"], dtype=np.uint8)
+        for i, v in ex["packed_sparse"].items():
+            packed[int(i)] = v
+    else:
+        packed = np.full(ex["packed_len"], ex["packed_fill"], dtype=np.uint8)
+    assert packed.size == N * kb * (g // 2)
+    zp = None
+    if ex.get("zero_points_hex"):
+        zp = np.frombuffer(bytes.fromhex(ex["zero_points_hex"]), dtype=np.uint8).copy()
+    scales = np.array(ex["scales_f32"], dtype=np.float32)
+    return N, K, g, packed, zp, scales
+
+
+def _case_A(spec, K):
+    if spec == "ones":
+        return np.ones((1, K), dtype=np.float32)
+    assert spec.startswith("e")
+    a = np.zeros((1, K), dtype=np.float32)
+    a[0, int(spec[1:])] = 1.0
+    return a
+
+
+# ---------------------------------------------------------------------------
+# pin functions (also run against planted mutants below)
+
+def pin_worked_examples():
+    for ex in _golden():
+        N, K, g, packed, zp, scales = _example_operands(ex)
+        codes = o.unpack_codes(packed, N, K, g)
+        if "codes" in ex:
+            assert (codes == np.array(ex["codes"], dtype=np.uint8)).all(), ex["name"]
+        for n, k, c in ex.get("codes_sparse", []):
+            assert codes[n, k] == c, (ex["name"], n, k)
+        if "zero_point_table" in ex:
+            z = o.unpack_zero_points(zp, N, K, g)
+            assert (z == np.array(ex["zero_point_table"])).all(), ex["name"]
+        w = o.dequant(packed, scales, zp, N, K, g)
+        if "weights" in ex:
+            assert (w == np.array(ex["weights"])).all(), ex["name"]
+        for n, k, v in ex.get("weights_sparse", []):
+            assert w[n, k] == v, (ex["name"], n, k)
+        for case in ex["cases"]:
+            A = _case_A(case["A"], K)
+            Y1, B1 = o.matmul(o.decode(A), w)
+            Y2, B2 = o.matmul_nbits(A, packed, scales, zp, N, K, g)
+            Y3, B3 = o.matmul_nbits_at(A, packed, scales, zp, N, K, g,
+                                       np.zeros(N, np.int64), np.arange(N))
+            for Y, B in ((Y1[0], B1[0]), (Y2[0], B2[0]), (Y3, B3)):
+                assert (Y == np.array(case["Y"])).all(), (ex["name"], case["A"], Y)
+                assert (B == np.array(case["B"])).all(), (ex["name"], case["A"], B)
+
+
+def pin_exhaustive_nibbles():
+    # 256 rows, each one block of 16 k holding the same byte 8 times.
+    g, K = 16, 16
+    packed = np.repeat(np.arange(256, dtype=np.uint8), 8)
+    codes = o.unpack_codes(packed, 256, K, g)
+    for b in range(256):
+        assert (codes[b, 0::2] == (b & 15)).all() and (codes[b, 1::2] == (b >> 4)).all(), b
+    # zero points: 256 rows of two blocks whose zp byte is b.
+    zp = np.arange(256, dtype=np.uint8)
+    z = o.unpack_zero_points(zp, 256, 32, 16)
+    assert (z[:, 0] == np.arange(256) % 16).all() and (z[:, 1] == np.arange(256) // 16).all()
+    assert (o.unpack_zero_points(None, 3, 64, 16) == 8).all()
+
+
+def pin_pack_unpack_identity():
+    rng = np.random.default_rng(7)
+    for g in (16, 32, 64, 128):
+        for N in (1, 5, 70, 130):
+            for K in (g, 3 * g, 5 * g):           # 5*g gives odd k_blocks
+                codes = rng.integers(0, 16, (N, K), dtype=np.uint8)
+                packed = o.pack_codes(codes, g)
+                assert packed.shape == (N, K // g, g // 2)
+                assert (o.unpack_codes(packed, N, K, g) == codes).all()
+                kb = K // g
+                z = rng.integers(0, 16, (N, kb), dtype=np.uint8)
+                zpk = o.pack_zero_points(z)
+                assert zpk.shape == (N, (kb + 1) // 2)
+                assert (o.unpack_zero_points(zpk, N, K, g) == z).all()
+
+
+def pin_code_equals_zero_point_gives_zero():
+    rng = np.random.default_rng(11)
+    N, K, g = 9, 96, 32
+    kb = K // g
+    z = rng.integers(0, 16, (N, kb), dtype=np.uint8)
+    codes = np.repeat(z, g, axis=1)
+    packed = o.pack_codes(codes, g)
+    zp = o.pack_zero_points(z)
+    scales = rng.uniform(0.5, 2.0, (N, kb)).astype(np.float16)
+    w = o.dequant(packed, scales, zp, N, K, g)
+    assert (w == 0.0).all() and not np.signbit(w).any()
+    A = rng.standard_normal((3, K)).astype(np.float16)
+    Y, B = o.matmul_nbits(A, packed, scales, zp, N, K, g)
+    assert (Y == 0.0).all() and (B == 0.0).all()
+
+
+def _fraction_reference(A, codes, z, scales, g):
+    """Exact rational Y = A . ((codes - z) * s)^T from the binary values."""
+    M, K = A.shape
+    N = codes.shape[0]
+    Af = [[Fraction(float(A[m, k])) for k in range(K)] for m in range(M)]
+    Y = [[Fraction(0)] * N for _ in range(M)]
+    B = [[Fraction(0)] * N for _ in range(M)]
+    for n in range(N):
+        wn = [(int(codes[n, k]) - int(z[n, k // g])) * Fraction(float(scales[n, k // g]))
+              for k in range(K)]
+        for m in range(M):
+            acc = Fraction(0)
+            mag = Fraction(0)
+            for k in range(K):
+                p = Af[m][k] * wn[k]
+                acc += p
+                mag += abs(p)
+            Y[m][n] = acc
+            B[m][n] = mag
+    return Y, B
+
+
+def pin_bruteforce_exact():
+    rng = np.random.default_rng(3)
+    u = 2.0 ** -53
+    for seed, (M, K, N, g, sdt, with_zp) in enumerate([
+            (1, 16, 3, 16, np.float32, False), (2, 32, 5, 16, np.float16, True),
+            (3, 64, 4, 32, np.float16, True), (4, 64, 7, 64, np.float32, True),
+            (2, 48, 6, 16, np.float16, True), (3, 40, 2, 32, np.float32, True)]):
+        kb = (K + g - 1) // g
+        codes = rng.integers(0, 16, (N, K), dtype=np.uint8)
+        z = rng.integers(0, 16, (N, kb), dtype=np.uint8) if with_zp else np.full((N, kb), 8, np.uint8)
+        scales = rng.uniform(0.003, 0.03, (N, kb)).astype(sdt)
+        A = rng.standard_normal((M, K)).astype(np.float16)
+        packed = o.pack_codes(np.pad(codes, ((0, 0), (0, kb * g - K))), g)
+        zp = o.pack_zero_points(z) if with_zp else None
+        Yq, Bq = _fraction_reference(A, codes, z, scales, g)
+        Y, B = o.matmul_nbits(A, packed, scales, zp, N, K, g)
+        W = o.dequant(packed, scales, zp, N, K, g)
+        for n in range(N):
+            for k in range(K):
+                exact = (int(codes[n, k]) - int(z[n, k // g])) * Fraction(float(scales[n, k // g]))
+                assert Fraction(W[n, k]) == exact
+        gamma = K * u / (1 - K * u)
+        for m in range(M):
+            for n in range(N):
+                assert abs(Fraction(Y[m, n]) - Yq[m][n]) <= Fraction(gamma) * Bq[m][n], (seed, m, n)
+                assert abs(Fraction(B[m, n]) - Bq[m][n]) <= Fraction(gamma) * Bq[m][n], (seed, m, n)
+
+
+def pin_integer_special_case():
+    # scale 1 and zero point 0 reduce the method to an integer GEMM
+    rng = np.random.default_rng(5)
+    for (M, K, N, g) in ((3, 64, 5, 16), (4, 256, 33, 128), (2, 96, 7, 32)):
+        kb = K // g
+        codes = rng.integers(0, 16, (N, K), dtype=np.uint8)
+        A = rng.integers(-50, 51, (M, K)).astype(np.float16)
+        packed = o.pack_codes(codes, g)
+        zp = o.pack_zero_points(np.zeros((N, kb), np.uint8))
+        scales = np.ones((N, kb), np.float32)
+        Y, _ = o.matmul_nbits(A, packed, scales, zp, N, K, g)
+        ref = A.astype(np.int64) @ codes.astype(np.int64).T
+        assert (Y == ref).all()
+        # transposition check: a non-square case with distinct M, N
+        assert Y.shape == (M, N)
+
+
+def pin_linear_and_one_hot():
+    rng = np.random.default_rng(9)
+    N, K, g = 6, 64, 16
+    kb = K // g
+    packed = rng.integers(0, 256, (N, kb, g // 2), dtype=np.uint8)
+    zp = rng.integers(0, 256, (N, (kb + 1) // 2), dtype=np.uint8)
+    scales = rng.uniform(0.01, 0.02, (N, kb)).astype(np.float16)
+    W = o.dequant(packed, scales, zp, N, K, g)
+    eye = np.eye(K, dtype=np.float16)
+    Y, _ = o.matmul_nbits(eye, packed, scales, zp, N, K, g)
+    assert (Y == W.T).all()
+    a1 = rng.integers(-8, 8, (1, K)).astype(np.float16)
+    a2 = rng.integers(-8, 8, (1, K)).astype(np.float16)
+    Y1, _ = o.matmul_nbits(a1, packed, scales, zp, N, K, g)
+    Y2, _ = o.matmul_nbits(a2, packed, scales, zp, N, K, g)
+    Y12, _ = o.matmul_nbits((a1 + a2).astype(np.float16), packed, scales, zp, N, K, g)
+    assert np.allclose(Y12, Y1 + Y2, rtol=1e-12, atol=1e-12)
+
+
+def pin_fp16_decode_all_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    mine = o.decode(bits)
+    ref = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert (np.isnan(mine) == nan).all()
+    assert (mine[~nan] == ref[~nan]).all()
+    assert (np.signbit(mine[~nan]) == np.signbit(ref[~nan])).all()
+
+
+def pin_swiglu():
+    from scipy.special import expit
+    x = np.concatenate([np.linspace(-40, 40, 2001), [0.0, -0.0, 1e-300, 700.0, -700.0]])
+    u = np.linspace(-3, 3, x.size)
+    S = o.swiglu(x, u)
+    ref = x * expit(x) * u
+    assert np.allclose(S, ref, rtol=1e-14, atol=1e-300)
+    assert o.swiglu(np.array([0.0]), np.array([5.0]))[0] == 0.0
+    big = np.array([50.0, 100.0])
+    assert (o.swiglu(big, np.ones(2)) == big).all()
+
+
+PINS = [pin_worked_examples, pin_exhaustive_nibbles, pin_pack_unpack_identity,
+        pin_code_equals_zero_point_gives_zero, pin_bruteforce_exact,
+        pin_integer_special_case, pin_linear_and_one_hot, pin_fp16_decode_all_patterns,
+        pin_swiglu]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
+def test_oracle_pin(pin):
+    pin()
+
+
+def test_within_bound_semantics():
+    Y = np.array([1.0, np.nan, np.inf, 2.0, 0.0])
+    B = np.array([10.0, 1.0, 1.0, 0.0, 0.0])
+    y = np.array([1.0 + 9e-3, np.nan, np.inf, np.nan, 2e-5])
+    assert o.within_bound(y, Y, B).tolist() == [True, True, True, False, False]
+    assert not o.within_bound([np.nan], [1.0], [1e9])[0]
+    assert not o.within_bound([-np.inf], [np.inf], [1.0])[0]
+    assert o.within_bound([1.0 + 1.1e-2], [1.0], [10.0]).tolist() == [False]
+
+
+def test_oracle_decodes_the_synthetic_workloads():
+    # the generator's uniform bytes give uniform nibbles and zero points
+    from block_wise_int4_amd import synth
+    w = synth.weight(64, 512, 32, "f16", (0.005, 0.02), True, (99,))
+    codes = o.unpack_codes(w.packed, w.N, w.K, w.group)
+    counts = np.bincount(codes.ravel(), minlength=16)
+    assert counts.min() > 0.8 * codes.size / 16 and counts.max() < 1.2 * codes.size / 16
+    z = o.unpack_zero_points(w.zero_points, w.N, w.K, w.group)
+    assert z.min() == 0 and z.max() == 15
+    s = o.decode(w.scales)
+    assert s.min() >= 0.005 - 1e-5 and s.max() <= 0.02 + 1e-5
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each mutant of the C oracle must fail at least one pin
+
+MUTANTS = {
+    # name: (text in mnb_oracle.c, replacement); every occurrence is replaced
+    "swapped nibble parity": ("(within % 2 == 0) ? (byte & 15) : (byte >> 4)",
+                              "(within % 2 == 0) ? (byte >> 4) : (byte & 15)"),
+    "zero-point byte by block not block/2": ("zp_row_bytes_of(kb) + b / 2]", "zp_row_bytes_of(kb) + b]"),
+    "zero-point parity swapped": ("(b % 2 == 0) ? (byte & 15) : (byte >> 4)",
+                                  "(b % 2 == 0) ? (byte >> 4) : (byte & 15)"),
+    "default zero point 0": ("if (zero_points == NULL) return 8;", "if (zero_points == NULL) return 0;"),
+    "sign of zero point": ("((double)code - (double)zp)", "((double)code + (double)zp)"),
+    "scale index by k not block": ("scales[n * kb + b]", "scales[n * kb + (k % kb)]"),
+    "transposed weight in matmul": ("A[m * K + k] * W[n * K + k]", "A[m * K + k] * W[(k * N + n) % (N * K)]"),
+    "dropped last k": ("k < K; ++k", "k + 1 < K; ++k"),
+    "blob size g not g/2": ("const int64_t blob = g / 2;\n    const int64_t block = k / g;",
+                            "const int64_t blob = g;\n    const int64_t block = k / g;"),
+    "fp16 exponent bias 16": ("expo - 25", "expo - 26"),
+    "fp16 subnormal scale": ("ldexp((double)frac, -24)", "ldexp((double)frac, -25)"),
+    "silu sign": ("(x / (1.0 + exp(-x))) * U[i]", "(x / (1.0 + exp(x))) * U[i]"),
+    "magnitude sum signed": ("mag += fabs(p);", "mag += p;"),
+}
+
+
+def _run_pins_against(lib_path):
+    import ctypes
+    saved = o._lib
+    o._lib = None
+    saved_path = o._LIB_PATH
+    try:
+        o._LIB_PATH = lib_path
+        o._load()
+        failed = []
+        for pin in PINS:
+            try:
+                pin()
+            except AssertionError:
+                failed.append(pin.__name__)
+        return failed
+    finally:
+        o._lib = saved
+        o._LIB_PATH = saved_path
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc missing")
+def test_planted_oracle_mistakes_are_caught(tmp_path):
+    src = open(o._SRC).read()
+    survivors = []
+    for name, (old, new) in MUTANTS.items():
+        assert src.count(old) >= 1, "mutation anchor missing: %s" % name
+        mutant = src.replace(old, new)
+        cfile = tmp_path / ("mut_%s.c" % abs(hash(name)))
+        cfile.write_text(mutant)
+        so = str(cfile) + ".so"
+        subprocess.check_call(["gcc", "-O1", "-fopenmp", "-fPIC", "-shared", str(cfile), "-o", so, "-lm"])
+        failed = _run_pins_against(so)
+        if not failed:
+            survivors.append(name)
+    assert not survivors, "mutants not caught by any pin: %s" % survivors
