@@ -1,0 +1,322 @@
+// gemv.hip -- decode GEMV (M = 1) and the fused gate/up + SwiGLU GEMV.
+//
+// Method: onnx-runtime-ep-cuda 0.1.0-dev.3, src/kernels/matmul_nbits.rs --
+// the f32 GEMV (matmul_nbits_gemv_f32), the fp16 GEMVs (fp32 partial per
+// block times its scale, lane reduction), the down-projection variant that
+// stages the activation once in shared memory, and the paired gate/up GEMV
+// with its SwiGLU epilogue (matmul_nbits_gemv_f16_gate_up_swiglu).
+//
+// gfx950 design: one workgroup per 16-column tile; its waves split the tile's
+// 128-k chunks.  Each lane streams one 16-byte word per chunk (a wave reads
+// a contiguous 1 KiB), unpacks nibbles to exact fp16 (c - z) in registers,
+// and multiplies with v_dot2_f32_f16 against the activation staged once in
+// LDS; each 8-k partial is scaled by its group's scale into an fp32 sum.
+// Lanes of a column reduce with cross-lane moves, waves through LDS, in a
+// fixed order (results are deterministic).
+#include "mnb_device.hpp"
+#include "mnb_internal.hpp"
+
+namespace mnb {
+
+namespace {
+
+constexpr int kBatch = 4;          // chunks per wave in flight
+constexpr int kMaxWaves = 8;
+// activation staging stays under the 64 KiB a workgroup gets without opt-in
+constexpr int64_t kMaxStageBytes = 63 * 1024;
+
+struct GemvWeight {
+    const u4_t* codes;
+    const void* scales;
+    const uint8_t* zp;
+};
+
+struct GemvParams {
+    GemvWeight w[2];
+    const void* a;
+    void* y;
+    int N, K, C;
+};
+
+template <int Q> struct LaneGroups {
+    static constexpr int NS = Q >= 4 ? 4 : Q;   // scales a lane needs per chunk
+    __device__ static int sidx(int j) { return Q == 1 ? 0 : (Q == 2 ? (j >> 1) : j); }
+};
+
+template <typename ST, int NS> struct ScaleVec;
+template <> struct ScaleVec<__half, 1> { typedef uint16_t raw; };
+template <> struct ScaleVec<__half, 2> { typedef uint32_t raw; };
+template <> struct ScaleVec<__half, 4> { typedef uint2 raw; };
+template <> struct ScaleVec<float, 1> { typedef float raw; };
+template <> struct ScaleVec<float, 2> { typedef float2 raw; };
+template <> struct ScaleVec<float, 4> { typedef float4 raw; };
+
+template <typename ST, int NS>
+__device__ __forceinline__ float scale_at(const typename ScaleVec<ST, NS>::raw& r, int s)
+{
+    const ST* e = reinterpret_cast<const ST*>(&r);
+    return to_f32(e[s]);
+}
+
+template <typename ST, int Q, bool HAS_ZP> struct ChunkRegs {
+    static constexpr int NS = LaneGroups<Q>::NS;
+    u4_t d;
+    typename ScaleVec<ST, NS>::raw s;
+    uint32_t zw;
+};
+
+template <typename ST, int Q, bool HAS_ZP>
+__device__ __forceinline__ void load_chunk(const GemvWeight& w, int64_t chunk, int lane,
+                                           ChunkRegs<ST, Q, HAS_ZP>& r)
+{
+    constexpr int NS = LaneGroups<Q>::NS;
+    const int i = lane & 15, h = lane >> 4;
+    const int sbase = Q <= 4 ? i * Q : ((h >> 1) * 16 + i) * 4;
+    r.d = __builtin_nontemporal_load(w.codes + chunk * 64 + lane);
+    const ST* sp = static_cast<const ST*>(w.scales) + chunk * kTileN * Q + sbase;
+    r.s = *reinterpret_cast<const typename ScaleVec<ST, NS>::raw*>(sp);
+    if (HAS_ZP) {
+        const uint8_t* zp = w.zp + chunk * (kTileN / 2) * Q;
+        if (Q == 1) {
+            r.zw = (zp[i >> 1] >> (4 * (i & 1))) & 15u;
+        } else if (Q == 2) {
+            r.zw = zp[i];
+        } else {
+            r.zw = *reinterpret_cast<const uint16_t*>(zp + sbase / 2);
+        }
+    } else {
+        r.zw = 0;
+    }
+}
+
+// fp16 activations: partial dot of one 128-bit code word per 32-k step.
+template <typename ST, int Q, bool HAS_ZP>
+__device__ __forceinline__ float chunk_dot_f16(const ChunkRegs<ST, Q, HAS_ZP>& r,
+                                               const _Float16* as, int c, int h, float acc)
+{
+    constexpr int NS = LaneGroups<Q>::NS;
+    const uint32_t dw[4] = {r.d.x, r.d.y, r.d.z, r.d.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int sj = LaneGroups<Q>::sidx(j);
+        const uint32_t z = HAS_ZP ? (r.zw >> (4 * sj)) & 15u : 8u;
+        h2_t q[4];
+        unpack8(dw[j], zp_const(z), q);
+        const u4_t av = *reinterpret_cast<const u4_t*>(as + c * kChunkK + 32 * j + 8 * h);
+        float part = __builtin_amdgcn_fdot2(q[0], as_h2(av.x), 0.0f, false);
+        part = __builtin_amdgcn_fdot2(q[1], as_h2(av.y), part, false);
+        part = __builtin_amdgcn_fdot2(q[2], as_h2(av.z), part, false);
+        part = __builtin_amdgcn_fdot2(q[3], as_h2(av.w), part, false);
+        acc = __builtin_fmaf(part, scale_at<ST, NS>(r.s, sj), acc);
+    }
+    return acc;
+}
+
+// fp32 activations: the same word, products in fp32.
+template <typename ST, int Q, bool HAS_ZP>
+__device__ __forceinline__ float chunk_dot_f32(const ChunkRegs<ST, Q, HAS_ZP>& r, const float* as,
+                                               int c, int h, float acc)
+{
+    constexpr int NS = LaneGroups<Q>::NS;
+    const uint32_t dw[4] = {r.d.x, r.d.y, r.d.z, r.d.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int sj = LaneGroups<Q>::sidx(j);
+        const float zf = HAS_ZP ? (float)((r.zw >> (4 * sj)) & 15u) : 8.0f;
+        const float* ap = as + c * kChunkK + 32 * j + 8 * h;
+        const f4_t a0 = *reinterpret_cast<const f4_t*>(ap);
+        const f4_t a1 = *reinterpret_cast<const f4_t*>(ap + 4);
+        const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        float part = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            part = __builtin_fmaf(av[e], (float)code_at(dw[j], e) - zf, part);
+        }
+        acc = __builtin_fmaf(part, scale_at<ST, NS>(r.s, sj), acc);
+    }
+    return acc;
+}
+
+__device__ __forceinline__ float silu_f32(float x) { return x / (1.0f + __expf(-x)); }
+
+template <typename AT, typename ST, int Q, bool HAS_ZP, bool FUSED>
+__global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
+{
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr bool F16 = sizeof(AT) == 2;
+    constexpr int NW = FUSED ? 2 : 1;
+    typedef ChunkRegs<ST, Q, HAS_ZP> Regs;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int nw = blockDim.x >> 6;
+    const int h = lane >> 4;
+    const int64_t t = blockIdx.x;
+    const int C = p.C;
+    const int64_t kpad = (int64_t)C * kChunkK;
+
+    // 1. first activation vector of this thread (16 bytes) -> registers
+    constexpr int kPerVec = 16 / sizeof(AT);
+    const int nvec = (int)(kpad / kPerVec);
+    const int nvec_valid = p.K / kPerVec;
+    const u4_t* a_vec = static_cast<const u4_t*>(p.a);
+    u4_t* s_vec = reinterpret_cast<u4_t*>(smem);
+    u4_t first = {0u, 0u, 0u, 0u};
+    if (tid < nvec_valid) first = a_vec[tid];
+
+    // 2. first batch of code words, scales and zero points
+    Regs cur[NW][kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+        const int c = wave + nw * u;
+        if (c < C) {
+#pragma unroll
+            for (int x = 0; x < NW; ++x) load_chunk<ST, Q, HAS_ZP>(p.w[x], t * C + c, lane, cur[x][u]);
+        }
+    }
+
+    // 3. stage the activation in LDS (zero beyond K)
+    if (tid < nvec) s_vec[tid] = first;
+    for (int v = tid + blockDim.x; v < nvec; v += blockDim.x) {
+        u4_t val = {0u, 0u, 0u, 0u};
+        if (v < nvec_valid) val = a_vec[v];
+        s_vec[v] = val;
+    }
+    block_sync_lds();
+
+    // 4. stream the wave's chunks, one batch ahead
+    float acc[NW];
+#pragma unroll
+    for (int x = 0; x < NW; ++x) acc[x] = 0.0f;
+    for (int cb = wave; cb < C; cb += nw * kBatch) {
+        Regs nxt[NW][kBatch];
+        const int cn = cb + nw * kBatch;
+        if (cn < C) {
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) {
+                const int c = cn + nw * u;
+                if (c < C) {
+#pragma unroll
+                    for (int x = 0; x < NW; ++x)
+                        load_chunk<ST, Q, HAS_ZP>(p.w[x], t * C + c, lane, nxt[x][u]);
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            const int c = cb + nw * u;
+            if (c < C) {
+#pragma unroll
+                for (int x = 0; x < NW; ++x) {
+                    if (F16)
+                        acc[x] = chunk_dot_f16<ST, Q, HAS_ZP>(
+                            cur[x][u], reinterpret_cast<const _Float16*>(smem), c, h, acc[x]);
+                    else
+                        acc[x] = chunk_dot_f32<ST, Q, HAS_ZP>(
+                            cur[x][u], reinterpret_cast<const float*>(smem), c, h, acc[x]);
+                }
+            }
+        }
+#pragma unroll
+        for (int x = 0; x < NW; ++x)
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u) cur[x][u] = nxt[x][u];
+    }
+
+    // 5. lanes L, L^16, L^32, L^48 hold the same column: reduce, then waves
+#pragma unroll
+    for (int x = 0; x < NW; ++x) {
+        acc[x] += __shfl_xor(acc[x], 16);
+        acc[x] += __shfl_xor(acc[x], 32);
+    }
+    float* red = reinterpret_cast<float*>(smem + kpad * sizeof(AT));
+    if (h == 0) {
+#pragma unroll
+        for (int x = 0; x < NW; ++x) red[(x * kMaxWaves + wave) * 16 + lane] = acc[x];
+    }
+    __syncthreads();
+    if (wave == 0 && lane < 16) {
+        float r[NW];
+#pragma unroll
+        for (int x = 0; x < NW; ++x) {
+            r[x] = 0.0f;
+            for (int ww = 0; ww < nw; ++ww) r[x] += red[(x * kMaxWaves + ww) * 16 + lane];
+        }
+        const int64_t n = t * kTileN + lane;
+        if (n < p.N) {
+            float out = r[0];
+            if (FUSED) out = silu_f32(r[0]) * r[NW - 1];
+            static_cast<AT*>(p.y)[n] = from_f32<AT>(out);
+        }
+    }
+}
+
+template <typename AT, typename ST, int Q, bool HAS_ZP, bool FUSED>
+hipError_t launch_t(const GemvParams& p, int waves, size_t smem, int64_t tiles, hipStream_t s)
+{
+    gemv_kernel<AT, ST, Q, HAS_ZP, FUSED><<<dim3((unsigned)tiles), dim3(waves * 64), smem, s>>>(p);
+    return hipGetLastError();
+}
+
+template <typename AT, typename ST, bool HAS_ZP, bool FUSED>
+hipError_t launch_q(const Layout& L, const GemvParams& p, int waves, size_t smem, hipStream_t s)
+{
+    switch (L.Q) {
+    case 1: return launch_t<AT, ST, 1, HAS_ZP, FUSED>(p, waves, smem, L.T, s);
+    case 2: return launch_t<AT, ST, 2, HAS_ZP, FUSED>(p, waves, smem, L.T, s);
+    case 4: return launch_t<AT, ST, 4, HAS_ZP, FUSED>(p, waves, smem, L.T, s);
+    default: return launch_t<AT, ST, 8, HAS_ZP, FUSED>(p, waves, smem, L.T, s);
+    }
+}
+
+template <typename AT, bool FUSED>
+hipError_t launch_a(const Layout& L, const GemvParams& p, int waves, size_t smem, hipStream_t s)
+{
+    if (L.ss == 2) {
+        return L.has_zp ? launch_q<AT, __half, true, FUSED>(L, p, waves, smem, s)
+                        : launch_q<AT, __half, false, FUSED>(L, p, waves, smem, s);
+    }
+    return L.has_zp ? launch_q<AT, float, true, FUSED>(L, p, waves, smem, s)
+                    : launch_q<AT, float, false, FUSED>(L, p, waves, smem, s);
+}
+
+GemvWeight gw(const WeightView& v)
+{
+    return GemvWeight{reinterpret_cast<const u4_t*>(v.codes), v.scales, v.zp};
+}
+
+}  // namespace
+
+int64_t gemv_max_k(bool f16_act)
+{
+    return kMaxStageBytes / (f16_act ? 2 : 4) / kChunkK * kChunkK;
+}
+
+hipError_t launch_gemv(const Layout& L, const WeightView& gate, const WeightView* up,
+                       const void* a, bool f16_act, void* y, hipStream_t stream,
+                       const char** variant)
+{
+    GemvParams p;
+    p.w[0] = gw(gate);
+    p.w[1] = up ? gw(*up) : gw(gate);
+    p.a = a;
+    p.y = y;
+    p.N = (int)L.N;
+    p.K = (int)L.K;
+    p.C = (int)L.C;
+    int waves = (int)(L.C < kMaxWaves ? L.C : kMaxWaves);
+    if (waves < 1) waves = 1;
+    const size_t smem = (size_t)L.C * kChunkK * (f16_act ? 2 : 4) + 2 * kMaxWaves * 16 * sizeof(float);
+    const bool fused = up != nullptr;
+    if (variant) *variant = fused ? (f16_act ? "gemv_gate_up_swiglu_f16" : "gemv_gate_up_swiglu_f32")
+                                  : (f16_act ? "gemv_f16" : "gemv_f32");
+    if (f16_act) {
+        return fused ? launch_a<__half, true>(L, p, waves, smem, stream)
+                     : launch_a<__half, false>(L, p, waves, smem, stream);
+    }
+    return fused ? launch_a<float, true>(L, p, waves, smem, stream)
+                 : launch_a<float, false>(L, p, waves, smem, stream);
+}
+
+}  // namespace mnb

@@ -1,0 +1,296 @@
+// mnb_api.cpp -- the C ABI of include/mnb.h: host-side validation, shape-class
+// dispatch and launches on the caller's stream.
+//
+// Validation follows the attribute and operand checks of
+// onnx-runtime-ep-cuda 0.1.0-dev.3, src/kernels/matmul_nbits.rs
+// (MatMulNBitsFactory::create, run, run_f16 and the require_* helpers): every
+// check runs on the host before any HIP call, and an unsupported request is
+// refused with a reason instead of being computed some other way.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+#include <string>
+
+#include "../../include/mnb.h"
+#include "mnb_internal.hpp"
+
+using mnb::Layout;
+
+namespace {
+
+thread_local std::string g_error;
+thread_local const char* g_variant = "";
+
+mnb_status fail(mnb_status s, const char* fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_error = std::string("mnb: ") + buf;
+    return s;
+}
+
+mnb_status ok(const char* variant)
+{
+    g_error.clear();
+    g_variant = variant ? variant : "";
+    return MNB_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+mnb_status check_desc(const mnb_weight_desc* w, Layout* L)
+{
+    if (!w) return fail(MNB_ERR_INVALID_ARGUMENT, "weight descriptor is NULL");
+    if (w->n < 0) return fail(MNB_ERR_INVALID_ARGUMENT, "N must be >= 0 (got %lld)", (long long)w->n);
+    if (w->k <= 0) return fail(MNB_ERR_INVALID_ARGUMENT, "K must be > 0 (got %lld)", (long long)w->k);
+    const int g = w->group_size;
+    if (g < 16 || (g & (g - 1)) != 0)
+        return fail(MNB_ERR_INVALID_ARGUMENT, "block_size must be a power of 2 and >= 16 (got %d)", g);
+    if (g > 128)
+        return fail(MNB_ERR_UNSUPPORTED, "block_size %d not supported (16, 32, 64 or 128)", g);
+    if (w->k % g != 0)
+        return fail(MNB_ERR_UNSUPPORTED, "K=%lld is not a multiple of block_size %d",
+                    (long long)w->k, g);
+    if (w->has_zero_points != 0 && w->has_zero_points != 1)
+        return fail(MNB_ERR_INVALID_ARGUMENT, "has_zero_points must be 0 or 1 (got %d)",
+                    w->has_zero_points);
+    if (w->scale_dtype != MNB_F16 && w->scale_dtype != MNB_F32)
+        return fail(MNB_ERR_INVALID_ARGUMENT, "scale_dtype must be MNB_F16 or MNB_F32 (got %d)",
+                    w->scale_dtype);
+    if (w->reserved != 0) return fail(MNB_ERR_INVALID_ARGUMENT, "reserved field must be 0");
+    if (w->n > INT32_MAX || w->k > INT32_MAX)
+        return fail(MNB_ERR_INVALID_ARGUMENT, "N and K must fit in 32 bits");
+    *L = mnb::make_layout(w->n, w->k, g, w->has_zero_points != 0, w->scale_dtype == MNB_F16);
+    if (L->total < 0 || L->total > (int64_t(1) << 46))
+        return fail(MNB_ERR_INVALID_ARGUMENT, "repacked size overflows");
+    return MNB_OK;
+}
+
+mnb_status check_act_dtype(int32_t a_dtype)
+{
+    if (a_dtype != MNB_F16 && a_dtype != MNB_F32)
+        return fail(MNB_ERR_INVALID_ARGUMENT, "a_dtype must be MNB_F16 or MNB_F32 (got %d)", a_dtype);
+    return MNB_OK;
+}
+
+mnb_status check_ptr(const void* p, uintptr_t align, const char* name)
+{
+    if (!p) return fail(MNB_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+    if (!aligned(p, align))
+        return fail(MNB_ERR_INVALID_ARGUMENT, "%s must be %u-byte aligned", name, (unsigned)align);
+    return MNB_OK;
+}
+
+// A gfx950 device must be current.  The architecture is looked up once per
+// device (a property query is not free); later calls cost one hipGetDevice.
+mnb_status check_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return fail(MNB_ERR_DEVICE, "no HIP device available");
+    }
+    static std::mutex mu;
+    static signed char is_gfx950[64] = {0};  // 0 unknown, 1 yes, -1 no
+    if (dev >= 64) return fail(MNB_ERR_DEVICE, "device index %d out of range", dev);
+    if (is_gfx950[dev] == 0) {
+        std::lock_guard<std::mutex> lock(mu);
+        if (is_gfx950[dev] == 0) {
+            hipDeviceProp_t prop;
+            if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+                (void)hipGetLastError();
+                return fail(MNB_ERR_DEVICE, "cannot query device %d", dev);
+            }
+            is_gfx950[dev] = std::string(prop.gcnArchName).rfind("gfx950", 0) == 0 ? 1 : -1;
+        }
+    }
+    if (is_gfx950[dev] < 0) return fail(MNB_ERR_DEVICE, "device %d is not gfx950", dev);
+    return MNB_OK;
+}
+
+mnb_status launched(hipError_t e, const char* variant)
+{
+    if (e != hipSuccess) return fail(MNB_ERR_DEVICE, "launch failed: %s", hipGetErrorString(e));
+    return ok(variant);
+}
+
+#define MNB_TRY(x)                           \
+    do {                                     \
+        const mnb_status s_ = (x);           \
+        if (s_ != MNB_OK) return s_;         \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t mnb_repacked_bytes(const mnb_weight_desc* w)
+{
+    Layout L;
+    if (check_desc(w, &L) != MNB_OK) return 0;
+    g_error.clear();
+    return (size_t)L.total;
+}
+
+mnb_status mnb_repacked_layout(const mnb_weight_desc* w, mnb_layout* out)
+{
+    Layout L;
+    MNB_TRY(check_desc(w, &L));
+    if (!out) return fail(MNB_ERR_INVALID_ARGUMENT, "out is NULL");
+    out->tiles = L.T;
+    out->chunks = L.C;
+    out->groups_per_chunk = L.Q;
+    out->codes_offset = L.codes_off;
+    out->codes_bytes = L.codes_bytes;
+    out->scales_offset = L.scales_off;
+    out->scales_bytes = L.scales_bytes;
+    out->zero_points_offset = L.zp_off;
+    out->zero_points_bytes = L.zp_bytes;
+    out->total_bytes = L.total;
+    g_error.clear();
+    return MNB_OK;
+}
+
+mnb_status mnb_repack(const mnb_weight_desc* w, const uint8_t* packed, const void* scales,
+                      const uint8_t* zero_points, void* repacked, void* stream)
+{
+    Layout L;
+    MNB_TRY(check_desc(w, &L));
+    MNB_TRY(check_ptr(repacked, 256, "repacked"));
+    if (L.N == 0) return ok("repack");
+    MNB_TRY(check_ptr(packed, 16, "packed"));
+    MNB_TRY(check_ptr(scales, 16, "scales"));
+    if (w->has_zero_points) {
+        MNB_TRY(check_ptr(zero_points, 16, "zero_points"));
+    } else if (zero_points) {
+        return fail(MNB_ERR_INVALID_ARGUMENT, "zero_points given but has_zero_points is 0");
+    }
+    MNB_TRY(check_device());
+    return launched(mnb::launch_repack(L, packed, scales, zero_points, repacked,
+                                       static_cast<hipStream_t>(stream)),
+                    "repack");
+}
+
+static mnb_status gemv_common(const mnb_weight_desc* w, const void* gate, const void* up,
+                              const void* a, int32_t a_dtype, void* y, void* stream)
+{
+    Layout L;
+    MNB_TRY(check_desc(w, &L));
+    MNB_TRY(check_act_dtype(a_dtype));
+    const bool f16 = a_dtype == MNB_F16;
+    if (L.K > mnb::gemv_max_k(f16))
+        return fail(MNB_ERR_UNSUPPORTED, "K=%lld exceeds the decode GEMV limit %lld for %s activations",
+                    (long long)L.K, (long long)mnb::gemv_max_k(f16), f16 ? "fp16" : "fp32");
+    if (L.N == 0) return ok("noop");
+    MNB_TRY(check_ptr(gate, 256, up ? "gate_repacked" : "repacked"));
+    if (up) MNB_TRY(check_ptr(up, 256, "up_repacked"));
+    MNB_TRY(check_ptr(a, 16, "a"));
+    MNB_TRY(check_ptr(y, f16 ? 2 : 4, "y"));
+    MNB_TRY(check_device());
+    const char* variant = "";
+    const mnb::WeightView gv = mnb::view_of(L, gate);
+    mnb::WeightView uv;
+    if (up) uv = mnb::view_of(L, up);
+    return launched(mnb::launch_gemv(L, gv, up ? &uv : nullptr, a, f16, y,
+                                     static_cast<hipStream_t>(stream), &variant),
+                    variant);
+}
+
+mnb_status mnb_gemv(const mnb_weight_desc* w, const void* repacked, const void* a, int32_t a_dtype,
+                    void* y, void* stream)
+{
+    return gemv_common(w, repacked, nullptr, a, a_dtype, y, stream);
+}
+
+mnb_status mnb_gemv_gate_up_swiglu(const mnb_weight_desc* w, const void* gate_repacked,
+                                   const void* up_repacked, const void* a, int32_t a_dtype,
+                                   void* y, void* stream)
+{
+    if (!up_repacked) return fail(MNB_ERR_INVALID_ARGUMENT, "up_repacked is NULL");
+    return gemv_common(w, gate_repacked, up_repacked, a, a_dtype, y, stream);
+}
+
+static size_t workspace_for(const Layout& L, int64_t m)
+{
+    if (m >= 2 && m <= 16) return mnb::gemm_small_workspace(L, m);
+    return 0;
+}
+
+size_t mnb_gemm_workspace_bytes(const mnb_weight_desc* w, int64_t m)
+{
+    Layout L;
+    if (check_desc(w, &L) != MNB_OK) return 0;
+    if (m < 0) {
+        fail(MNB_ERR_INVALID_ARGUMENT, "M must be >= 0");
+        return 0;
+    }
+    g_error.clear();
+    return workspace_for(L, m);
+}
+
+mnb_status mnb_gemm(const mnb_weight_desc* w, const void* repacked, const void* a, int64_t m,
+                    int32_t a_dtype, void* y, void* workspace, size_t workspace_bytes, void* stream)
+{
+    Layout L;
+    MNB_TRY(check_desc(w, &L));
+    MNB_TRY(check_act_dtype(a_dtype));
+    if (m < 0) return fail(MNB_ERR_INVALID_ARGUMENT, "M must be >= 0 (got %lld)", (long long)m);
+    if (m > INT32_MAX) return fail(MNB_ERR_INVALID_ARGUMENT, "M must fit in 32 bits");
+    if (m == 1) return gemv_common(w, repacked, nullptr, a, a_dtype, y, stream);
+    if (m > 1 && a_dtype != MNB_F16)
+        return fail(MNB_ERR_UNSUPPORTED, "M>1 GEMM takes fp16 activations only");
+    const size_t need = workspace_for(L, m);
+    if (m == 0 || L.N == 0) return ok("noop");
+    if (workspace_bytes < need)
+        return fail(MNB_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed",
+                    workspace_bytes, need);
+    if (need > 0) MNB_TRY(check_ptr(workspace, 16, "workspace"));
+    MNB_TRY(check_ptr(repacked, 256, "repacked"));
+    MNB_TRY(check_ptr(a, 16, "a"));
+    MNB_TRY(check_ptr(y, 2, "y"));
+    MNB_TRY(check_device());
+    const mnb::WeightView v = mnb::view_of(L, repacked);
+    const char* variant = "";
+    hipError_t e;
+    if (m <= 16)
+        e = mnb::launch_gemm_small(L, v, a, m, y, workspace, static_cast<hipStream_t>(stream), &variant);
+    else
+        e = mnb::launch_gemm_mfma(L, v, a, m, y, static_cast<hipStream_t>(stream), &variant);
+    return launched(e, variant);
+}
+
+mnb_status mnb_unpack_debug(const mnb_weight_desc* w, const void* repacked, uint8_t* codes,
+                            float* w_f32, void* stream)
+{
+    Layout L;
+    MNB_TRY(check_desc(w, &L));
+    MNB_TRY(check_ptr(repacked, 256, "repacked"));
+    if (L.N == 0 || (!codes && !w_f32)) return ok("unpack_debug");
+    if (w_f32) MNB_TRY(check_ptr(w_f32, 4, "w_f32"));
+    MNB_TRY(check_device());
+    return launched(mnb::launch_unpack_debug(L, repacked, codes, w_f32,
+                                             static_cast<hipStream_t>(stream)),
+                    "unpack_debug");
+}
+
+const char* mnb_status_string(mnb_status s)
+{
+    switch (s) {
+    case MNB_OK: return "MNB_OK";
+    case MNB_ERR_INVALID_ARGUMENT: return "MNB_ERR_INVALID_ARGUMENT";
+    case MNB_ERR_UNSUPPORTED: return "MNB_ERR_UNSUPPORTED";
+    case MNB_ERR_DEVICE: return "MNB_ERR_DEVICE";
+    }
+    return "MNB_ERR_UNKNOWN";
+}
+
+const char* mnb_last_error(void) { return g_error.c_str(); }
+
+const char* mnb_last_variant(void) { return g_variant; }
+
+}  // extern "C"

@@ -1,0 +1,74 @@
+// mnb_device.hpp -- device helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#include "mnb_layout.hpp"
+
+namespace mnb {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ h2_t as_h2(uint32_t x) { return __builtin_bit_cast(h2_t, x); }
+__device__ __forceinline__ uint32_t as_u32(h2_t x) { return __builtin_bit_cast(uint32_t, x); }
+
+// Per-group constants of the magic-number unpack, as packed fp16 pairs.
+//   neg1024z = -(1024 + z): OR-ing a nibble c into the mantissa of fp16
+//              1024.0 (0x6400) gives exactly 1024 + c; adding this gives c - z.
+//   neg64z   = -(64 + z):   a nibble OR-ed one position higher (bits 4..7)
+//              gives 1024 + 16c; times 1/16 plus this gives c - z.
+// Both results are small integers, so every step is exact in fp16.  This is
+// the integer-to-half trick of the fp16 GEMVs of onnx-runtime-ep-cuda
+// 0.1.0-dev.3, src/kernels/matmul_nbits.rs, re-derived from the binary16
+// format, with the zero point folded into the subtracted constant.
+struct ZpConst {
+    uint32_t neg1024z;
+    uint32_t neg64z;
+};
+
+__device__ __forceinline__ ZpConst zp_const(uint32_t z)
+{
+    const uint32_t a = 0xE400u | z;            // -(1024 + z)
+    const uint32_t b = 0xD400u + (z << 4);     // -(64 + z)
+    return ZpConst{a | (a << 16), b | (b << 16)};
+}
+
+// Unpack one repacked word (8 nibbles, slots holding k-offsets
+// 0,2,4,6,1,3,5,7) into (c - z) as 4 fp16 pairs in k order:
+// (k0,k1), (k2,k3), (k4,k5), (k6,k7).
+__device__ __forceinline__ void unpack8(uint32_t d, ZpConst zc, h2_t out[4])
+{
+    const h2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const uint32_t d8 = d >> 8;
+    out[0] = as_h2((d & 0x000F000Fu) | 0x64006400u) + as_h2(zc.neg1024z);
+    out[1] = as_h2((d & 0x00F000F0u) | 0x64006400u) * sixteenth + as_h2(zc.neg64z);
+    out[2] = as_h2((d8 & 0x000F000Fu) | 0x64006400u) + as_h2(zc.neg1024z);
+    out[3] = as_h2((d8 & 0x00F000F0u) | 0x64006400u) * sixteenth + as_h2(zc.neg64z);
+}
+
+// The code of k-offset i (0..7) of a repacked word.
+__device__ __forceinline__ uint32_t code_at(uint32_t d, int i)
+{
+    return (d >> (4 * nibble_slot(i))) & 15u;
+}
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__half x) { return __half2float(x); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ __half from_f32<__half>(float x) { return __float2half_rn(x); }
+
+// Workgroup barrier that orders LDS traffic only: outstanding global loads
+// stay in flight across it.
+__device__ __forceinline__ void block_sync_lds()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+}  // namespace mnb

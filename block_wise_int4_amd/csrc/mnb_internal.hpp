@@ -1,0 +1,45 @@
+// mnb_internal.hpp -- kernel launchers behind the C ABI (library-internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mnb_layout.hpp"
+
+namespace mnb {
+
+// Pointers to the three sections of one repacked weight.
+struct WeightView {
+    const uint8_t* codes;
+    const void* scales;
+    const uint8_t* zp;  // nullptr without zero points
+};
+
+inline WeightView view_of(const Layout& L, const void* repacked)
+{
+    const uint8_t* b = static_cast<const uint8_t*>(repacked);
+    return WeightView{b + L.codes_off, b + L.scales_off, L.has_zp ? b + L.zp_off : nullptr};
+}
+
+hipError_t launch_repack(const Layout& L, const uint8_t* packed, const void* scales,
+                         const uint8_t* zp, void* repacked, hipStream_t stream);
+hipError_t launch_unpack_debug(const Layout& L, const void* repacked, uint8_t* codes, float* w,
+                               hipStream_t stream);
+
+// Largest K the decode GEMV stages in LDS, per activation dtype.
+int64_t gemv_max_k(bool f16_act);
+// y = a . dequant(B)^T (up == nullptr) or silu(a . Bg^T) * (a . Bu^T).
+hipError_t launch_gemv(const Layout& L, const WeightView& gate, const WeightView* up,
+                       const void* a, bool f16_act, void* y, hipStream_t stream,
+                       const char** variant);
+
+// 2 <= M <= 16, fp16 activations.
+size_t gemm_small_workspace(const Layout& L, int64_t m);
+hipError_t launch_gemm_small(const Layout& L, const WeightView& w, const void* a, int64_t m,
+                             void* y, void* ws, hipStream_t stream, const char** variant);
+
+// M > 16, fp16 activations.
+hipError_t launch_gemm_mfma(const Layout& L, const WeightView& w, const void* a, int64_t m,
+                            void* y, hipStream_t stream, const char** variant);
+
+}  // namespace mnb

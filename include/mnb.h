@@ -1,0 +1,204 @@
+/*
+ * mnb.h -- C ABI of libmnb: block-wise int4 weight-only matmul in the ONNX
+ * MatMulNBits layout, on AMD MI355X (gfx950).
+ *
+ *   Y[M,N] = A[M,K] . dequant(B)^T,
+ *   dequant(B)[n,k] = (code[n,k] - zp[n, k/group]) * scale[n, k/group]
+ *
+ * The operation and the input format are those of the module doc of
+ * onnx-runtime-ep-cuda 0.1.0-dev.6, src/kernels/marlin_gemm.rs, section
+ * "ONNX MatMulNBits int4 format (input to the repack)":
+ *   packed       u8 [N, k_blocks, group/2]; the nibble of (n,k) is in byte
+ *                (n*k_blocks + k/group)*(group/2) + (k%group)/2, low nibble
+ *                for even k, high nibble for odd k; code in 0..15.
+ *   scales       [N, k_blocks], fp16 or fp32 (a flat [N*k_blocks] array has
+ *                the same memory).
+ *   zero_points  optional u8 [N, ceil(k_blocks/2)]; the nibble of (n,block) is
+ *                in byte n*ceil(k_blocks/2) + block/2, low nibble for even
+ *                block.  When absent every zero point is 8.
+ * with k_blocks = ceil(K/group).  onnx-runtime-ep-cuda 0.1.0-dev.3,
+ * src/kernels/matmul_nbits.rs (MatMulNBitsFactory::create, run, run_f16)
+ * fixes the operand dtypes: A is fp16 or fp32, Y has A's dtype, scales are
+ * fp16 or fp32 independently of A, bits = 4 only.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers named "device" are HIP device pointers (any allocation visible
+ *   to the current device); descriptors are host pointers.  Device buffers
+ *   must be 16-byte aligned, except y, which needs element alignment.  All
+ *   arrays are dense and row-major.
+ * - `stream` is a hipStream_t passed as void*; NULL means the null stream.
+ *   Every call only enqueues work on `stream` and returns; it never
+ *   allocates, frees, synchronises, or copies between host and device, and
+ *   its grid depends on the shapes only, so a call can be recorded into a
+ *   HIP graph (the capture-safety convention of the MatMulNBits kernels on
+ *   the onnx-runtime-ep-cuda pages: static grid, no per-call allocation).
+ * - The caller owns every buffer.  A repacked buffer is immutable once the
+ *   repack that wrote it has completed; calls that read it may overlap.
+ * - All arguments are validated on the host before any HIP call.  A failing
+ *   check returns an error status and enqueues nothing; mnb_last_error()
+ *   then gives the reason ("mnb: ..."), in the calling thread.
+ *   MNB_ERR_INVALID_ARGUMENT: a malformed request (null pointer, bad size or
+ *     enum, misalignment, workspace too small, size overflow).
+ *   MNB_ERR_UNSUPPORTED: a valid MatMulNBits request this library does not
+ *     implement (K not a multiple of group, group outside 16/32/64/128, a
+ *     dtype pairing other than the ones below).  The library never computes
+ *     something else instead (the "Unsupported" convention of ferrox-cuda
+ *     gpu.rs, enum CudaError), and never falls back internally.
+ *   MNB_ERR_DEVICE: no usable gfx950 device, or the launch failed.
+ * - m == 0 or n == 0 is a no-op returning MNB_OK.
+ * - Offsets are computed in 64-bit; sizes whose byte counts overflow are
+ *   rejected.
+ *
+ * Repacked layout (written by mnb_repack, read by every other call)
+ * -----------------------------------------------------------------
+ * A permutation of the ONNX nibbles plus a re-indexing of scales and zero
+ * points (no expansion: the same bytes plus padding to whole tiles).  Let
+ *   T = ceil(N/16)   column tiles of 16 columns,
+ *   C = ceil(K/128)  k-chunks of 128 k,
+ *   Q = 128/group    groups per k-chunk (8, 4, 2 or 1),
+ *   ss = 2 (fp16 scales) or 4 (fp32 scales),
+ *   align(x) = x rounded up to a multiple of 256.
+ * Section CODES, offset 0, T*C*1024 bytes.  Chunk (t,c) is the 1024 bytes at
+ *   ((t*C) + c) * 1024.  Inside it, lane L in 0..63 owns bytes
+ *   [16L, 16L+16) = four little-endian 32-bit words D_j, j = 0..3.  D_j holds
+ *   column n = 16t + (L mod 16) and the 8 values k = 128c + 32j + 8*(L div 16)
+ *   + i, i = 0..7; the code of offset i is the nibble at bits [4p, 4p+4) with
+ *   p = (0,4,1,5,2,6,3,7)[i] (nibble slots 0..7 hold i = 0,2,4,6,1,3,5,7).
+ *   Columns n >= N and k >= K hold code 0.
+ * Section SCALES, offset S0 = align(T*C*1024), T*C*16*Q scale values of the
+ *   scale dtype.  Chunk (t,c) owns elements [((t*C)+c)*16Q, +16Q).  The scale
+ *   of column i = n mod 16 and in-chunk group q = (k mod 128)/group sits at
+ *   slot s(i,q) = i*Q + q when Q <= 4, and s(i,q) = ((q mod 2)*16 + i)*4 +
+ *   q div 2 when Q = 8.  Columns n >= N and groups >= K/group hold 0.
+ * Section ZERO_POINTS, present iff has_zero_points, offset
+ *   Z0 = align(S0 + T*C*16*Q*ss), T*C*8*Q bytes.  Chunk (t,c) owns bytes
+ *   [((t*C)+c)*8Q, +8Q); the zero point of slot s is the nibble of byte s/2,
+ *   low nibble for even s.  Padding holds 0.
+ * Total size mnb_repacked_bytes() = align(end of the last section).
+ * The 16-lane x 8-k ownership is the B-operand distribution of the gfx950
+ * v_mfma_f32_16x16x32_f16 instruction, so the same bytes feed the decode
+ * GEMVs (one 128-bit load per lane per chunk) and the MFMA GEMMs.
+ */
+#ifndef MNB_H
+#define MNB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MNB_OK = 0,
+    MNB_ERR_INVALID_ARGUMENT = 1,
+    MNB_ERR_UNSUPPORTED = 2,
+    MNB_ERR_DEVICE = 3
+} mnb_status;
+
+typedef enum { MNB_F32 = 0, MNB_F16 = 1 } mnb_dtype;
+
+/* One quantized weight B[N,K].  group_size in {16,32,64,128} and K % group
+ * == 0 (the GEMM tiles of marlin_gemm.rs demand the same); scale_dtype is an
+ * mnb_dtype; has_zero_points is 0 or 1. */
+typedef struct {
+    int64_t n;
+    int64_t k;
+    int32_t group_size;
+    int32_t has_zero_points;
+    int32_t scale_dtype;
+    int32_t reserved; /* must be 0 */
+} mnb_weight_desc;
+
+/* Byte offsets of the repacked sections (see "Repacked layout"). */
+typedef struct {
+    int64_t tiles, chunks, groups_per_chunk;
+    int64_t codes_offset, codes_bytes;
+    int64_t scales_offset, scales_bytes;
+    int64_t zero_points_offset, zero_points_bytes; /* 0, 0 without zero points */
+    int64_t total_bytes;
+} mnb_layout;
+
+/* Size in bytes of the repacked buffer for `w`; 0 if `w` is invalid or
+ * unsupported (mnb_last_error() says why).  Host only, no HIP call.  The
+ * size-query convention of marlin_gemm.rs, fn repacked_bytes. */
+size_t mnb_repacked_bytes(const mnb_weight_desc* w);
+
+/* Section offsets of the repacked buffer for `w` into *out.  Host only. */
+mnb_status mnb_repacked_layout(const mnb_weight_desc* w, mnb_layout* out);
+
+/* Offline repack (the weight reordering of marlin_gemm.rs, fn
+ * repack_int4_weights and kernel matmul_nbits_marlin_repack, re-targeted to
+ * the layout above).  Reads the ONNX operands from device memory:
+ *   packed       u8 [N, k_blocks, group/2]
+ *   scales       [N, k_blocks] in w->scale_dtype
+ *   zero_points  u8 [N, ceil(k_blocks/2)]; must be NULL iff
+ *                !w->has_zero_points
+ * and writes every byte of `repacked` (device, mnb_repacked_bytes(w) bytes,
+ * 256-byte aligned), padding included.  Asynchronous on `stream`. */
+mnb_status mnb_repack(const mnb_weight_desc* w, const uint8_t* packed, const void* scales,
+                      const uint8_t* zero_points, void* repacked, void* stream);
+
+/* Decode GEMV, M = 1 (the f32 GEMV and the fp16 GEMVs of matmul_nbits.rs):
+ *   y[n] = sum_k a[k] * dequant(B)[n,k]   for n < N,
+ * with a (device, [K]) and y (device, [N]) both of a_dtype (MNB_F16 or
+ * MNB_F32).  Products accumulate in fp32; fp16 outputs are rounded once
+ * (round to nearest even). */
+mnb_status mnb_gemv(const mnb_weight_desc* w, const void* repacked, const void* a,
+                    int32_t a_dtype, void* y, void* stream);
+
+/* Fused gate/up projection + SwiGLU, M = 1 (kernel
+ * matmul_nbits_gemv_f16_gate_up_swiglu of matmul_nbits.rs):
+ *   y[n] = silu(g[n]) * u[n],  g = a . dequant(B_gate)^T,
+ *   u = a . dequant(B_up)^T,   silu(x) = x / (1 + e^-x).
+ * Gate and up share the descriptor `w` (same N, K, group, dtypes).  a is
+ * [K], y is [N], both of a_dtype; g and u are kept in fp32 (not rounded)
+ * before the activation. */
+mnb_status mnb_gemv_gate_up_swiglu(const mnb_weight_desc* w, const void* gate_repacked,
+                                   const void* up_repacked, const void* a, int32_t a_dtype,
+                                   void* y, void* stream);
+
+/* Workspace in bytes that mnb_gemm needs for (w, m); 0 when none.  Host
+ * only.  Like splitk_partials_len of marlin_gemm.rs. */
+size_t mnb_gemm_workspace_bytes(const mnb_weight_desc* w, int64_t m);
+
+/* GEMM for any M >= 1 (marlin_gemm.rs, kernels matmul_nbits_marlin_gemm_f16
+ * and its split-K form, re-designed for gfx950):
+ *   Y[m,n] = sum_k A[m,k] * dequant(B)[n,k],
+ * A (device, [M,K]) and Y (device, [M,N]) of a_dtype.  M = 1 runs the decode
+ * GEMV; 2 <= M <= 16 a weight-streaming MFMA kernel (with a fixed-order
+ * split-K reduction through `workspace` when that fills the chip better);
+ * larger M the MFMA prefill GEMM.  The GEMM paths take fp16 A only
+ * (MNB_ERR_UNSUPPORTED for fp32 A with M > 1).  Products are fp16 x fp16 on
+ * the matrix cores with fp32 accumulation; each group's partial sum is
+ * multiplied by its scale after that group's accumulation.  `workspace`
+ * (device, 16-byte aligned) must hold mnb_gemm_workspace_bytes(w, m) bytes;
+ * it may be NULL when that is 0.  Results are deterministic. */
+mnb_status mnb_gemm(const mnb_weight_desc* w, const void* repacked, const void* a, int64_t m,
+                    int32_t a_dtype, void* y, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Test-only: decode a repacked buffer with the production unpack code.
+ * codes: device u8 [N,K] (the stored nibbles); w_f32: device f32 [N,K], the
+ * dequantized weights (code - zp) * scale rounded once to fp32.  Either
+ * output may be NULL. */
+mnb_status mnb_unpack_debug(const mnb_weight_desc* w, const void* repacked, uint8_t* codes,
+                            float* w_f32, void* stream);
+
+/* Static string naming a status. */
+const char* mnb_status_string(mnb_status s);
+
+/* Reason for the last non-OK status returned in this thread ("" if none). */
+const char* mnb_last_error(void);
+
+/* Name of the kernel variant the last successful call in this thread
+ * enqueued (the dispatch record of matmul_nbits.rs, record_kernel_variant),
+ * e.g. "gemv_f16" or "gemm_small_m"; "" if none. */
+const char* mnb_last_variant(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MNB_H */

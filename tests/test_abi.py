@@ -1,0 +1,167 @@
+"""C-ABI boundary tests that need no GPU: the library loads, exports every
+symbol include/mnb.h declares, and validates every argument on the host
+(errors are returned before any HIP call).  A well-formed request with no
+usable device returns MNB_ERR_DEVICE instead of aborting."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from block_wise_int4_amd import mnb
+from tests import layout_ref
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mnb.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mnb_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    declared = _declared_functions()
+    assert set(declared) == set(mnb.EXPORTS), declared
+    out = subprocess.run(["nm", "-D", "--defined-only", mnb.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (mnb_[a-z_]+)\b", out))
+    for name in declared:
+        assert name in exported, name
+        assert hasattr(mnb.lib, name)
+
+
+def test_status_strings():
+    assert mnb.mnb_status_string(0) == "MNB_OK"
+    assert mnb.mnb_status_string(1) == "MNB_ERR_INVALID_ARGUMENT"
+    assert mnb.mnb_status_string(2) == "MNB_ERR_UNSUPPORTED"
+    assert mnb.mnb_status_string(3) == "MNB_ERR_DEVICE"
+
+
+@pytest.mark.parametrize("N,K,g,zp,f16", [
+    (4096, 4096, 32, True, True), (11008, 4096, 128, False, True), (256, 256, 32, False, False),
+    (14336, 4096, 64, True, True), (5, 48, 16, True, False), (70, 384, 128, True, True),
+    (1, 16, 16, False, True), (130, 4352, 64, False, False)])
+def test_repacked_size_and_layout_match_the_documented_formula(N, K, g, zp, f16):
+    d = mnb.desc(N, K, g, zp, mnb.MNB_F16 if f16 else mnb.MNB_F32)
+    G = layout_ref.geometry(N, K, g, zp, f16)
+    assert mnb.mnb_repacked_bytes(d) == G["total"]
+    L = mnb.mnb_repacked_layout(d)
+    assert L["tiles"] == G["T"] and L["chunks"] == G["C"] and L["groups_per_chunk"] == G["Q"]
+    assert L["codes_offset"] == 0 and L["codes_bytes"] == G["T"] * G["C"] * 1024
+    assert L["scales_offset"] == G["S0"]
+    assert L["zero_points_offset"] == G["Z0"]
+    assert L["total_bytes"] == G["total"]
+    # no expansion beyond tile padding: ONNX bytes vs repacked bytes
+    kb = K // g
+    onnx = N * K // 2 + N * kb * (2 if f16 else 4) + (N * ((kb + 1) // 2) if zp else 0)
+    padded = G["T"] * 16 * G["C"] * 128
+    assert G["total"] <= onnx * padded / (N * K) + 3 * 256 + G["T"] * G["C"] * 16 * 128 // 8
+
+
+def test_host_layout_model_is_a_bijection():
+    # the numpy model used by the GPU tests inverts itself on ragged shapes
+    rng = np.random.default_rng(1)
+    for (N, K, g) in ((5, 48, 16), (70, 384, 128), (17, 160, 32), (33, 4096, 64)):
+        codes = rng.integers(0, 16, (N, K), dtype=np.uint8)
+        kb = K // g
+        z = rng.integers(0, 16, (N, kb), dtype=np.uint8)
+        s = rng.uniform(0.01, 0.02, (N, kb)).astype(np.float16)
+        buf = layout_ref.repack_ref(codes, z, s, g, True)
+        assert (layout_ref.unrepack_codes(buf, N, K, g, True, True) == codes).all()
+        # a permutation: the code section holds every nibble exactly once
+        G = layout_ref.geometry(N, K, g, True, True)
+        nib = np.concatenate([buf[:G["T"] * G["C"] * 1024] & 15, buf[:G["T"] * G["C"] * 1024] >> 4])
+        assert np.bincount(nib, minlength=16)[1:].sum() == np.count_nonzero(codes)
+
+
+def _expect(status, call, *args):
+    r = call(*args)
+    assert r == status, (r, mnb.mnb_last_error())
+    assert mnb.mnb_last_error().startswith("mnb: ")
+    return mnb.mnb_last_error()
+
+
+FAKE = 1 << 40          # a 256-byte-aligned non-null address; never dereferenced
+D = ctypes.byref
+
+
+def test_descriptor_validation():
+    lib = mnb.lib
+    bad = [
+        (mnb.desc(16, 0, 32, False, mnb.MNB_F16), mnb.MNB_ERR_INVALID_ARGUMENT),
+        (mnb.desc(-1, 64, 32, False, mnb.MNB_F16), mnb.MNB_ERR_INVALID_ARGUMENT),
+        (mnb.desc(16, 64, 8, False, mnb.MNB_F16), mnb.MNB_ERR_INVALID_ARGUMENT),
+        (mnb.desc(16, 96, 48, False, mnb.MNB_F16), mnb.MNB_ERR_INVALID_ARGUMENT),
+        (mnb.desc(16, 512, 256, False, mnb.MNB_F16), mnb.MNB_ERR_UNSUPPORTED),
+        (mnb.desc(16, 40, 32, False, mnb.MNB_F16), mnb.MNB_ERR_UNSUPPORTED),
+        (mnb.desc(16, 64, 32, False, 7), mnb.MNB_ERR_INVALID_ARGUMENT),
+        (mnb.mnb_weight_desc(16, 64, 32, 2, 1, 0), mnb.MNB_ERR_INVALID_ARGUMENT),
+        (mnb.mnb_weight_desc(16, 64, 32, 0, 1, 5), mnb.MNB_ERR_INVALID_ARGUMENT),
+        (mnb.desc(1 << 33, 64, 32, False, mnb.MNB_F16), mnb.MNB_ERR_INVALID_ARGUMENT),
+    ]
+    for d, status in bad:
+        assert lib.mnb_repacked_bytes(D(d)) == 0
+        _expect(status, lib.mnb_gemv, D(d), FAKE, FAKE, mnb.MNB_F16, FAKE, None)
+        _expect(status, lib.mnb_gemm, D(d), FAKE, FAKE, 4, mnb.MNB_F16, FAKE, None, 0, None)
+        _expect(status, lib.mnb_repack, D(d), FAKE, FAKE, None, FAKE, None)
+    assert lib.mnb_repacked_bytes(None) == 0
+    _expect(mnb.MNB_ERR_INVALID_ARGUMENT, lib.mnb_gemv, None, FAKE, FAKE, 1, FAKE, None)
+
+
+def test_argument_validation():
+    lib = mnb.lib
+    d = mnb.desc(64, 256, 32, True, mnb.MNB_F16)
+    E = mnb.MNB_ERR_INVALID_ARGUMENT
+    assert "repacked is NULL" in _expect(E, lib.mnb_gemv, D(d), None, FAKE, 1, FAKE, None)
+    assert "aligned" in _expect(E, lib.mnb_gemv, D(d), FAKE + 16, FAKE, 1, FAKE, None)
+    assert "aligned" in _expect(E, lib.mnb_gemv, D(d), FAKE, FAKE + 2, 1, FAKE, None)
+    assert "aligned" in _expect(E, lib.mnb_gemv, D(d), FAKE, FAKE, 1, FAKE + 1, None)
+    assert "a_dtype" in _expect(E, lib.mnb_gemv, D(d), FAKE, FAKE, 9, FAKE, None)
+    assert "up_repacked" in _expect(E, lib.mnb_gemv_gate_up_swiglu, D(d), FAKE, None, FAKE, 1, FAKE, None)
+    # zero points: required iff has_zero_points
+    assert "zero_points" in _expect(E, lib.mnb_repack, D(d), FAKE, FAKE, None, FAKE, None)
+    d0 = mnb.desc(64, 256, 32, False, mnb.MNB_F16)
+    assert "has_zero_points" in _expect(E, lib.mnb_repack, D(d0), FAKE, FAKE, FAKE, FAKE, None)
+    # GEMM: fp32 activations only for M = 1; negative M; workspace size
+    assert "fp16" in _expect(mnb.MNB_ERR_UNSUPPORTED, lib.mnb_gemm, D(d), FAKE, FAKE, 8, mnb.MNB_F32,
+                             FAKE, None, 0, None)
+    _expect(E, lib.mnb_gemm, D(d), FAKE, FAKE, -1, 1, FAKE, None, 0, None)
+    need = lib.mnb_gemm_workspace_bytes(D(mnb.desc(64, 4096, 64, True, 1)), 4)
+    if need:
+        assert "workspace" in _expect(E, lib.mnb_gemm, D(mnb.desc(64, 4096, 64, True, 1)), FAKE,
+                                      FAKE, 4, 1, FAKE, None, need - 1, None)
+    # decode GEMV K limit
+    big = mnb.desc(16, 1 << 20, 128, False, mnb.MNB_F16)
+    assert "limit" in _expect(mnb.MNB_ERR_UNSUPPORTED, lib.mnb_gemv, D(big), FAKE, FAKE, 1, FAKE, None)
+
+
+def test_empty_problems_are_noops_without_a_device():
+    lib = mnb.lib
+    d = mnb.desc(0, 256, 32, True, mnb.MNB_F16)
+    assert lib.mnb_gemv(D(d), None, None, 1, None, None) == mnb.MNB_OK
+    assert lib.mnb_gemm(D(d), None, None, 5, 1, None, None, 0, None) == mnb.MNB_OK
+    d = mnb.desc(64, 256, 32, True, mnb.MNB_F16)
+    assert lib.mnb_gemm(D(d), None, None, 0, 1, None, None, 0, None) == mnb.MNB_OK
+
+
+def test_no_device_is_an_error_not_an_abort():
+    try:
+        import torch
+        if torch.cuda.is_available():
+            pytest.skip("a GPU is visible")
+    except ImportError:
+        pass
+    lib = mnb.lib
+    d = mnb.desc(64, 256, 32, True, mnb.MNB_F16)
+    r = lib.mnb_gemv(D(d), FAKE, FAKE, 1, FAKE, None)
+    assert r == mnb.MNB_ERR_DEVICE, mnb.mnb_last_error()
+    assert "device" in mnb.mnb_last_error()
+
+
+def test_one_hip_runtime_in_the_process():
+    # torch's HIP runtime and libmnb's must be the same library instance
+    runtimes = mnb._hip_runtimes_mapped()
+    assert len(runtimes) == 1, runtimes

@@ -1,0 +1,347 @@
+"""GPU parity: the HIP path, called through the C ABI, against the fp64 CPU
+oracle on the same seeded inputs.
+
+Bars: repacked bytes, unpacked codes and dequantized weights bit-exact;
+outputs within |gpu - oracle| <= 1e-3 * sum_k |a_k w_nk| + 1e-5 per element
+(NaN == NaN agrees); the fused SwiGLU output within the bound propagated from
+that one (oracle.swiglu_bound).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from block_wise_int4_amd import synth
+from oracle import oracle as o
+from tests import gpu_util as G
+from tests import layout_ref
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mnb():
+    from block_wise_int4_amd import mnb as m
+    return m
+
+
+def _weight(N, K, g, sdt="f16", zp=True, seed=0, lo=0.005, hi=0.02):
+    return synth.weight(N, K, g, sdt, (lo, hi), zp, (100, N, K, g, seed))
+
+
+def _act(M, K, dtype="f16", sigma=1.0, seed=0):
+    return synth.activation(M, K, dtype, sigma, (200, M, K, seed))
+
+
+# ---------------------------------------------------------------- repack ----
+
+REPACK_CASES = [
+    (1, 16, 16, "f32", False), (5, 48, 16, "f16", True), (70, 384, 128, "f16", True),
+    (130, 160, 32, "f32", True), (33, 4096, 64, "f16", False), (200, 640, 64, "f16", True),
+    (17, 96, 32, "f16", True), (256, 256, 32, "f32", False)]
+
+
+@pytest.mark.parametrize("N,K,g,sdt,zp", REPACK_CASES)
+def test_repack_bytes_match_the_documented_layout(mnb, N, K, g, sdt, zp):
+    w = _weight(N, K, g, sdt, zp)
+    q = G.upload(w)
+    got = q.repacked.cpu().numpy()
+    codes = o.unpack_codes(w.packed, N, K, g)
+    z = o.unpack_zero_points(w.zero_points, N, K, g)
+    want = layout_ref.repack_ref(codes, z, w.scales, g, zp)
+    assert got.size == want.size
+    assert (got == want).all(), np.argwhere(got != want)[:10]
+
+
+@pytest.mark.parametrize("N,K,g,sdt,zp", REPACK_CASES)
+def test_unpacked_codes_and_weights_are_bit_exact(mnb, N, K, g, sdt, zp):
+    t = G.torch()
+    w = _weight(N, K, g, sdt, zp)
+    q = G.upload(w)
+    codes = t.empty((N, K), dtype=t.uint8, device="cuda")
+    wf = t.empty((N, K), dtype=t.float32, device="cuda")
+    mnb.mnb_unpack_debug(q.desc, q.repacked, codes, wf)
+    t.cuda.synchronize()
+    assert (codes.cpu().numpy() == o.unpack_codes(w.packed, N, K, g)).all()
+    want = o.dequant(w.packed, w.scales, w.zero_points, N, K, g).astype(np.float32)
+    got = wf.cpu().numpy()
+    assert (got.view(np.uint32) == want.view(np.uint32)).all()
+
+
+# --------------------------------------------------------- worked examples --
+
+def _golden():
+    path = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
+    return json.load(open(path))["examples"]
+
+
+def test_worked_examples_through_the_f32_gemv(mnb):
+    """Hand-derived values (tests/golden) are exactly representable, so the
+    fp32 GEMV must reproduce them bit for bit."""
+    t = G.torch()
+    from tests.test_oracle import _example_operands, _case_A
+    for ex in _golden():
+        N, K, g, packed, zp, scales = _example_operands(ex)
+        if K % g:
+            d = mnb.desc(N, K, g, zp is not None, mnb.MNB_F32)
+            with pytest.raises(mnb.MnbError) as e:
+                mnb.mnb_repacked_layout(d)
+            assert e.value.status == mnb.MNB_ERR_UNSUPPORTED
+            continue
+        q = mnb.repack(G.to_dev(packed), G.to_dev(scales.reshape(-1)),
+                       None if zp is None else G.to_dev(zp), N, K, g)
+        for case in ex["cases"]:
+            a = G.to_dev(_case_A(case["A"], K).reshape(-1))
+            y = t.empty(N, dtype=t.float32, device="cuda")
+            mnb.mnb_gemv(q.desc, q.repacked, a, y)
+            assert G.host(y).tolist() == case["Y"], (ex["name"], case["A"])
+
+
+# ------------------------------------------------------------------ GEMV ----
+
+GEMV_CASES = [
+    # N, K, g, act, scale dtype, zp
+    (256, 256, 32, "f32", "f32", False),      # tiny GEMV workload
+    (4096, 4096, 32, "f16", "f16", True),     # decode GEMV workload
+    (70, 4096, 32, "f16", "f16", False),
+    (130, 384, 128, "f16", "f32", True),
+    (5, 48, 16, "f16", "f16", True),
+    (200, 640, 64, "f32", "f16", True),
+    (1, 16, 16, "f32", "f32", True),
+    (333, 2176, 16, "f16", "f16", True),
+    (4864, 896, 32, "f16", "f16", False),
+    (96, 11008, 128, "f16", "f16", True),
+]
+
+
+@pytest.mark.parametrize("N,K,g,adt,sdt,zp", GEMV_CASES)
+def test_gemv_parity(mnb, N, K, g, adt, sdt, zp):
+    t = G.torch()
+    w = _weight(N, K, g, sdt, zp)
+    A = _act(1, K, adt)
+    q = G.upload(w)
+    y = t.empty(N, dtype=t.float16 if adt == "f16" else t.float32, device="cuda")
+    mnb.mnb_gemv(q.desc, q.repacked, G.to_dev(A.reshape(-1)), y)
+    assert mnb.mnb_last_variant() == ("gemv_" + adt)
+    Y, B, _ = G.oracle_dense(A, w)
+    G.assert_within(G.host(y)[None, :], Y, B, "gemv N=%d K=%d g=%d %s" % (N, K, g, adt))
+    # mnb_gemm with M = 1 is the same kernel and the same bits
+    y2 = t.empty_like(y)
+    mnb.mnb_gemm(q.desc, q.repacked, G.to_dev(A), 1, y2)
+    assert t.equal(y, y2)
+
+
+def test_tiny_gemv_workload_exact_match_with_one_hot_rows(mnb):
+    """One-hot activations pull single dequantized weights through the f32
+    GEMV: the result is the exact product (code - zp) * scale rounded once to
+    fp32."""
+    t = G.torch()
+    wl = synth.TINY_GEMV
+    w = synth.workload_weights(wl)
+    q = G.upload(w)
+    W = o.dequant(w.packed, w.scales, w.zero_points, w.N, w.K, w.group)
+    for k in (0, 1, 31, 32, 127, 255):
+        a = np.zeros(wl.K, np.float32)
+        a[k] = 1.0
+        y = t.empty(wl.N, dtype=t.float32, device="cuda")
+        mnb.mnb_gemv(q.desc, q.repacked, G.to_dev(a), y)
+        got = y.cpu().numpy()
+        assert (got.view(np.uint32) == W[:, k].astype(np.float32).view(np.uint32)).all(), k
+
+
+# ------------------------------------------------------- gate/up SwiGLU ----
+
+GATE_UP_CASES = [(11008, 4096, 128, "f16"), (4864, 896, 32, "f16"), (70, 384, 64, "f16"),
+                 (133, 512, 16, "f32")]
+
+
+@pytest.mark.parametrize("N,K,g,adt", GATE_UP_CASES)
+def test_gate_up_swiglu_parity(mnb, N, K, g, adt):
+    t = G.torch()
+    if (N, K, g) == (11008, 4096, 128):
+        wg, wu = synth.workload_weights(synth.GATE_UP_SWIGLU)
+        A = synth.workload_activation(synth.GATE_UP_SWIGLU)
+    else:
+        wg = _weight(N, K, g, "f16", False, seed=1, lo=0.002, hi=0.01)
+        wu = _weight(N, K, g, "f16", False, seed=2, lo=0.002, hi=0.01)
+        A = _act(1, K, adt)
+    qg, qu = G.upload(wg), G.upload(wu)
+    odt = t.float16 if adt == "f16" else t.float32
+    a = G.to_dev(A.reshape(-1))
+    y = t.empty(N, dtype=odt, device="cuda")
+    mnb.mnb_gemv_gate_up_swiglu(qg.desc, qg.repacked, qu.repacked, a, y)
+    assert mnb.mnb_last_variant().startswith("gemv_gate_up_swiglu")
+    Yg, Bg, _ = G.oracle_dense(A, wg)
+    Yu, Bu, _ = G.oracle_dense(A, wu)
+    S = o.swiglu(Yg, Yu)
+    G.assert_within(G.host(y)[None, :], S, None, "gate/up N=%d K=%d" % (N, K),
+                    bound=o.swiglu_bound(Yg, Bg, Yu, Bu))
+    # each projection alone through mnb_gemv, under the base bound
+    for q_, Y_, B_ in ((qg, Yg, Bg), (qu, Yu, Bu)):
+        yy = t.empty(N, dtype=odt, device="cuda")
+        mnb.mnb_gemv(q_.desc, q_.repacked, a, yy)
+        G.assert_within(G.host(yy)[None, :], Y_, B_, "projection")
+
+
+# --------------------------------------------------------------- small M ----
+
+@pytest.fixture(scope="module")
+def small_m_workload():
+    w = synth.workload_weights(synth.SMALL_M_GEMM)
+    W64 = o.dequant(w.packed, w.scales, w.zero_points, w.N, w.K, w.group)
+    return w, W64
+
+
+@pytest.mark.parametrize("M", synth.SMALL_M_VALUES)
+def test_small_m_workload_parity(mnb, small_m_workload, M):
+    t = G.torch()
+    w, W64 = small_m_workload
+    A = synth.workload_activation(synth.SMALL_M_GEMM, M)
+    q = G.upload(w)
+    y = t.empty((M, w.N), dtype=t.float16, device="cuda")
+    ws_n = mnb.mnb_gemm_workspace_bytes(q.desc, M)
+    ws = t.empty(max(ws_n, 16), dtype=t.uint8, device="cuda")
+    mnb.mnb_gemm(q.desc, q.repacked, G.to_dev(A), M, y, ws, ws_n)
+    assert mnb.mnb_last_variant() == "gemm_small_m"
+    Y, B, _ = G.oracle_dense(A, w, W64)
+    G.assert_within(G.host(y), Y, B, "small-M M=%d" % M)
+
+
+SMALL_CASES = [(2, 70, 384, 128, True), (3, 130, 160, 32, True), (7, 33, 4096, 64, False),
+               (16, 5, 48, 16, True), (9, 300, 640, 16, False), (5, 257, 896, 32, True)]
+
+
+@pytest.mark.parametrize("M,N,K,g,zp", SMALL_CASES)
+def test_small_m_ragged_parity(mnb, M, N, K, g, zp):
+    t = G.torch()
+    w = _weight(N, K, g, "f16", zp)
+    A = _act(M, K)
+    q = G.upload(w)
+    y = t.empty((M, N), dtype=t.float16, device="cuda")
+    ws_n = mnb.mnb_gemm_workspace_bytes(q.desc, M)
+    ws = t.empty(max(ws_n, 16), dtype=t.uint8, device="cuda")
+    mnb.mnb_gemm(q.desc, q.repacked, G.to_dev(A), M, y, ws, ws_n)
+    Y, B, _ = G.oracle_dense(A, w)
+    G.assert_within(G.host(y), Y, B, "small-M M=%d N=%d K=%d g=%d" % (M, N, K, g))
+
+
+# --------------------------------------------------------------- prefill ----
+
+PREFILL_CASES = [(17, 70, 384, 128, True, "f16"), (130, 300, 512, 64, True, "f16"),
+                 (64, 257, 256, 32, False, "f32"), (33, 40, 160, 16, True, "f16"),
+                 (300, 512, 1024, 128, False, "f16"), (129, 16, 4096, 128, True, "f16")]
+
+
+@pytest.mark.parametrize("M,N,K,g,zp,sdt", PREFILL_CASES)
+def test_prefill_ragged_parity(mnb, M, N, K, g, zp, sdt):
+    t = G.torch()
+    w = _weight(N, K, g, sdt, zp, lo=0.002, hi=0.01)
+    A = _act(M, K, sigma=0.5)
+    q = G.upload(w)
+    y = t.empty((M, N), dtype=t.float16, device="cuda")
+    mnb.mnb_gemm(q.desc, q.repacked, G.to_dev(A), M, y)
+    assert mnb.mnb_last_variant().startswith("gemm_mfma")
+    Y, B, _ = G.oracle_dense(A, w)
+    G.assert_within(G.host(y), Y, B, "prefill M=%d N=%d K=%d g=%d" % (M, N, K, g))
+
+
+def test_prefill_workload_sampled_parity(mnb):
+    """The full prefill workload (M=2048, K=4096, N=14336, g=128) in the
+    launch bench.py times; 6000 outputs checked one by one against the
+    oracle: random ones plus every tile-boundary row/column pattern."""
+    t = G.torch()
+    wl = synth.PREFILL_GEMM
+    w = synth.workload_weights(wl)
+    A = synth.workload_activation(wl)
+    q = G.upload(w)
+    y = t.empty((wl.M, wl.N), dtype=t.float16, device="cuda")
+    mnb.mnb_gemm(q.desc, q.repacked, G.to_dev(A), wl.M, y)
+    yh = G.host(y)
+    rng = np.random.default_rng(5)
+    ms = list(rng.integers(0, wl.M, 4000))
+    ns = list(rng.integers(0, wl.N, 4000))
+    for m in (0, 1, 15, 16, 127, 128, 2047):
+        for n in (0, 15, 16, 63, 64, 255, 256, 14335):
+            ms.append(m)
+            ns.append(n)
+    ms += list(range(0, wl.M, 1))[:1000]
+    ns += list(rng.integers(0, wl.N, 1000))
+    ms, ns = np.array(ms), np.array(ns)
+    Y, B = o.matmul_nbits_at(A, w.packed, w.scales, w.zero_points, wl.N, wl.K, wl.group, ms, ns)
+    G.assert_within(yh[ms, ns], Y, B, "prefill workload (sampled)")
+    assert np.isfinite(yh).all()
+
+
+# ------------------------------------------------------------ properties ----
+
+def test_results_are_deterministic(mnb):
+    t = G.torch()
+    for (M, N, K, g) in ((1, 4096, 4096, 32), (8, 1000, 4096, 64), (200, 512, 1024, 128)):
+        w = _weight(N, K, g)
+        q = G.upload(w)
+        a = G.to_dev(_act(M, K))
+        y1 = t.empty((M, N), dtype=t.float16, device="cuda")
+        y2 = t.empty_like(y1)
+        mnb.mnb_gemm(q.desc, q.repacked, a, M, y1)
+        mnb.mnb_gemm(q.desc, q.repacked, a, M, y2)
+        t.cuda.synchronize()
+        assert t.equal(y1, y2)
+
+
+def test_absent_zero_points_equal_explicit_eights(mnb):
+    t = G.torch()
+    for (M, N, K, g) in ((1, 200, 512, 32), (4, 96, 1024, 64), (40, 64, 256, 128)):
+        w = _weight(N, K, g, zp=False)
+        kb = K // g
+        w8 = synth.Weight(N, K, g, w.packed, w.scales, np.full((N, (kb + 1) // 2), 0x88, np.uint8))
+        q, q8 = G.upload(w), G.upload(w8)
+        a = G.to_dev(_act(M, K))
+        y, y8 = (t.empty((M, N), dtype=t.float16, device="cuda") for _ in range(2))
+        mnb.mnb_gemm(q.desc, q.repacked, a, M, y)
+        mnb.mnb_gemm(q8.desc, q8.repacked, a, M, y8)
+        t.cuda.synchronize()
+        assert t.equal(y, y8)
+
+
+def test_code_equal_to_zero_point_gives_zero(mnb):
+    t = G.torch()
+    for (M, N, K, g) in ((1, 48, 256, 32), (5, 48, 256, 16), (64, 48, 256, 128)):
+        kb = K // g
+        rng = np.random.default_rng(M)
+        z = rng.integers(0, 16, (N, kb), dtype=np.uint8)
+        packed = o.pack_codes(np.repeat(z, g, axis=1), g)
+        w = synth.Weight(N, K, g, packed, rng.uniform(1, 2, (N, kb)).astype(np.float16),
+                         o.pack_zero_points(z))
+        q = G.upload(w)
+        y = t.full((M, N), 7.0, dtype=t.float16, device="cuda")
+        mnb.mnb_gemm(q.desc, q.repacked, G.to_dev(_act(M, K)), M, y)
+        assert (G.host(y) == 0.0).all()
+
+
+def test_nan_and_inf_propagate(mnb):
+    t = G.torch()
+    for (M, N, K, g) in ((1, 40, 256, 32), (3, 40, 256, 32), (20, 40, 256, 32)):
+        w = _weight(N, K, g)
+        A = _act(M, K)
+        A[0, 7] = np.nan
+        if M > 1:
+            A[M - 1, 100] = np.inf
+        q = G.upload(w)
+        y = t.empty((M, N), dtype=t.float16, device="cuda")
+        mnb.mnb_gemm(q.desc, q.repacked, G.to_dev(A), M, y)
+        Y, B, _ = G.oracle_dense(A, w)
+        G.assert_within(G.host(y), Y, B, "nan/inf M=%d" % M)
+
+
+def test_empty_and_unsupported_requests(mnb):
+    t = G.torch()
+    w = _weight(64, 256, 32)
+    q = G.upload(w)
+    y = t.full((1, 64), 3.0, dtype=t.float16, device="cuda")
+    mnb.mnb_gemm(q.desc, q.repacked, G.to_dev(_act(1, 256)), 0, y)
+    assert (G.host(y) == 3.0).all()
+    with pytest.raises(mnb.MnbError) as e:
+        mnb.mnb_gemm(q.desc, q.repacked, G.to_dev(_act(4, 256, "f32")), 4,
+                     t.empty((4, 64), dtype=t.float32, device="cuda"))
+    assert e.value.status == mnb.MNB_ERR_UNSUPPORTED
