@@ -8,8 +8,10 @@ so the working set (> 1 GiB per workload) defeats the 256 MB Infinity Cache:
   gate/up SwiGLU   M=1  K=4096 N=11008 g=128 fp16 (two weights, fused)
   small-M GEMM     M=2,4,8,16 K=4096 N=14336 g=64 fp16, asymmetric zero points
   prefill GEMM     M=2048 K=4096 N=14336 g=128 fp16, asymmetric zero points
-Every kernel is timed with HIP events on the stream it is launched on.  The
-headline value is the decode GEMV's effective bandwidth: algorithmic bytes
+Each workload's R launches are recorded once into a HIP graph; every step
+replays the graphs, timed with HIP events on the replay stream, so the
+figures are back-to-back GPU time (kernel plus dispatch gap), not the host's
+launch rate.  The headline value is the decode GEMV's effective bandwidth: algorithmic bytes
 (ONNX-layout codes + scales + zero points + A + Y) per launch over the
 average launch duration.  The prefill GEMM is reported in TFLOP/s (2MNK).
 Prints one JSON line.
@@ -91,6 +93,22 @@ class Workload:
                 mnb.mnb_gemv_gate_up_swiglu(self.desc, ws[0], ws[1], a, y)
             else:
                 mnb.mnb_gemm(self.desc, ws[0], a, self.M, y, self.workspaces[r], self.ws_bytes)
+        self.variant = mnb.mnb_last_variant()
+
+    def capture(self):
+        """Record the R launches into one HIP graph, so a replay measures the
+        GPU (back-to-back kernels) rather than the host's launch rate."""
+        import torch
+        self.launch_all()                      # first-call setup outside capture
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(self.graph, stream=s):
+                self.launch_all()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
 
     def run(self, timed):
         import torch
@@ -98,7 +116,7 @@ class Workload:
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record()
-        self.launch_all()
+        self.graph.replay()
         if timed:
             e1.record()
             self.events = getattr(self, "events", []) + [(e0, e1)]
@@ -107,7 +125,6 @@ class Workload:
         from block_wise_int4_amd import mnb
         total = sum(a.elapsed_time(b) for a, b in self.events)
         self.avg_launch_ms = total / (len(self.events) * self.R)
-        self.variant = mnb.mnb_last_variant()
         s = self.avg_launch_ms * 1e-3
         return {"workload": self.name, "variant": self.variant, "avg_launch_us": round(s * 1e6, 3),
                 "rotating_copies": self.R, "algorithmic_bytes": self.bytes, "flops": self.flops,
@@ -188,6 +205,8 @@ def main():
     from block_wise_int4_amd import mnb  # noqa: F401  (loads libmnb.so; fails loudly if absent)
     torch.cuda.set_device(0)
     wls = build_workloads(args.only)
+    for w in wls:
+        w.capture()
     for _ in range(args.warmup):
         for w in wls:
             w.run(timed=False)

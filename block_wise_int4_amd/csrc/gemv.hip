@@ -8,11 +8,12 @@
 //
 // gfx950 design: one workgroup per 16-column tile; its waves split the tile's
 // 128-k chunks.  Each lane streams one 16-byte word per chunk (a wave reads
-// a contiguous 1 KiB), unpacks nibbles to exact fp16 (c - z) in registers,
-// and multiplies with v_dot2_f32_f16 against the activation staged once in
-// LDS; each 8-k partial is scaled by its group's scale into an fp32 sum.
-// Lanes of a column reduce with cross-lane moves, waves through LDS, in a
-// fixed order (results are deterministic).
+// a contiguous 1 KiB), unpacks nibbles to exact fp16 (c - z) in registers
+// (already in the B-operand distribution of v_mfma_f32_16x16x32_f16), and
+// the matrix cores multiply them with the activation staged once in LDS and
+// reduce over k; each group's fp32 partial is scaled into an fp32 sum.  fp32
+// activations take a VALU path with fp32 products instead.  Waves reduce
+// through LDS in a fixed order (results are deterministic).
 #include "mnb_device.hpp"
 #include "mnb_internal.hpp"
 
@@ -89,25 +90,64 @@ __device__ __forceinline__ void load_chunk(const GemvWeight& w, int64_t chunk, i
     }
 }
 
-// fp16 activations: partial dot of one 128-bit code word per 32-k step.
+// fp16 activations: the four 32-k steps of one chunk on the matrix cores.
+// Every row of the v_mfma_f32_16x16x32_f16 A operand holds the same 8
+// activations (each lane reads the slice of its k-octet), so all 16 output
+// rows equal the column's partial sum over the step: the instruction does
+// the k-reduction across lanes.  Each group's partial starts from zero and
+// is scaled into the fp32 total once the group is complete.
+__device__ __forceinline__ f4_t mfma16(const h8_t& a, const h8_t& b, const f4_t& c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ h8_t as_h8(const h2_t q[4])
+{
+    h8_t b;
+    b[0] = q[0][0]; b[1] = q[0][1];
+    b[2] = q[1][0]; b[3] = q[1][1];
+    b[4] = q[2][0]; b[5] = q[2][1];
+    b[6] = q[3][0]; b[7] = q[3][1];
+    return b;
+}
+
 template <typename ST, int Q, bool HAS_ZP>
 __device__ __forceinline__ float chunk_dot_f16(const ChunkRegs<ST, Q, HAS_ZP>& r,
                                                const _Float16* as, int c, int h, float acc)
 {
     constexpr int NS = LaneGroups<Q>::NS;
     const uint32_t dw[4] = {r.d.x, r.d.y, r.d.z, r.d.w};
+    const f4_t zero = {0.f, 0.f, 0.f, 0.f};
+    f4_t grp = zero;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int sj = LaneGroups<Q>::sidx(j);
         const uint32_t z = HAS_ZP ? (r.zw >> (4 * sj)) & 15u : 8u;
         h2_t q[4];
         unpack8(dw[j], zp_const(z), q);
-        const u4_t av = *reinterpret_cast<const u4_t*>(as + c * kChunkK + 32 * j + 8 * h);
-        float part = __builtin_amdgcn_fdot2(q[0], as_h2(av.x), 0.0f, false);
-        part = __builtin_amdgcn_fdot2(q[1], as_h2(av.y), part, false);
-        part = __builtin_amdgcn_fdot2(q[2], as_h2(av.z), part, false);
-        part = __builtin_amdgcn_fdot2(q[3], as_h2(av.w), part, false);
-        acc = __builtin_fmaf(part, scale_at<ST, NS>(r.s, sj), acc);
+        const h8_t b = as_h8(q);
+        const h8_t a = *reinterpret_cast<const h8_t*>(as + c * kChunkK + 32 * j + 8 * h);
+        if (Q <= 4) {
+            constexpr int steps = 4 / (Q <= 4 ? Q : 1);   // k-steps per group
+            grp = mfma16(a, b, (j % steps == 0) ? zero : grp);
+            if ((j + 1) % steps == 0) acc = __builtin_fmaf(grp[0], scale_at<ST, NS>(r.s, sj), acc);
+        } else {
+            // group 16: octets 0,1 of the step are group 2j, octets 2,3 group
+            // 2j+1.  A lane's scale vector holds the groups of its own octet
+            // half (h >> 1), so the other half's scale comes from the lane 32
+            // positions away.
+            h8_t zh;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) zh[e] = (_Float16)0.0f;
+            const f4_t ge = mfma16(a, (h < 2) ? b : zh, zero);
+            const f4_t go = mfma16(a, (h < 2) ? zh : b, zero);
+            const float s_own = scale_at<ST, NS>(r.s, sj);
+            const float s_other = __shfl_xor(s_own, 32);
+            const float se = (h < 2) ? s_own : s_other;
+            const float so = (h < 2) ? s_other : s_own;
+            acc = __builtin_fmaf(ge[0], se, acc);
+            acc = __builtin_fmaf(go[0], so, acc);
+        }
     }
     return acc;
 }
@@ -149,60 +189,51 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = uniform(tid >> 6);
     const int nw = blockDim.x >> 6;
     const int h = lane >> 4;
     const int64_t t = blockIdx.x;
     const int C = p.C;
     const int64_t kpad = (int64_t)C * kChunkK;
 
-    // 1. first activation vector of this thread (16 bytes) -> registers
+    // 1. first activation vector of this thread (16 bytes), loaded before the
+    //    code stream so its wait does not cover the code loads
     constexpr int kPerVec = 16 / sizeof(AT);
     const int nvec = (int)(kpad / kPerVec);
     const int nvec_valid = p.K / kPerVec;
     const u4_t* a_vec = static_cast<const u4_t*>(p.a);
     u4_t* s_vec = reinterpret_cast<u4_t*>(smem);
-    u4_t first = {0u, 0u, 0u, 0u};
-    if (tid < nvec_valid) first = a_vec[tid];
+    const u4_t first = a_vec[tid < nvec_valid ? tid : 0];   // zeroed at the store
+    __builtin_amdgcn_sched_barrier(0);   // keep this load ahead of the code stream
 
-    // 2. first batch of code words, scales and zero points
-    Regs cur[NW][kBatch];
-#pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-        const int c = wave + nw * u;
-        if (c < C) {
-#pragma unroll
-            for (int x = 0; x < NW; ++x) load_chunk<ST, Q, HAS_ZP>(p.w[x], t * C + c, lane, cur[x][u]);
-        }
-    }
-
-    // 3. stage the activation in LDS (zero beyond K)
-    if (tid < nvec) s_vec[tid] = first;
-    for (int v = tid + blockDim.x; v < nvec; v += blockDim.x) {
-        u4_t val = {0u, 0u, 0u, 0u};
-        if (v < nvec_valid) val = a_vec[v];
-        s_vec[v] = val;
-    }
-    block_sync_lds();
-
-    // 4. stream the wave's chunks, one batch ahead
     float acc[NW];
 #pragma unroll
     for (int x = 0; x < NW; ++x) acc[x] = 0.0f;
-    for (int cb = wave; cb < C; cb += nw * kBatch) {
-        Regs nxt[NW][kBatch];
-        const int cn = cb + nw * kBatch;
-        if (cn < C) {
+
+    // 2. the wave's chunks c = wave + nw*u, a batch of kBatch at a time.
+    //    Chunk indices are clamped so a batch's loads are unconditional and
+    //    all in flight together; the compute is guarded instead.
+    const int stride = nw * kBatch;
+    auto load_batch = [&](Regs (&r)[NW][kBatch], int cb) {
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u) {
-                const int c = cn + nw * u;
-                if (c < C) {
+        for (int u = 0; u < kBatch; ++u) {
+            int c = cb + nw * u;
+            c = c < C ? c : C - 1;
 #pragma unroll
-                    for (int x = 0; x < NW; ++x)
-                        load_chunk<ST, Q, HAS_ZP>(p.w[x], t * C + c, lane, nxt[x][u]);
-                }
-            }
+            for (int x = 0; x < NW; ++x) load_chunk<ST, Q, HAS_ZP>(p.w[x], t * C + c, lane, r[x][u]);
         }
+    };
+    Regs cur[NW][kBatch];
+    load_batch(cur, wave < C ? wave : 0);
+
+    // 3. stage the activation in LDS (zero beyond K) while the codes stream in
+    if (tid < nvec) s_vec[tid] = tid < nvec_valid ? first : u4_t{0u, 0u, 0u, 0u};
+    for (int v = tid + blockDim.x; v < nvec; v += blockDim.x)
+        s_vec[v] = v < nvec_valid ? a_vec[v] : u4_t{0u, 0u, 0u, 0u};
+    block_sync_lds();
+
+    // 4. compute a batch while the next one is in flight
+    auto compute_batch = [&](Regs (&r)[NW][kBatch], int cb) {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int c = cb + nw * u;
@@ -211,24 +242,40 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
                 for (int x = 0; x < NW; ++x) {
                     if (F16)
                         acc[x] = chunk_dot_f16<ST, Q, HAS_ZP>(
-                            cur[x][u], reinterpret_cast<const _Float16*>(smem), c, h, acc[x]);
+                            r[x][u], reinterpret_cast<const _Float16*>(smem), c, h, acc[x]);
                     else
                         acc[x] = chunk_dot_f32<ST, Q, HAS_ZP>(
-                            cur[x][u], reinterpret_cast<const float*>(smem), c, h, acc[x]);
+                            r[x][u], reinterpret_cast<const float*>(smem), c, h, acc[x]);
                 }
             }
         }
+    };
+    if (wave + stride >= C) {
+        // one batch per wave (the common decode shapes): straight-line code
+        if (wave < C) compute_batch(cur, wave);
+    } else {
+        for (int cb = wave; cb < C; cb += stride) {
+            Regs nxt[NW][kBatch];
+            const bool more = cb + stride < C;   // wave-uniform
+            if (more) load_batch(nxt, cb + stride);
+            compute_batch(cur, cb);
+            if (more) {
 #pragma unroll
-        for (int x = 0; x < NW; ++x)
+                for (int x = 0; x < NW; ++x)
 #pragma unroll
-            for (int u = 0; u < kBatch; ++u) cur[x][u] = nxt[x][u];
+                    for (int u = 0; u < kBatch; ++u) cur[x][u] = nxt[x][u];
+            }
+        }
     }
 
-    // 5. lanes L, L^16, L^32, L^48 hold the same column: reduce, then waves
+    // 5. the fp32 path's lanes L, L^16, L^32, L^48 hold parts of the same
+    //    column (the MFMA path already has the column sum): reduce, then waves
+    if (!F16) {
 #pragma unroll
-    for (int x = 0; x < NW; ++x) {
-        acc[x] += __shfl_xor(acc[x], 16);
-        acc[x] += __shfl_xor(acc[x], 32);
+        for (int x = 0; x < NW; ++x) {
+            acc[x] += __shfl_xor(acc[x], 16);
+            acc[x] += __shfl_xor(acc[x], 32);
+        }
     }
     float* red = reinterpret_cast<float*>(smem + kpad * sizeof(AT));
     if (h == 0) {

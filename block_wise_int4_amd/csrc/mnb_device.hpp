@@ -33,9 +33,9 @@ struct ZpConst {
 
 __device__ __forceinline__ ZpConst zp_const(uint32_t z)
 {
-    const uint32_t a = 0xE400u | z;            // -(1024 + z)
-    const uint32_t b = 0xD400u + (z << 4);     // -(64 + z)
-    return ZpConst{a | (a << 16), b | (b << 16)};
+    // z <= 15, so each half is formed without carries: one 24-bit mad each
+    return ZpConst{z * 0x00010001u + 0xE400E400u,    // -(1024 + z) in both halves
+                   z * 0x00100010u + 0xD400D400u};   // -(64 + z) in both halves
 }
 
 // Unpack one repacked word (8 nibbles, slots holding k-offsets
@@ -43,12 +43,14 @@ __device__ __forceinline__ ZpConst zp_const(uint32_t z)
 // (k0,k1), (k2,k3), (k4,k5), (k6,k7).
 __device__ __forceinline__ void unpack8(uint32_t d, ZpConst zc, h2_t out[4])
 {
+    // (x & mask) | 0x64006400 in one v_bitop3_b32 (truth table 0xEA)
+    const uint32_t lo = 0x000F000Fu, hi = 0x00F000F0u, magic = 0x64006400u;
     const h2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
     const uint32_t d8 = d >> 8;
-    out[0] = as_h2((d & 0x000F000Fu) | 0x64006400u) + as_h2(zc.neg1024z);
-    out[1] = as_h2((d & 0x00F000F0u) | 0x64006400u) * sixteenth + as_h2(zc.neg64z);
-    out[2] = as_h2((d8 & 0x000F000Fu) | 0x64006400u) + as_h2(zc.neg1024z);
-    out[3] = as_h2((d8 & 0x00F000F0u) | 0x64006400u) * sixteenth + as_h2(zc.neg64z);
+    out[0] = as_h2(__builtin_amdgcn_bitop3_b32(d, lo, magic, 0xEA)) + as_h2(zc.neg1024z);
+    out[1] = as_h2(__builtin_amdgcn_bitop3_b32(d, hi, magic, 0xEA)) * sixteenth + as_h2(zc.neg64z);
+    out[2] = as_h2(__builtin_amdgcn_bitop3_b32(d8, lo, magic, 0xEA)) + as_h2(zc.neg1024z);
+    out[3] = as_h2(__builtin_amdgcn_bitop3_b32(d8, hi, magic, 0xEA)) * sixteenth + as_h2(zc.neg64z);
 }
 
 // The code of k-offset i (0..7) of a repacked word.
@@ -63,6 +65,9 @@ __device__ __forceinline__ float to_f32(__half x) { return __half2float(x); }
 template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ __half from_f32<__half>(float x) { return __float2half_rn(x); }
+
+// A wave-uniform value the compiler can keep in scalar registers.
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // Workgroup barrier that orders LDS traffic only: outstanding global loads
 // stay in flight across it.
