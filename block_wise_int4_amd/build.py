@@ -32,9 +32,15 @@ DEVICE_FLAGS = [
 ]
 
 
+# per-source extras: the prefill GEMM keeps its MFMA accumulators in VGPRs, so
+# the per-group scaling reads them without v_accvgpr_read copies
+EXTRA_FLAGS = {"gemm_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + COMMON_FLAGS + DEVICE_FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = ([HIPCC] + COMMON_FLAGS + DEVICE_FLAGS + EXTRA_FLAGS.get(src, []) +
+           ["-c", os.path.join(CSRC, src), "-o", obj])
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
