@@ -38,7 +38,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
-    p.add_argument("--only", default="", help="comma list of: gemv,gate_up,small_m,prefill")
+    p.add_argument("--only", default="",
+                   help="comma list of: gemv,gate_up,small_m,prefill (default all); "
+                        "copy adds a plain 256 MiB device copy, the reference kernel "
+                        "for scaling the HBM byte counters")
     return p.parse_args()
 
 
@@ -47,6 +50,37 @@ def onnx_bytes(M, K, N, g, scale_bytes, zp, act_bytes, n_weights=1, out_n=None):
     w = N * K // 2 + N * kb * scale_bytes + (N * ((kb + 1) // 2) if zp else 0)
     out_n = N if out_n is None else out_n
     return n_weights * w + M * K * act_bytes + M * out_n * act_bytes
+
+
+class CopyWorkload:
+    """A plain streaming kernel of known size: torch's elementwise negation
+    of a 256 MiB fp16 tensor into another, which reads 256 MiB and writes
+    256 MiB.  The FETCH_SIZE / WRITE_SIZE counters of the other kernels are
+    scaled by what the same counters read for it (its kernel name is unique
+    in the run, unlike the runtime's blit copies)."""
+
+    def __init__(self, nbytes=256 << 20):
+        import torch
+        self.name, self.variant = "plain copy %d MiB" % (nbytes >> 20), "torch neg (copy)"
+        self.src = torch.ones(nbytes // 2, dtype=torch.float16, device="cuda:0")
+        self.dst = torch.empty_like(self.src)
+        self.bytes, self.flops, self.R = 2 * nbytes, 0, 1
+        self.times_ms, self.events = [], []
+
+    def capture(self):
+        pass
+
+    def run(self, timed):
+        import torch
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.neg(self.src, out=self.dst)
+        e1.record()
+        if timed:
+            self.events.append((e0, e1))
+
+    finish = None  # set below (shares Workload.finish)
 
 
 class Workload:
@@ -127,6 +161,7 @@ class Workload:
         self.avg_launch_ms = total / (len(self.events) * self.R)
         s = self.avg_launch_ms * 1e-3
         return {"workload": self.name, "variant": self.variant, "avg_launch_us": round(s * 1e6, 3),
+                "kernel_source": kernel_source_sha(self.variant),
                 "rotating_copies": self.R, "algorithmic_bytes": self.bytes, "flops": self.flops,
                 "GBps": round(self.bytes / s / 1e9, 1),
                 "hbm_frac": round(self.bytes / s / 1e9 / HBM_PEAK_GBS, 4),
@@ -134,10 +169,50 @@ class Workload:
                 "mfma_frac": round(self.flops / s / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
 
 
+CopyWorkload.finish = Workload.finish
+
+# Source files each variant's kernel is compiled from (its own file plus the
+# shared headers): a counter summary applies only while these are unchanged.
+CSRC = os.path.join(ROOT, "block_wise_int4_amd", "csrc")
+SHARED_HEADERS = ["mnb_device.hpp", "mnb_layout.hpp", "mnb_internal.hpp"]
+VARIANT_SOURCE = {"gemv": "gemv.hip", "gemm_small": "gemm_small.hip", "gemm_mfma": "gemm_mfma.hip"}
+
+
+def kernel_source_sha(variant):
+    import hashlib
+    src = next((f for p, f in VARIANT_SOURCE.items() if variant.startswith(p)), None)
+    if src is None:
+        return None
+    h = hashlib.sha256()
+    for f in [src] + SHARED_HEADERS:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def counted_traffic(workload, variant):
+    """HBM bytes per launch of `workload`, from the committed counter summary
+    profiles/hbm_traffic.txt (FETCH_SIZE + WRITE_SIZE, each scaled by what the
+    counter reads for the plain copy).  None when no summary covers this
+    workload or its kernel source has changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    sha = kernel_source_sha(variant)
+    with open(path) as fh:
+        for line in fh:
+            if not line.startswith("traffic|"):
+                continue
+            _, name, src_sha, nbytes = [x.strip() for x in line.split("|")[:4]]
+            if name == workload and src_sha == sha:
+                return int(nbytes)
+    return None
+
+
 def build_workloads(only):
     from block_wise_int4_amd import synth as S
     sel = set(x for x in only.split(",") if x) or {"gemv", "gate_up", "small_m", "prefill"}
-    wl = []
+    wl = [CopyWorkload()] if "copy" in sel else []
     if "gemv" in sel:
         c = S.DECODE_GEMV
         wl.append(Workload(c.name, 1, [S.workload_weights(c)], c.K, c.N, c.group, seed=c.seed + (1,)))
@@ -229,11 +304,13 @@ def main():
         if bound == "hbm":
             a = r["algorithmic_bytes"] / s / 1e9
             return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(a / HBM_PEAK_GBS, 4), "traffic": None, "kernel": r["variant"],
-                    "avg_launch_us": r["avg_launch_us"]}
+                    "frac": round(a / HBM_PEAK_GBS, 4),
+                    "traffic": counted_traffic(r["workload"], r["variant"]),
+                    "kernel": r["variant"], "avg_launch_us": r["avg_launch_us"]}
         a = r["flops"] / s / 1e12
         return {"bound": "mfma", "achieved": round(a, 1), "peak": MFMA_F16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(a / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(a / MFMA_F16_PEAK_TFLOPS, 4),
+                "traffic": counted_traffic(r["workload"], r["variant"]),
                 "kernel": r["variant"], "avg_launch_us": r["avg_launch_us"]}
 
     out = {
