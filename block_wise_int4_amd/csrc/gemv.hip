@@ -21,10 +21,14 @@ namespace mnb {
 
 namespace {
 
-constexpr int kBatch = 4;          // chunks per wave in flight
-constexpr int kMaxWaves = 8;
-// activation staging stays under the 64 KiB a workgroup gets without opt-in
-constexpr int64_t kMaxStageBytes = 63 * 1024;
+// Waves per workgroup and chunks per wave in flight: 16 x 2 when every
+// workgroup of the grid fits on the chip at once with 16 waves, else 8 x 4
+// (the same bytes in flight per workgroup, half the wave slots).
+constexpr int kMaxWaves = 16;
+constexpr int kResidentWaves = 256 * 32;   // CUs x wave slots per CU
+// activation staging plus the wave reduction stay under the 64 KiB a
+// workgroup gets without opt-in
+constexpr int64_t kMaxStageBytes = 62 * 1024;
 
 struct GemvWeight {
     const u4_t* codes;
@@ -44,19 +48,29 @@ template <int Q> struct LaneGroups {
     __device__ static int sidx(int j) { return Q == 1 ? 0 : (Q == 2 ? (j >> 1) : j); }
 };
 
+// A lane's scales of one chunk, loaded as one integer so the load stays a
+// single instruction where it is written.
 template <typename ST, int NS> struct ScaleVec;
 template <> struct ScaleVec<__half, 1> { typedef uint16_t raw; };
 template <> struct ScaleVec<__half, 2> { typedef uint32_t raw; };
-template <> struct ScaleVec<__half, 4> { typedef uint2 raw; };
-template <> struct ScaleVec<float, 1> { typedef float raw; };
-template <> struct ScaleVec<float, 2> { typedef float2 raw; };
-template <> struct ScaleVec<float, 4> { typedef float4 raw; };
+template <> struct ScaleVec<__half, 4> { typedef uint64_t raw; };
+template <> struct ScaleVec<float, 1> { typedef uint32_t raw; };
+template <> struct ScaleVec<float, 2> { typedef uint64_t raw; };
+template <> struct ScaleVec<float, 4> { typedef u4_t raw; };
 
 template <typename ST, int NS>
 __device__ __forceinline__ float scale_at(const typename ScaleVec<ST, NS>::raw& r, int s)
 {
-    const ST* e = reinterpret_cast<const ST*>(&r);
-    return to_f32(e[s]);
+    if constexpr (sizeof(ST) == 2) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(r >> (16 * s)));
+    } else if constexpr (NS == 4) {
+        // element first, then the cast: this compiler's __builtin_bit_cast of
+        // a vector subscript reads element 0 whatever the index
+        const uint32_t e = r[s];
+        return __builtin_bit_cast(float, e);
+    } else {
+        return __builtin_bit_cast(float, (uint32_t)(r >> (32 * s)));
+    }
 }
 
 template <typename ST, int Q, bool HAS_ZP> struct ChunkRegs {
@@ -66,14 +80,15 @@ template <typename ST, int Q, bool HAS_ZP> struct ChunkRegs {
     uint32_t zw;
 };
 
+// The scales and zero points of one chunk (small loads, issued ahead of the
+// code stream so that their wait does not cover the code loads).
 template <typename ST, int Q, bool HAS_ZP>
-__device__ __forceinline__ void load_chunk(const GemvWeight& w, int64_t chunk, int lane,
-                                           ChunkRegs<ST, Q, HAS_ZP>& r)
+__device__ __forceinline__ void load_meta(const GemvWeight& w, int64_t chunk, int lane,
+                                          ChunkRegs<ST, Q, HAS_ZP>& r)
 {
     constexpr int NS = LaneGroups<Q>::NS;
     const int i = lane & 15, h = lane >> 4;
     const int sbase = Q <= 4 ? i * Q : ((h >> 1) * 16 + i) * 4;
-    r.d = __builtin_nontemporal_load(w.codes + chunk * 64 + lane);
     const ST* sp = static_cast<const ST*>(w.scales) + chunk * kTileN * Q + sbase;
     r.s = *reinterpret_cast<const typename ScaleVec<ST, NS>::raw*>(sp);
     if (HAS_ZP) {
@@ -90,12 +105,21 @@ __device__ __forceinline__ void load_chunk(const GemvWeight& w, int64_t chunk, i
     }
 }
 
+// The chunk's code words: one 16-byte load per lane, a contiguous 1 KiB per wave.
+template <typename ST, int Q, bool HAS_ZP>
+__device__ __forceinline__ void load_codes(const GemvWeight& w, int64_t chunk, int lane,
+                                           ChunkRegs<ST, Q, HAS_ZP>& r)
+{
+    r.d = __builtin_nontemporal_load(w.codes + chunk * 64 + lane);
+}
+
 // fp16 activations: the four 32-k steps of one chunk on the matrix cores.
 // Every row of the v_mfma_f32_16x16x32_f16 A operand holds the same 8
 // activations (each lane reads the slice of its k-octet), so all 16 output
 // rows equal the column's partial sum over the step: the instruction does
-// the k-reduction across lanes.  Each group's partial starts from zero and
-// is scaled into the fp32 total once the group is complete.
+// the k-reduction across lanes, and every lane ends with its column's sum.
+// Each group's partial starts from zero and is scaled into the fp32 total
+// once the group is complete.
 __device__ __forceinline__ f4_t mfma16(const h8_t& a, const h8_t& b, const f4_t& c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -152,7 +176,8 @@ __device__ __forceinline__ float chunk_dot_f16(const ChunkRegs<ST, Q, HAS_ZP>& r
     return acc;
 }
 
-// fp32 activations: the same word, products in fp32.
+// fp32 activations: the same word, products in fp32.  Lanes L, L^16, L^32,
+// L^48 hold parts of the same column; they are summed after the chunks.
 template <typename ST, int Q, bool HAS_ZP>
 __device__ __forceinline__ float chunk_dot_f32(const ChunkRegs<ST, Q, HAS_ZP>& r, const float* as,
                                                int c, int h, float acc)
@@ -179,7 +204,7 @@ __device__ __forceinline__ float chunk_dot_f32(const ChunkRegs<ST, Q, HAS_ZP>& r
 
 __device__ __forceinline__ float silu_f32(float x) { return x / (1.0f + __expf(-x)); }
 
-template <typename AT, typename ST, int Q, bool HAS_ZP, bool FUSED>
+template <typename AT, typename ST, int Q, bool HAS_ZP, bool FUSED, int kBatch>
 __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
 {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -196,15 +221,20 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
     const int C = p.C;
     const int64_t kpad = (int64_t)C * kChunkK;
 
-    // 1. first activation vector of this thread (16 bytes), loaded before the
-    //    code stream so its wait does not cover the code loads
+    // Issue order of a wave: its first activation vector, then the scales
+    // and zero points of its batch, then the batch's code words.  Waits
+    // count completions in issue order, so the small loads never wait behind
+    // the code stream, and chunk u is computed as soon as its own code word
+    // is in while the later ones are still streaming.
+
+    // 1. first activation vector of this thread (16 bytes)
     constexpr int kPerVec = 16 / sizeof(AT);
     const int nvec = (int)(kpad / kPerVec);
     const int nvec_valid = p.K / kPerVec;
     const u4_t* a_vec = static_cast<const u4_t*>(p.a);
     u4_t* s_vec = reinterpret_cast<u4_t*>(smem);
     const u4_t first = a_vec[tid < nvec_valid ? tid : 0];   // zeroed at the store
-    __builtin_amdgcn_sched_barrier(0);   // keep this load ahead of the code stream
+    __builtin_amdgcn_sched_barrier(0);
 
     float acc[NW];
 #pragma unroll
@@ -220,8 +250,17 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
             int c = cb + nw * u;
             c = c < C ? c : C - 1;
 #pragma unroll
-            for (int x = 0; x < NW; ++x) load_chunk<ST, Q, HAS_ZP>(p.w[x], t * C + c, lane, r[x][u]);
+            for (int x = 0; x < NW; ++x) load_meta<ST, Q, HAS_ZP>(p.w[x], t * C + c, lane, r[x][u]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            int c = cb + nw * u;
+            c = c < C ? c : C - 1;
+#pragma unroll
+            for (int x = 0; x < NW; ++x) load_codes<ST, Q, HAS_ZP>(p.w[x], t * C + c, lane, r[x][u]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
     };
     Regs cur[NW][kBatch];
     load_batch(cur, wave < C ? wave : 0);
@@ -268,8 +307,10 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
         }
     }
 
-    // 5. the fp32 path's lanes L, L^16, L^32, L^48 hold parts of the same
-    //    column (the MFMA path already has the column sum): reduce, then waves
+    // 5. every lane now holds its column's partial (the fp32 path after its
+    //    lane sum), and every lane stores it: the four lanes of a column write
+    //    the same value, so no part of the computation is confined to some
+    //    lanes (where the compiler would sink the scale loads behind it).
     if (!F16) {
 #pragma unroll
         for (int x = 0; x < NW; ++x) {
@@ -278,10 +319,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
         }
     }
     float* red = reinterpret_cast<float*>(smem + kpad * sizeof(AT));
-    if (h == 0) {
 #pragma unroll
-        for (int x = 0; x < NW; ++x) red[(x * kMaxWaves + wave) * 16 + lane] = acc[x];
-    }
+    for (int x = 0; x < NW; ++x) red[(x * kMaxWaves + wave) * 16 + (lane & 15)] = acc[x];
     __syncthreads();
     if (wave == 0 && lane < 16) {
         float r[NW];
@@ -302,7 +341,10 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
 template <typename AT, typename ST, int Q, bool HAS_ZP, bool FUSED>
 hipError_t launch_t(const GemvParams& p, int waves, size_t smem, int64_t tiles, hipStream_t s)
 {
-    gemv_kernel<AT, ST, Q, HAS_ZP, FUSED><<<dim3((unsigned)tiles), dim3(waves * 64), smem, s>>>(p);
+    if (waves > kMaxWaves / 2)
+        gemv_kernel<AT, ST, Q, HAS_ZP, FUSED, 2><<<dim3((unsigned)tiles), dim3(waves * 64), smem, s>>>(p);
+    else
+        gemv_kernel<AT, ST, Q, HAS_ZP, FUSED, 4><<<dim3((unsigned)tiles), dim3(waves * 64), smem, s>>>(p);
     return hipGetLastError();
 }
 
@@ -352,7 +394,8 @@ hipError_t launch_gemv(const Layout& L, const WeightView& gate, const WeightView
     p.N = (int)L.N;
     p.K = (int)L.K;
     p.C = (int)L.C;
-    int waves = (int)(L.C < kMaxWaves ? L.C : kMaxWaves);
+    const int max_waves = L.T * kMaxWaves <= kResidentWaves ? kMaxWaves : kMaxWaves / 2;
+    int waves = (int)(L.C < max_waves ? L.C : max_waves);
     if (waves < 1) waves = 1;
     const size_t smem = (size_t)L.C * kChunkK * (f16_act ? 2 : 4) + 2 * kMaxWaves * 16 * sizeof(float);
     const bool fused = up != nullptr;
