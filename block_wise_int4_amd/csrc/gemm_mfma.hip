@@ -2,32 +2,36 @@
 //
 // Method: onnx-runtime-ep-cuda 0.1.0-dev.6, src/kernels/marlin_gemm.rs
 // (matmul_nbits_marlin_gemm_f16 and its module doc): weights enter the matrix
-// multiply centred but unscaled, as exact fp16 (code - zp); each group's
-// products accumulate in fp32 from zero and the group's scale multiplies that
-// partial after the group's accumulate, so the accumulator never carries a
-// scale that varies along K.
+// multiply centred but unscaled, as exact fp16 (code - zp); products
+// accumulate in fp32 and each group's scale is applied in fp32 after that
+// group's accumulate, never folded into the fp16 weights.
 //
 // gfx950 design.
-// * v_mfma_f32_32x32x16_f16 (32x32 output, 16 k): it reaches the matrix
-//   cores' full rate from one wave per SIMD, which the 16x16x32 shape does not.
-// * Workgroup tile 128 (M) x 256 (N), 4 waves, one per SIMD; each wave owns
-//   all 128 rows and 64 columns: 4 row blocks x 2 column pairs of 32x32
-//   tiles.
-// * Every operand of a 128-k chunk -- the A rows, the wave's four 1 KiB code
-//   word blocks, and the scales and zero points of its tiles -- is copied
-//   into LDS by buffer_load ... lds (no VGPR round trip) into a ring of
-//   stages, ahead of the compute.  Rows and k outside the operand read as
-//   zero through the buffer range check.  A's 16-byte segments are
-//   XOR-swizzled by row, so fragment reads are bank-conflict free.
-// * The repacked layout distributes a 16-column tile over the 64 lanes as 16
-//   columns x 4 k-octets; two v_permlane*_swap instructions on the raw words
-//   of two adjacent tiles give the 32 columns x 2 k-octets of the 32x32x16 B
-//   operand before the unpack.
-// * Each group accumulates from zero into one set of 32x32 accumulators; at
-//   the group's end they are multiplied by the group's scales into the fp32
-//   running total.
+// * v_mfma_f32_32x32x16_f16 (32x32 output, 16 k).
+// * Workgroup tile 96 (M) x 256 (N), 4 waves; wave w owns columns
+//   [64w, +64) of all 96 rows: 3 row blocks x 2 column pairs of 32x32 tiles.
+//   Two workgroups share a CU (two waves per SIMD).
+// * A rows reach LDS by buffer_load ... lds (no VGPR round trip) into a ring
+//   of three stages; the DMAs of a chunk are spread over the matrix work of
+//   the chunk two ahead.  A's 16-byte segments are XOR-swizzled by row, so
+//   fragment reads are conflict free.  Rows and k outside the operand read as
+//   zero through the range check.
+// * Code words are loaded straight into the lanes that use them, a chunk
+//   ahead: the repacked 16-column tile (16 columns x 4 k-octets per 32 k)
+//   holds, in one 16-byte lane record, the four 32-k steps of one column and
+//   k-octet, which is exactly what a lane of the 32x32x16 B operand needs.
+// * Per-group scaling with a single accumulator per output: while group g
+//   accumulates, acc holds total / s_g; entering group g+1 it is multiplied
+//   by s_g / s_{g+1}, and after the last group the output is acc * s_last.
+//   The algebra is exact; each rescale adds one fp32 rounding.  A group with
+//   scale 0 gets all-zero B operands (it adds exactly nothing, NaN for
+//   infinite activations as (c - z) * 0 * a does) and keeps the units; the
+//   padding past K is such a group.  Half the registers of a separate group
+//   accumulator are freed for deeper prefetch and for two waves per SIMD.
 // * Workgroup ids are remapped so the tiles resident on one XCD at a time
-//   share A rows and B columns in that XCD's L2.
+//   share A rows and code columns in that XCD's L2.
+#include <type_traits>
+
 #include "mnb_device.hpp"
 #include "mnb_internal.hpp"
 
@@ -64,15 +68,19 @@ struct GemmParams {
 template <int Q, int SS, bool HAS_ZP> struct StageGeom {
     static constexpr int kScaleDw = kTileN * Q * SS / 4;               // dwords per tile record
     static constexpr int kZpDw = HAS_ZP ? kTileN * Q / 8 : 0;          // 8Q bytes per tile record
-    static constexpr int kMetaDw = TPW * (kScaleDw + kZpDw);           // per wave
-    static constexpr int kMetaInstr = (kMetaDw + 63) / 64;             // dword DMAs per wave
+    // per wave: the scale records of its tiles, then (from a 64-dword
+    // boundary) their zero-point records; one dword DMA per 64 dwords
+    static constexpr int kScaleInstr = (TPW * kScaleDw + 63) / 64;
+    static constexpr int kZpInstr = (TPW * kZpDw + 63) / 64;
+    static constexpr int kMetaInstr = kScaleInstr + kZpInstr;
+    static constexpr int kZpOffDw = kScaleInstr * 64;                  // zero points in the record
     static constexpr int kMetaDwPad = kMetaInstr * 64;
     static constexpr int kA = BM * SEGS * 16;                          // bytes
-    static constexpr int kB = WAVES * TPW * 1024;
+    static constexpr int kB = 0;                                       // codes go to VGPRs
     static constexpr int kMeta = WAVES * kMetaDwPad * 4;
     static constexpr int kBytes = kA + kB + kMeta;
     static constexpr int kStages = 3 * kBytes <= kLdsBudget ? 3 : 2;
-    static constexpr int kDmaPerChunk = A_DMA + TPW + kMetaInstr;      // per wave
+    static constexpr int kDmaPerChunk = A_DMA + kMetaInstr;            // per wave
 };
 
 __device__ __forceinline__ f16v_t mfma32(const h8_t& a, const h8_t& b, const f16v_t& c)
@@ -88,6 +96,28 @@ __device__ __forceinline__ h8_t as_h8(const h2_t q[4])
     b[4] = q[2][0]; b[5] = q[2][1];
     b[6] = q[3][0]; b[7] = q[3][1];
     return b;
+}
+
+// unpack8 for the rescaled accumulator: (c - z) as exact fp16 pairs, or all
+// zeros for a group whose scale is zero (bit 4 of zf), so such a group adds
+// exactly nothing (NaN for infinite activations, as (c - z) * 0 * a does).
+// Both nibble halves use one packed fma, (x | magic) * m + a, with m = 1 or
+// 1/16 and a = -(1024 + z) or -(64 + z) for a live group and m = a = 0 for a
+// dead one: the same instruction count as unpack8.
+__device__ __forceinline__ void unpack8_scaled(uint32_t d, uint32_t zf, h2_t out[4])
+{
+    const uint32_t lo = 0x000F000Fu, hi = 0x00F000F0u, magic = 0x64006400u;
+    const bool dead = zf >= 16u;
+    const ZpConst zc = zp_const(zf & 15u);
+    const h2_t m_lo = as_h2(dead ? 0u : 0x3C003C00u);   // 1.0
+    const h2_t m_hi = as_h2(dead ? 0u : 0x2C002C00u);   // 1/16
+    const h2_t a_lo = as_h2(dead ? 0u : zc.neg1024z);
+    const h2_t a_hi = as_h2(dead ? 0u : zc.neg64z);
+    const uint32_t d8 = d >> 8;
+    out[0] = as_h2(__builtin_amdgcn_bitop3_b32(d, lo, magic, 0xEA)) * m_lo + a_lo;
+    out[1] = as_h2(__builtin_amdgcn_bitop3_b32(d, hi, magic, 0xEA)) * m_hi + a_hi;
+    out[2] = as_h2(__builtin_amdgcn_bitop3_b32(d8, lo, magic, 0xEA)) * m_lo + a_lo;
+    out[3] = as_h2(__builtin_amdgcn_bitop3_b32(d8, hi, magic, 0xEA)) * m_hi + a_hi;
 }
 
 // LDS destination pointers of buffer_load ... lds.  (Cast inline: a
@@ -157,183 +187,281 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_mfma_kernel(GemmParams p)
     };
 
     // ---- DMA sources ------------------------------------------------------
-    // A: rows m0 .. m0+BM as a buffer that ends at the last valid row, so
-    // rows >= M read zero; k >= K uses an offset past the range.
+    // Every buffer starts at this workgroup's first row or first tile, so
+    // offsets stay far inside 32 bits whatever the size of the operands, and
+    // rows, tiles and k outside the operand read as zero through the range
+    // check.  A: rows m0 .. m0+BM, ending at the last valid row; k >= K uses
+    // an offset past the range.
     const int rows_here = (p.M - m0) < BM ? (p.M - m0) : BM;
     const uint32_t a_bytes = (uint32_t)rows_here * (uint32_t)K * 2u;
     const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(p.a + (int64_t)m0 * K), (short)0, (int)a_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t w_rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void*)p.w, (short)0, (int)p.w_bytes, 0x00020000);
+    const int t0 = nb * (BN / 16);                         // first tile of the workgroup
+    const int tiles_here = (p.T - t0) < BN / 16 ? (p.T - t0) : BN / 16;
+    const uint32_t code_bytes = (uint32_t)tiles_here * (uint32_t)C * 1024u;
+    const uint32_t scale_bytes = (uint32_t)tiles_here * (uint32_t)C * (uint32_t)(G::kScaleDw * 4);
+    const uint32_t zp_bytes = (uint32_t)tiles_here * (uint32_t)C * (uint32_t)(G::kZpDw * 4);
+    const __amdgpu_buffer_rsrc_t c_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.w + (int64_t)t0 * C * 1024), (short)0, (int)code_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.w + p.scales_off + (int64_t)t0 * C * (G::kScaleDw * 4)), (short)0, (int)scale_bytes,
+        0x00020000);
+    const __amdgpu_buffer_rsrc_t z_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.w + (HAS_ZP ? p.zp_off : 0) + (int64_t)t0 * C * (G::kZpDw * 4)), (short)0,
+        (int)zp_bytes, 0x00020000);
 
-    // this wave's 4 tiles (clamped for loads; stores are masked by N)
-    uint32_t tile_chunk0[TPW];   // chunk index of (tile, chunk 0)
-#pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) {
-        int t = nb * (BN / 16) + wave * TPW + tt;
-        if (t >= p.T) t = p.T - 1;
-        tile_chunk0[tt] = (uint32_t)t * (uint32_t)C;
-    }
-
-    auto issue_chunk = [&](int c, int st) {
-        // A rows [ROWS_PER_WAVE*wave, +ROWS_PER_WAVE): DMAs of 4 rows each
-#pragma unroll
-        for (int b = 0; b < A_DMA; ++b) {
-            const int r = ROWS_PER_WAVE * wave + 4 * b + (lane >> 4);
+    // The LDS DMAs of one chunk, one "piece" (one instruction) at a time, so
+    // they can be spread over the compute of an earlier chunk: pieces
+    // 0 .. A_DMA-1 copy A rows, then the scale records and the zero-point
+    // records of the wave's tiles.
+    auto issue_piece = [&](int c, int st, int idx) {
+        if (idx < A_DMA) {
+            // A rows [ROWS_PER_WAVE*wave + 4*idx, +4)
+            const int r = ROWS_PER_WAVE * wave + 4 * idx + (lane >> 4);
             const int sg = (lane & 15) ^ (r & 15);          // logical segment at this slot
             const int k = c * kChunkK + 8 * sg;
             const uint32_t off = k < K ? ((uint32_t)r * (uint32_t)K + (uint32_t)k) * 2u : a_bytes;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)(stage_a(st) + (ROWS_PER_WAVE * wave + 4 * b) * SEGS),
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)(stage_a(st) + (ROWS_PER_WAVE * wave + 4 * idx) * SEGS),
                                                      16, off, 0, 0, 0);
-        }
-        // code words: one 1 KiB block per tile
-#pragma unroll
-        for (int tt = 0; tt < TPW; ++tt) {
-            const uint32_t off = (tile_chunk0[tt] + (uint32_t)c) * 1024u + (uint32_t)lane * 16u;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_ptr_t)(stage_b(st) + (wave * TPW + tt) * 256),
-                                                     16, off, 0, 0, 0);
-        }
-        // scale records, then zero-point records, of the 4 tiles (dwords)
-#pragma unroll
-        for (int m = 0; m < G::kMetaInstr; ++m) {
-            int d = m * 64 + lane;
-            uint32_t off;
-            if (d < TPW * G::kScaleDw) {
-                const int tt = d / G::kScaleDw, o = d % G::kScaleDw;
-                off = (uint32_t)p.scales_off + (tile_chunk0[tt] + (uint32_t)c) * (uint32_t)(G::kScaleDw * 4) + o * 4;
-            } else if (HAS_ZP && d < G::kMetaDw) {
-                constexpr int ZD = G::kZpDw > 0 ? G::kZpDw : 1;
-                d -= TPW * G::kScaleDw;
-                const int tt = d / ZD, o = d % ZD;
-                off = (uint32_t)p.zp_off + (tile_chunk0[tt] + (uint32_t)c) * (uint32_t)(ZD * 4) + o * 4;
-            } else {
-                off = p.w_bytes;   // padding lanes read zero
-            }
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_ptr_t)(stage_m(st) + m * 256), 4, off, 0, 0, 0);
+        } else if (idx < A_DMA + G::kScaleInstr) {
+            // lanes past the records read zero through the range check
+            const int m = idx - A_DMA;
+            const int d = m * 64 + lane;
+            const int tt = d / G::kScaleDw, o = d % G::kScaleDw;
+            const uint32_t off = d < TPW * G::kScaleDw
+                ? ((uint32_t)(wave * TPW + tt) * (uint32_t)C + (uint32_t)c) * (uint32_t)(G::kScaleDw * 4) + o * 4
+                : scale_bytes;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_ptr_t)(stage_m(st) + m * 256), 4, off, 0, 0, 0);
+        } else {
+            constexpr int ZD = G::kZpDw > 0 ? G::kZpDw : 1;
+            const int m = idx - A_DMA - G::kScaleInstr;
+            const int d = m * 64 + lane;
+            const int tt = d / ZD, o = d % ZD;
+            const uint32_t off = d < TPW * G::kZpDw
+                ? ((uint32_t)(wave * TPW + tt) * (uint32_t)C + (uint32_t)c) * (uint32_t)(ZD * 4) + o * 4
+                : zp_bytes;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(z_rsrc, (lds_ptr_t)(stage_m(st) + (G::kScaleInstr + m) * 256), 4, off,
+                                                     0, 0, 0);
         }
     };
 
-    // ---- accumulators -----------------------------------------------------
-    f16v_t total[RB][PAIRS];
-    f16v_t grp[RB][PAIRS];
-    f16v_t zero;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) zero[e] = 0.f;
+    // One fp32 accumulator per output, kept in units of the current
+    // group's scale: acc = total / s_g while group g accumulates.  At a group
+    // boundary acc is multiplied by s_g / s_{g+1}; after the last group the
+    // output is acc * s_last.
+    f16v_t acc[RB][PAIRS];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int q = 0; q < PAIRS; ++q) {
-            total[rb][q] = zero;
-            grp[rb][q] = zero;
-        }
+        for (int q = 0; q < PAIRS; ++q)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[rb][q][e] = 0.f;
 
     constexpr int HS_PER_GROUP = 8 / Q;          // 16-k steps per group (group = 128/Q)
+    constexpr int NP = G::kDmaPerChunk;           // DMA pieces per chunk and wave
+    constexpr int NP_STEP = (NP + 5) / 6;         // pieces issued per step (steps 0..5)
+    static_assert(NST == 3, "the pipeline below keeps three stages");
 
-    // one 128-k chunk from stage st
-    auto chunk = [&](int st) {
-        const u4_t* As = stage_a(st);
-        const uint32_t* Bs = stage_b(st) + wave * TPW * 256;
+    // units of acc per column pair: the scale of the last group with a
+    // nonzero scale (groups past K have scale 0 and contribute exactly 0)
+    float unit[PAIRS];
+#pragma unroll
+    for (int q = 0; q < PAIRS; ++q) unit[q] = 0.f;
+
+    // per-chunk state: the rescale factor entering each group and the zero
+    // points of the lane's columns, for the current and the next chunk
+    float ratio[PAIRS][Q], ratio_n[PAIRS][Q];
+    uint32_t zc[PAIRS][Q], zc_n[PAIRS][Q];
+    auto read_meta = [&](int st, float (&rt)[PAIRS][Q], uint32_t (&z)[PAIRS][Q]) {
         const unsigned char* Ms = stage_m(st);
-        // this lane's column lives in tile 2q + half of pair q
-        float sc[PAIRS][Q];
-        uint32_t zc[PAIRS][Q];
 #pragma unroll
         for (int q = 0; q < PAIRS; ++q) {
-            const int tt = 2 * q + half;
+            const int tt = 2 * q + half;   // this lane's column lives in tile 2q + half
             const ST* srec = reinterpret_cast<const ST*>(Ms + tt * G::kScaleDw * 4);
 #pragma unroll
             for (int g = 0; g < Q; ++g) {
-                const int s = slot_of(i, g, Q);
-                sc[q][g] = to_f32(srec[s]);
+                const int sl = slot_of(i, g, Q);
+                const float sg = to_f32(srec[sl]);
+                rt[q][g] = sg != 0.f ? unit[q] * __builtin_amdgcn_rcpf(sg) : 1.f;
+                unit[q] = sg != 0.f ? sg : unit[q];
+                uint32_t zv = 8u;
                 if (HAS_ZP) {
-                    const unsigned char* zrec = Ms + (TPW * G::kScaleDw + tt * G::kZpDw) * 4;
-                    zc[q][g] = (zrec[s >> 1] >> (4 * (s & 1))) & 15u;
-                } else {
-                    zc[q][g] = 8u;
+                    const unsigned char* zrec = Ms + (G::kZpOffDw + tt * G::kZpDw) * 4;
+                    zv = (zrec[sl >> 1] >> (4 * (sl & 1))) & 15u;
                 }
-            }
-        }
-        // A fragments of 16-k step hs: row (rb*32 + lane%32), k-octet oct;
-        // the XOR swizzle term depends on the lane only (rb*32 is a multiple
-        // of 16), so rows of different blocks differ by a constant offset.
-        auto load_afr = [&](h8_t (&afr)[RB], int hs) {
-            const int sgi = (2 * hs + oct) ^ (lane & 15);
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-                afr[rb] = __builtin_bit_cast(h8_t, As[(rb * 32 + (lane & 31)) * SEGS + sgi]);
-        };
-        // raw code words of 32-k step j for the wave's 4 tiles
-        auto load_words = [&](uint32_t (&w)[TPW], int j) {
-#pragma unroll
-            for (int tt = 0; tt < TPW; ++tt) w[tt] = Bs[tt * 256 + lane * 4 + j];
-        };
-        h8_t afr[RB], afr_next[RB];
-        uint32_t wcur[TPW], wnext[TPW];
-        load_afr(afr, 0);
-        load_words(wcur, 0);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {          // 32-k steps
-            if (j < 3) load_words(wnext, j + 1);
-            uint32_t bh[2][PAIRS];
-#pragma unroll
-            for (int q = 0; q < PAIRS; ++q) {
-                const auto s1 = __builtin_amdgcn_permlane16_swap(wcur[2 * q], wcur[2 * q + 1], false, false);
-                const auto s2 = __builtin_amdgcn_permlane32_swap(s1[0], s1[1], false, false);
-                bh[0][q] = s2[0];
-                bh[1][q] = s2[1];
-            }
-#pragma unroll
-            for (int ph = 0; ph < 2; ++ph) {   // 16-k halves
-                const int hs = 2 * j + ph;     // 16-k step within the chunk
-                const int gq = hs / HS_PER_GROUP;               // group within the chunk
-                const int t_in = hs % HS_PER_GROUP;             // step within the group
-                if (hs < 7) load_afr(afr_next, hs + 1);         // one step ahead
-#pragma unroll
-                for (int q = 0; q < PAIRS; ++q) {
-                    h2_t u[4];
-                    unpack8(bh[ph][q], zp_const(zc[q][gq]), u);
-                    const h8_t b = as_h8(u);
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb) grp[rb][q] = mfma32(afr[rb], b, t_in == 0 ? zero : grp[rb][q]);
-                }
-                if (t_in == HS_PER_GROUP - 1) {
-                    // group complete: scale it into the running total
-#pragma unroll
-                    for (int q = 0; q < PAIRS; ++q)
-#pragma unroll
-                        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                            for (int e = 0; e < 16; ++e)
-                                total[rb][q][e] = __builtin_fmaf(grp[rb][q][e], sc[q][gq], total[rb][q][e]);
-                }
-                if (hs < 7) {
-#pragma unroll
-                    for (int rb = 0; rb < RB; ++rb) afr[rb] = afr_next[rb];
-                }
-                // keep each step's reads one step ahead of their use: no
-                // instruction moves across a 16-k step boundary
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            if (j < 3) {
-#pragma unroll
-                for (int tt = 0; tt < TPW; ++tt) wcur[tt] = wnext[tt];
+                // bit 4: the group's scale is zero, so its B operands are zero
+                z[q][g] = zv | (sg == 0.f ? 16u : 0u);
             }
         }
     };
-
-    // ---- pipeline: chunks c+1 .. c+NST-1 are in flight while c computes ----
+    // A fragments of 16-k step hs: row (rb*32 + lane%32), k-octet oct; the
+    // XOR swizzle term depends on the lane only (rb*32 is a multiple of 16).
+    auto load_afr = [&](int st, h8_t (&afr)[RB], int hs) {
+        const u4_t* As = stage_a(st);
+        const int sgi = (2 * hs + oct) ^ (lane & 15);
 #pragma unroll
-    for (int s = 0; s < NST - 1; ++s) {
-        if (s < C) issue_chunk(s, s);
+        for (int rb = 0; rb < RB; ++rb)
+            afr[rb] = __builtin_bit_cast(h8_t, As[(rb * 32 + (lane & 31)) * SEGS + sgi]);
+    };
+    // Code words go straight from memory to the lanes that use them, in
+    // the 32x32x16 B-operand distribution: lane l takes column l%32 (tile
+    // 2q + (l/16)%2 of pair q, column l%16) and, for 16-k step hs, k-octet
+    // 2*(hs%2) + l/32 of 32-k step hs/2.  The repacked chunk holds that
+    // octet in word hs/2 of the tile's lane (k-octet*16 + column), so one
+    // 16-byte load per (pair, hs%2) brings a lane all four 32-k steps.
+    auto load_b = [&](int c, u4_t (&bq)[PAIRS][2]) {
+#pragma unroll
+        for (int q = 0; q < PAIRS; ++q)
+#pragma unroll
+            for (int ph = 0; ph < 2; ++ph) {
+                const int src = (2 * ph + oct) * 16 + i;
+                const uint32_t off = ((uint32_t)(wave * TPW + 2 * q + half) * (uint32_t)C + (uint32_t)c) * 1024u +
+                                     (uint32_t)src * 16u;
+                bq[q][ph] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, off, 0, 0));
+            }
+    };
+    auto load_bw = [&](const u4_t (&bq)[PAIRS][2], uint32_t (&w)[PAIRS], int hs) {
+#pragma unroll
+        for (int q = 0; q < PAIRS; ++q) w[q] = bq[q][hs & 1][hs >> 1];
+    };
+    auto unpack_b = [&](const uint32_t (&w)[PAIRS], const uint32_t (&z)[PAIRS][Q], int hs, h8_t (&bop)[PAIRS]) {
+        const int gq = hs / HS_PER_GROUP;
+#pragma unroll
+        for (int q = 0; q < PAIRS; ++q) {
+            h2_t u[4];
+            unpack8_scaled(w[q], z[q][gq], u);
+            bop[q] = as_h8(u);
+        }
+    };
+
+    // A fragments: a ring indexed by the step number (8 steps per chunk, so
+    // step hs of every chunk uses slot hs % 4), read two steps ahead; the
+    // first two steps of the next chunk are read in step 7, after the
+    // barrier that makes that chunk visible.  Code words: this chunk's and
+    // the next one's, loaded a chunk ahead.  B operands: unpacked one step
+    // ahead.
+    h8_t afr[4][RB];
+    u4_t bq[PAIRS][2], bq_n[PAIRS][2];
+    h8_t bop[2][PAIRS];
+
+    // ---- prologue: chunks 0 and 1 in flight, chunk 0 read in ----
+    if (C > 0) {
+#pragma unroll
+        for (int k = 0; k < NP; ++k) issue_piece(0, 0, k);
     }
+    if (C > 1) {
+#pragma unroll
+        for (int k = 0; k < NP; ++k) issue_piece(1, 1, k);
+    }
+    load_b(0, bq);
+    // chunk 0's DMAs landed for this wave (later issues may stay in flight)
+    if (C > 1) wait_vm<NP + 2 * PAIRS>();
+    else wait_vm<2 * PAIRS>();
+    block_sync_lds();
+    read_meta(0, ratio, zc);
+    load_afr(0, afr[0], 0);
+    load_afr(0, afr[1], 1);
+    {
+        uint32_t w[PAIRS];
+        load_bw(bq, w, 0);
+        unpack_b(w, zc, 0, bop[0]);
+    }
+
     for (int c = 0; c < C; ++c) {
-        // chunk c landed for this wave (later chunks may stay in flight) ...
-        if (c + NST - 2 < C) wait_vm<(NST - 2) * G::kDmaPerChunk>();
-        else wait_vm<0>();
-        block_sync_lds();   // ... and for every wave; stage (c-1) % NST is free
-        if (c + NST - 1 < C) issue_chunk(c + NST - 1, (c + NST - 1) % NST);
-        chunk(c % NST);
+        const int st = c % NST, nst = (c + 1) % NST, dst = (c + 2) % NST;
+        const bool more = c + 1 < C;        // wave-uniform
+        const bool dma = c + 2 < C;
+        // one 16-k step; hs is a compile-time constant (the interleave
+        // pattern needs constant counts)
+        auto step = [&](auto hs_c) {
+            constexpr int hs = decltype(hs_c)::value;
+            constexpr int gq = hs / HS_PER_GROUP;   // group within the chunk
+            constexpr int t_in = hs % HS_PER_GROUP; // step within the group
+            // the next chunk's code words, a chunk ahead
+            if (hs == 0 && more) load_b(c + 1, bq_n);
+            // LDS reads two steps ahead (step 7 reads the next chunk's first two)
+            if (hs + 2 < 8) {
+                load_afr(st, afr[(hs + 2) % 4], hs + 2);
+            } else if (hs == 7 && more) {
+                read_meta(nst, ratio_n, zc_n);
+                load_afr(nst, afr[0], 0);
+                load_afr(nst, afr[1], 1);
+            }
+            // this chunk's share of the DMAs of chunk c+2
+            if (hs < 6 && dma) {
+#pragma unroll
+                for (int k = hs * NP_STEP; k < (hs + 1) * NP_STEP && k < NP; ++k) issue_piece(c + 2, dst, k);
+            }
+            // the matrix work, each group entered with its rescale
+            const bool rescale = t_in == 0 && !(c == 0 && hs == 0);
+#pragma unroll
+            for (int q = 0; q < PAIRS; ++q) {
+                const float r = ratio[q][gq];
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    if (rescale) {
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) acc[rb][q][e] *= r;
+                    }
+                    acc[rb][q] = mfma32(afr[hs % 4][rb], bop[hs & 1][q], acc[rb][q]);
+                }
+            }
+            // the next step's B operands
+            uint32_t w[PAIRS];
+            if (hs + 1 < 8) {
+                load_bw(bq, w, hs + 1);
+                unpack_b(w, zc, hs + 1, bop[(hs + 1) & 1]);
+            } else if (more) {
+                load_bw(bq_n, w, 0);
+                unpack_b(w, zc_n, 0, bop[0]);
+            }
+            // interleave: LDS reads first, then each MFMA followed by a share
+            // of the VALU work and of the memory issue
+            constexpr int kReads = hs + 2 < 8 ? RB : (hs == 7 ? 2 * RB : 0);
+            if (kReads > 0) __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);   // DS reads
+#pragma unroll
+            for (int k = 0; k < RB * PAIRS; ++k) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // 1 MFMA
+                __builtin_amdgcn_sched_group_barrier(0x002, t_in == 0 ? 19 : 3, 0); // VALU
+                if (hs < 6 && k < NP_STEP + (hs == 0 ? 2 * PAIRS : 0))
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);             // VMEM
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        step(std::integral_constant<int, 0>());
+        step(std::integral_constant<int, 1>());
+        step(std::integral_constant<int, 2>());
+        step(std::integral_constant<int, 3>());
+        step(std::integral_constant<int, 4>());
+        step(std::integral_constant<int, 5>());
+        step(std::integral_constant<int, 6>());
+        if (more) {
+            // chunk c+1's DMAs landed for this wave (this chunk's later issues:
+            // chunk c+1's code words and chunk c+2's DMAs, may stay in flight) ...
+            if (dma) wait_vm<2 * PAIRS + NP>();
+            else wait_vm<2 * PAIRS>();
+            block_sync_lds();   // ... and for every wave
+        }
+        step(std::integral_constant<int, 7>());
+#pragma unroll
+        for (int q = 0; q < PAIRS; ++q) {
+#pragma unroll
+            for (int g = 0; g < Q; ++g) {
+                ratio[q][g] = ratio_n[q][g];
+                zc[q][g] = zc_n[q][g];
+            }
+            bq[q][0] = bq_n[q][0];
+            bq[q][1] = bq_n[q][1];
+        }
     }
+
+    // back from units of the last group's scale
+#pragma unroll
+    for (int q = 0; q < PAIRS; ++q)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[rb][q][e] *= unit[q];
 
     // ---- epilogue: lane holds column (lane & 31) of each 32x32 block, rows
     // 8*(e/4) + 4*oct + e%4
@@ -346,7 +474,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_mfma_kernel(GemmParams p)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int m = m0 + rb * 32 + 8 * (e >> 2) + 4 * oct + (e & 3);
-                if (m < p.M) p.y[(int64_t)m * p.N + n] = __float2half_rn(total[rb][q][e]);
+                if (m < p.M) p.y[(int64_t)m * p.N + n] = __float2half_rn(acc[rb][q][e]);
             }
         }
     }

@@ -225,7 +225,10 @@ def within_bound(y, Y: np.ndarray, Bnd: np.ndarray, rel: float = REL_TOL,
     both_nan = np.isnan(y) & np.isnan(Y)
     same_inf = np.isinf(y) & np.isinf(Y) & (np.sign(y) == np.sign(Y))
     with np.errstate(invalid="ignore"):
-        ok = np.abs(y - Y) <= rel * Bnd + abs_
+        # the distance test applies to finite expected values only: an
+        # infinite Y (whose bound is infinite too) is matched only by the
+        # same infinity, a NaN only by a NaN
+        ok = np.isfinite(Y) & (np.abs(y - Y) <= rel * Bnd + abs_)
     return ok | both_nan | same_inf
 
 

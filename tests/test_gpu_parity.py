@@ -334,6 +334,37 @@ def test_nan_and_inf_propagate(mnb):
         G.assert_within(G.host(y), Y, B, "nan/inf M=%d" % M)
 
 
+def test_zero_and_non_finite_scales(mnb):
+    """Groups whose scale is 0 add exactly nothing, and a NaN scale makes
+    its column NaN, on every path: GEMV, small M, MFMA.  The same weights are
+    checked at several group sizes and both scale dtypes (the dequantized
+    weight (c - z) * s is exact in fp64).  Infinite scales are left out: the
+    oracle dequantizes first, (c - z) * inf, which is NaN wherever a code
+    equals its zero point, while scaling a group's sum gives +-inf; the
+    stored format carries finite scales."""
+    t = G.torch()
+    for (N, K, g, sdt) in ((64, 512, 128, "f16"), (48, 384, 32, "f16"), (40, 256, 64, "f32")):
+        w = _weight(N, K, g, sdt, seed=7)
+        kb = K // g
+        rng = np.random.default_rng(N + K)
+        s = w.scales.copy()
+        # a third of all groups, at random, have scale 0; column 3 has every
+        # scale 0; column 9 one NaN scale
+        s[rng.random((N, kb)) < 0.33] = 0
+        s[3, :] = 0
+        s[9, 0] = np.nan
+        w2 = synth.Weight(N, K, g, w.packed, s.astype(w.scales.dtype), w.zero_points)
+        q = G.upload(w2)
+        for M in (1, 4, 40):
+            A = _act(M, K, seed=M)
+            y = t.empty((M, N), dtype=t.float16, device="cuda")
+            mnb.mnb_gemm(q.desc, q.repacked, G.to_dev(A), M, y)
+            Y, B, _ = G.oracle_dense(A, w2)
+            yh = G.host(y)
+            G.assert_within(yh, Y, B, "special scales M=%d N=%d K=%d g=%d %s" % (M, N, K, g, sdt))
+            assert (yh[:, 3] == 0).all()
+
+
 def test_empty_and_unsupported_requests(mnb):
     t = G.torch()
     w = _weight(64, 256, 32)

@@ -257,6 +257,11 @@ def test_within_bound_semantics():
     assert o.within_bound(y, Y, B).tolist() == [True, True, True, False, False]
     assert not o.within_bound([np.nan], [1.0], [1e9])[0]
     assert not o.within_bound([-np.inf], [np.inf], [1.0])[0]
+    # an infinite expected value (whose magnitude bound is infinite too) is
+    # matched only by the same infinity, never by a finite value
+    assert o.within_bound([5.0, np.inf, -np.inf, np.nan], [np.inf] * 4, [np.inf] * 4).tolist() == \
+        [False, True, False, False]
+    assert o.within_bound([5.0], [-np.inf], [np.inf]).tolist() == [False]
     assert o.within_bound([1.0 + 1.1e-2], [1.0], [10.0]).tolist() == [False]
 
 
