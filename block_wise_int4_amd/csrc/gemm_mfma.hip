@@ -160,8 +160,8 @@ template <typename ST, int Q, bool HAS_ZP> struct KernelLds {
     static constexpr int kBytes = G::kStages * G::kBytes;
 };
 
-template <typename ST, int Q, bool HAS_ZP>
-__global__ __launch_bounds__(WAVES * 64, 1) void gemm_mfma_kernel(GemmParams p)
+template <typename ST, int Q, bool HAS_ZP, bool KTAIL>
+__global__ __launch_bounds__(WAVES * 64, 2) void gemm_mfma_kernel(GemmParams p)
 {
     typedef StageGeom<Q, (int)sizeof(ST), HAS_ZP> G;
     constexpr int NST = G::kStages;
@@ -213,35 +213,54 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_mfma_kernel(GemmParams p)
     // The LDS DMAs of one chunk, one "piece" (one instruction) at a time, so
     // they can be spread over the compute of an earlier chunk: pieces
     // 0 .. A_DMA-1 copy A rows, then the scale records and the zero-point
-    // records of the wave's tiles.
+    // records of the wave's tiles.  Each lane's part of an offset is fixed
+    // for the whole loop; the chunk's part is uniform and goes in the scalar
+    // offset.  Padding lanes of the record DMAs use an offset past every
+    // range, so they read zero.
+    constexpr uint32_t kFar = 0x80000000u;
+    uint32_t a_voff[A_DMA];
+#pragma unroll
+    for (int idx = 0; idx < A_DMA; ++idx) {
+        const int r = ROWS_PER_WAVE * wave + 4 * idx + (lane >> 4);
+        const int sg = (lane & 15) ^ (r & 15);         // logical segment at this slot
+        a_voff[idx] = ((uint32_t)r * (uint32_t)K + 8u * (uint32_t)sg) * 2u;
+    }
+    uint32_t s_voff[G::kScaleInstr], z_voff[G::kZpInstr > 0 ? G::kZpInstr : 1];
+#pragma unroll
+    for (int m = 0; m < G::kScaleInstr; ++m) {
+        const int d = m * 64 + lane;
+        const int tt = d / G::kScaleDw, o = d % G::kScaleDw;
+        s_voff[m] = d < TPW * G::kScaleDw
+            ? (uint32_t)(wave * TPW + tt) * (uint32_t)C * (uint32_t)(G::kScaleDw * 4) + (uint32_t)o * 4u : kFar;
+    }
+#pragma unroll
+    for (int m = 0; m < G::kZpInstr; ++m) {
+        constexpr int ZD = G::kZpDw > 0 ? G::kZpDw : 1;
+        const int d = m * 64 + lane;
+        const int tt = d / ZD, o = d % ZD;
+        z_voff[m] = d < TPW * G::kZpDw
+            ? (uint32_t)(wave * TPW + tt) * (uint32_t)C * (uint32_t)(ZD * 4) + (uint32_t)o * 4u : kFar;
+    }
     auto issue_piece = [&](int c, int st, int idx) {
         if (idx < A_DMA) {
-            // A rows [ROWS_PER_WAVE*wave + 4*idx, +4)
-            const int r = ROWS_PER_WAVE * wave + 4 * idx + (lane >> 4);
-            const int sg = (lane & 15) ^ (r & 15);          // logical segment at this slot
-            const int k = c * kChunkK + 8 * sg;
-            const uint32_t off = k < K ? ((uint32_t)r * (uint32_t)K + (uint32_t)k) * 2u : a_bytes;
+            // A rows [ROWS_PER_WAVE*wave + 4*idx, +4); a chunk reaching past K
+            // (K not a multiple of 128) sends its lanes past K out of range
+            uint32_t voff = a_voff[idx];
+            if (KTAIL && (c + 1) * kChunkK > K) {
+                const int r = ROWS_PER_WAVE * wave + 4 * idx + (lane >> 4);
+                if (c * kChunkK + 8 * ((lane & 15) ^ (r & 15)) >= K) voff = kFar;
+            }
             __builtin_amdgcn_raw_ptr_buffer_load_lds(a_rsrc, (lds_ptr_t)(stage_a(st) + (ROWS_PER_WAVE * wave + 4 * idx) * SEGS),
-                                                     16, off, 0, 0, 0);
+                                                     16, voff, (uint32_t)c * (kChunkK * 2), 0, 0);
         } else if (idx < A_DMA + G::kScaleInstr) {
-            // lanes past the records read zero through the range check
             const int m = idx - A_DMA;
-            const int d = m * 64 + lane;
-            const int tt = d / G::kScaleDw, o = d % G::kScaleDw;
-            const uint32_t off = d < TPW * G::kScaleDw
-                ? ((uint32_t)(wave * TPW + tt) * (uint32_t)C + (uint32_t)c) * (uint32_t)(G::kScaleDw * 4) + o * 4
-                : scale_bytes;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_ptr_t)(stage_m(st) + m * 256), 4, off, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_ptr_t)(stage_m(st) + m * 256), 4, s_voff[m],
+                                                     (uint32_t)c * (uint32_t)(G::kScaleDw * 4), 0, 0);
         } else {
             constexpr int ZD = G::kZpDw > 0 ? G::kZpDw : 1;
             const int m = idx - A_DMA - G::kScaleInstr;
-            const int d = m * 64 + lane;
-            const int tt = d / ZD, o = d % ZD;
-            const uint32_t off = d < TPW * G::kZpDw
-                ? ((uint32_t)(wave * TPW + tt) * (uint32_t)C + (uint32_t)c) * (uint32_t)(ZD * 4) + o * 4
-                : zp_bytes;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(z_rsrc, (lds_ptr_t)(stage_m(st) + (G::kScaleInstr + m) * 256), 4, off,
-                                                     0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(z_rsrc, (lds_ptr_t)(stage_m(st) + (G::kScaleInstr + m) * 256), 4,
+                                                     z_voff[m], (uint32_t)c * (uint32_t)(ZD * 4), 0, 0);
         }
     };
 
@@ -270,8 +289,8 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_mfma_kernel(GemmParams p)
 
     // per-chunk state: the rescale factor entering each group and the zero
     // points of the lane's columns, for the current and the next chunk
-    float ratio[PAIRS][Q], ratio_n[PAIRS][Q];
-    uint32_t zc[PAIRS][Q], zc_n[PAIRS][Q];
+    float ratioA[PAIRS][Q], ratioB[PAIRS][Q];
+    uint32_t zcA[PAIRS][Q], zcB[PAIRS][Q];
     auto read_meta = [&](int st, float (&rt)[PAIRS][Q], uint32_t (&z)[PAIRS][Q]) {
         const unsigned char* Ms = stage_m(st);
 #pragma unroll
@@ -309,16 +328,21 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_mfma_kernel(GemmParams p)
     // 2*(hs%2) + l/32 of 32-k step hs/2.  The repacked chunk holds that
     // octet in word hs/2 of the tile's lane (k-octet*16 + column), so one
     // 16-byte load per (pair, hs%2) brings a lane all four 32-k steps.
+    uint32_t b_voff[PAIRS][2];
+#pragma unroll
+    for (int q = 0; q < PAIRS; ++q)
+#pragma unroll
+        for (int ph = 0; ph < 2; ++ph) {
+            const int src = (2 * ph + oct) * 16 + i;
+            b_voff[q][ph] = (uint32_t)(wave * TPW + 2 * q + half) * (uint32_t)C * 1024u + (uint32_t)src * 16u;
+        }
     auto load_b = [&](int c, u4_t (&bq)[PAIRS][2]) {
 #pragma unroll
         for (int q = 0; q < PAIRS; ++q)
 #pragma unroll
-            for (int ph = 0; ph < 2; ++ph) {
-                const int src = (2 * ph + oct) * 16 + i;
-                const uint32_t off = ((uint32_t)(wave * TPW + 2 * q + half) * (uint32_t)C + (uint32_t)c) * 1024u +
-                                     (uint32_t)src * 16u;
-                bq[q][ph] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(c_rsrc, off, 0, 0));
-            }
+            for (int ph = 0; ph < 2; ++ph)
+                bq[q][ph] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                    c_rsrc, b_voff[q][ph], (uint32_t)c * 1024u, 0));
     };
     auto load_bw = [&](const u4_t (&bq)[PAIRS][2], uint32_t (&w)[PAIRS], int hs) {
 #pragma unroll
@@ -334,14 +358,13 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_mfma_kernel(GemmParams p)
         }
     };
 
-    // A fragments: a ring indexed by the step number (8 steps per chunk, so
-    // step hs of every chunk uses slot hs % 4), read two steps ahead; the
-    // first two steps of the next chunk are read in step 7, after the
-    // barrier that makes that chunk visible.  Code words: this chunk's and
-    // the next one's, loaded a chunk ahead.  B operands: unpacked one step
-    // ahead.
-    h8_t afr[4][RB];
-    u4_t bq[PAIRS][2], bq_n[PAIRS][2];
+    // A fragments: two sets indexed by the parity of the step, read one step
+    // ahead (the other wave on the SIMD covers the LDS latency); the next
+    // chunk's first step is read in step 7, after the barrier that makes
+    // that chunk visible.  Code words: this chunk's and the next one's,
+    // loaded a chunk ahead.  B operands: unpacked one step ahead.
+    h8_t afr[2][RB];
+    u4_t bqA[PAIRS][2], bqB[PAIRS][2];
     h8_t bop[2][PAIRS];
 
     // ---- prologue: chunks 0 and 1 in flight, chunk 0 read in ----
@@ -353,22 +376,30 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_mfma_kernel(GemmParams p)
 #pragma unroll
         for (int k = 0; k < NP; ++k) issue_piece(1, 1, k);
     }
-    load_b(0, bq);
+    load_b(0, bqA);
     // chunk 0's DMAs landed for this wave (later issues may stay in flight)
     if (C > 1) wait_vm<NP + 2 * PAIRS>();
     else wait_vm<2 * PAIRS>();
     block_sync_lds();
-    read_meta(0, ratio, zc);
+    read_meta(0, ratioA, zcA);
     load_afr(0, afr[0], 0);
-    load_afr(0, afr[1], 1);
     {
         uint32_t w[PAIRS];
-        load_bw(bq, w, 0);
-        unpack_b(w, zc, 0, bop[0]);
+        load_bw(bqA, w, 0);
+        unpack_b(w, zcA, 0, bop[0]);
     }
 
-    for (int c = 0; c < C; ++c) {
-        const int st = c % NST, nst = (c + 1) % NST, dst = (c + 2) % NST;
+    // One chunk.  The code words, rescale factors and zero points of the
+    // chunk and of the next one alternate between two register sets (the
+    // loop below runs two chunks per trip), so nothing is copied between
+    // chunks.  st: pipeline stage of chunk c (wave-uniform).
+    int st = 0;
+    auto chunk = [&](int c, const u4_t (&bq)[PAIRS][2], u4_t (&bq_n)[PAIRS][2],
+                     const float (&ratio)[PAIRS][Q], float (&ratio_n)[PAIRS][Q],
+                     const uint32_t (&zc)[PAIRS][Q], uint32_t (&zc_n)[PAIRS][Q])
+        __attribute__((always_inline)) {
+        const int nst = st == NST - 1 ? 0 : st + 1;
+        const int dst = nst == NST - 1 ? 0 : nst + 1;
         const bool more = c + 1 < C;        // wave-uniform
         const bool dma = c + 2 < C;
         // one 16-k step; hs is a compile-time constant (the interleave
@@ -379,13 +410,12 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_mfma_kernel(GemmParams p)
             constexpr int t_in = hs % HS_PER_GROUP; // step within the group
             // the next chunk's code words, a chunk ahead
             if (hs == 0 && more) load_b(c + 1, bq_n);
-            // LDS reads two steps ahead (step 7 reads the next chunk's first two)
-            if (hs + 2 < 8) {
-                load_afr(st, afr[(hs + 2) % 4], hs + 2);
-            } else if (hs == 7 && more) {
+            // LDS reads one step ahead (step 7 reads the next chunk's first)
+            if (hs + 1 < 8) {
+                load_afr(st, afr[(hs + 1) & 1], hs + 1);
+            } else if (more) {
                 read_meta(nst, ratio_n, zc_n);
                 load_afr(nst, afr[0], 0);
-                load_afr(nst, afr[1], 1);
             }
             // this chunk's share of the DMAs of chunk c+2
             if (hs < 6 && dma) {
@@ -403,7 +433,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_mfma_kernel(GemmParams p)
 #pragma unroll
                         for (int e = 0; e < 16; ++e) acc[rb][q][e] *= r;
                     }
-                    acc[rb][q] = mfma32(afr[hs % 4][rb], bop[hs & 1][q], acc[rb][q]);
+                    acc[rb][q] = mfma32(afr[hs & 1][rb], bop[hs & 1][q], acc[rb][q]);
                 }
             }
             // the next step's B operands
@@ -417,7 +447,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_mfma_kernel(GemmParams p)
             }
             // interleave: LDS reads first, then each MFMA followed by a share
             // of the VALU work and of the memory issue
-            constexpr int kReads = hs + 2 < 8 ? RB : (hs == 7 ? 2 * RB : 0);
+            constexpr int kReads = RB;
             if (kReads > 0) __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);   // DS reads
 #pragma unroll
             for (int k = 0; k < RB * PAIRS; ++k) {
@@ -443,16 +473,11 @@ __global__ __launch_bounds__(WAVES * 64, 1) void gemm_mfma_kernel(GemmParams p)
             block_sync_lds();   // ... and for every wave
         }
         step(std::integral_constant<int, 7>());
-#pragma unroll
-        for (int q = 0; q < PAIRS; ++q) {
-#pragma unroll
-            for (int g = 0; g < Q; ++g) {
-                ratio[q][g] = ratio_n[q][g];
-                zc[q][g] = zc_n[q][g];
-            }
-            bq[q][0] = bq_n[q][0];
-            bq[q][1] = bq_n[q][1];
-        }
+        st = nst;
+    };
+    for (int c = 0; c < C; c += 2) {
+        chunk(c, bqA, bqB, ratioA, ratioB, zcA, zcB);
+        if (c + 1 < C) chunk(c + 1, bqB, bqA, ratioB, ratioA, zcB, zcA);
     }
 
     // back from units of the last group's scale
@@ -484,7 +509,10 @@ template <typename ST, int Q, bool HAS_ZP>
 hipError_t launch_t(const GemmParams& p, hipStream_t s)
 {
     const int blocks = p.num_m * p.num_n;
-    gemm_mfma_kernel<ST, Q, HAS_ZP><<<dim3(blocks), dim3(WAVES * 64), 0, s>>>(p);
+    if (p.K % kChunkK != 0)
+        gemm_mfma_kernel<ST, Q, HAS_ZP, true><<<dim3(blocks), dim3(WAVES * 64), 0, s>>>(p);
+    else
+        gemm_mfma_kernel<ST, Q, HAS_ZP, false><<<dim3(blocks), dim3(WAVES * 64), 0, s>>>(p);
     return hipGetLastError();
 }
 
