@@ -12,10 +12,11 @@
 //   [64w, +64) of all 96 rows: 3 row blocks x 2 column pairs of 32x32 tiles.
 //   Two workgroups share a CU (two waves per SIMD).
 // * A rows reach LDS by buffer_load ... lds (no VGPR round trip) into a ring
-//   of three stages; the DMAs of a chunk are spread over the matrix work of
-//   the chunk two ahead.  A's 16-byte segments are XOR-swizzled by row, so
-//   fragment reads are conflict free.  Rows and k outside the operand read as
-//   zero through the range check.
+//   of as many stages as the workgroup's share of LDS holds (three for the
+//   common record sizes); the DMAs of chunk c + stages - 1 are spread over the
+//   matrix work of chunk c.  A's 16-byte segments are XOR-swizzled by row,
+//   so fragment reads are conflict free.  Rows and k outside the operand read
+//   as zero through the range check.
 // * Code words are loaded straight into the lanes that use them, a chunk
 //   ahead: the repacked 16-column tile (16 columns x 4 k-octets per 32 k)
 //   holds, in one 16-byte lane record, the four 32-k steps of one column and
@@ -47,9 +48,13 @@ constexpr int PAIRS = 2;           // 32-column pairs of tiles per wave
 constexpr int TPW = 2 * PAIRS;     // 16-column tiles per wave
 constexpr int SEGS = kChunkK / 8;  // 16-byte segments per A row per chunk
 constexpr int kGroupM = 4;         // m-blocks per XCD-local band
-constexpr int kLdsBudget = 160 * 1024;
+constexpr int kWgPerCu = 8 / WAVES;          // two waves per SIMD
+constexpr int kLdsCu = 160 * 1024;
+constexpr int kLdsBudget = kLdsCu / kWgPerCu;   // this workgroup's share
+constexpr int kMaxStages = 6;
 constexpr int ROWS_PER_WAVE = BM / WAVES;   // A rows each wave copies per chunk
 constexpr int A_DMA = ROWS_PER_WAVE / 4;    // 1 KiB (4-row) DMAs per wave per chunk
+static_assert(ROWS_PER_WAVE % 4 == 0, "A is copied in 4-row pieces");
 
 typedef float f16v_t __attribute__((ext_vector_type(16)));
 
@@ -79,7 +84,11 @@ template <int Q, int SS, bool HAS_ZP> struct StageGeom {
     static constexpr int kB = 0;                                       // codes go to VGPRs
     static constexpr int kMeta = WAVES * kMetaDwPad * 4;
     static constexpr int kBytes = kA + kB + kMeta;
-    static constexpr int kStages = 3 * kBytes <= kLdsBudget ? 3 : 2;
+    // as many pipeline stages as the workgroup's share of LDS holds (up to
+    // kMaxStages); when that is fewer than three (large scale records), three
+    // or more in the whole LDS, leaving one workgroup per CU
+    static constexpr int kFit = kLdsBudget / kBytes >= 3 ? kLdsBudget / kBytes : kLdsCu / kBytes;
+    static constexpr int kStages = kFit < kMaxStages ? kFit : kMaxStages;
     static constexpr int kDmaPerChunk = A_DMA + kMetaInstr;            // per wave
 };
 
@@ -161,7 +170,7 @@ template <typename ST, int Q, bool HAS_ZP> struct KernelLds {
 };
 
 template <typename ST, int Q, bool HAS_ZP, bool KTAIL>
-__global__ __launch_bounds__(WAVES * 64, 2) void gemm_mfma_kernel(GemmParams p)
+__global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmParams p)
 {
     typedef StageGeom<Q, (int)sizeof(ST), HAS_ZP> G;
     constexpr int NST = G::kStages;
@@ -279,7 +288,18 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_mfma_kernel(GemmParams p)
     constexpr int HS_PER_GROUP = 8 / Q;          // 16-k steps per group (group = 128/Q)
     constexpr int NP = G::kDmaPerChunk;           // DMA pieces per chunk and wave
     constexpr int NP_STEP = (NP + 5) / 6;         // pieces issued per step (steps 0..5)
-    static_assert(NST == 3, "the pipeline below keeps three stages");
+    static_assert(NST >= 3, "the pipeline keeps at least three stages");
+    static_assert((NST - 2) * NP + 2 * PAIRS < 64, "vmcnt range");
+    // Wait until chunk j's DMAs (this wave's) have landed, with y later
+    // chunks' DMAs and the next chunk's code words issued after them
+    // (y <= NST - 2; a smaller y than the truth only waits longer).
+    auto wait_landed = [&](int y) {
+        if constexpr (NST - 2 >= 4) { if (y >= 4) { wait_vm<4 * NP + 2 * PAIRS>(); return; } }
+        if constexpr (NST - 2 >= 3) { if (y >= 3) { wait_vm<3 * NP + 2 * PAIRS>(); return; } }
+        if constexpr (NST - 2 >= 2) { if (y >= 2) { wait_vm<2 * NP + 2 * PAIRS>(); return; } }
+        if (y >= 1) { wait_vm<NP + 2 * PAIRS>(); return; }
+        wait_vm<2 * PAIRS>();
+    };
 
     // units of acc per column pair: the scale of the last group with a
     // nonzero scale (groups past K have scale 0 and contribute exactly 0)
@@ -367,19 +387,18 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_mfma_kernel(GemmParams p)
     u4_t bqA[PAIRS][2], bqB[PAIRS][2];
     h8_t bop[2][PAIRS];
 
-    // ---- prologue: chunks 0 and 1 in flight, chunk 0 read in ----
-    if (C > 0) {
+    // ---- prologue: chunks 0 .. NST-2 in flight, chunk 0 read in ----
+    const int npre = C < NST - 1 ? C : NST - 1;
 #pragma unroll
-        for (int k = 0; k < NP; ++k) issue_piece(0, 0, k);
-    }
-    if (C > 1) {
+    for (int j = 0; j < NST - 1; ++j) {
+        if (j < npre) {
 #pragma unroll
-        for (int k = 0; k < NP; ++k) issue_piece(1, 1, k);
+            for (int k = 0; k < NP; ++k) issue_piece(j, j, k);
+        }
     }
     load_b(0, bqA);
     // chunk 0's DMAs landed for this wave (later issues may stay in flight)
-    if (C > 1) wait_vm<NP + 2 * PAIRS>();
-    else wait_vm<2 * PAIRS>();
+    wait_landed(npre - 1);
     block_sync_lds();
     read_meta(0, ratioA, zcA);
     load_afr(0, afr[0], 0);
@@ -399,9 +418,9 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_mfma_kernel(GemmParams p)
                      const uint32_t (&zc)[PAIRS][Q], uint32_t (&zc_n)[PAIRS][Q])
         __attribute__((always_inline)) {
         const int nst = st == NST - 1 ? 0 : st + 1;
-        const int dst = nst == NST - 1 ? 0 : nst + 1;
+        const int dst = st == 0 ? NST - 1 : st - 1;   // stage of chunk c + NST - 1
         const bool more = c + 1 < C;        // wave-uniform
-        const bool dma = c + 2 < C;
+        const bool dma = c + NST - 1 < C;
         // one 16-k step; hs is a compile-time constant (the interleave
         // pattern needs constant counts)
         auto step = [&](auto hs_c) {
@@ -417,10 +436,10 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_mfma_kernel(GemmParams p)
                 read_meta(nst, ratio_n, zc_n);
                 load_afr(nst, afr[0], 0);
             }
-            // this chunk's share of the DMAs of chunk c+2
+            // this chunk's share of the DMAs of chunk c + NST - 1
             if (hs < 6 && dma) {
 #pragma unroll
-                for (int k = hs * NP_STEP; k < (hs + 1) * NP_STEP && k < NP; ++k) issue_piece(c + 2, dst, k);
+                for (int k = hs * NP_STEP; k < (hs + 1) * NP_STEP && k < NP; ++k) issue_piece(c + NST - 1, dst, k);
             }
             // the matrix work, each group entered with its rescale
             const bool rescale = t_in == 0 && !(c == 0 && hs == 0);
@@ -466,10 +485,10 @@ __global__ __launch_bounds__(WAVES * 64, 2) void gemm_mfma_kernel(GemmParams p)
         step(std::integral_constant<int, 5>());
         step(std::integral_constant<int, 6>());
         if (more) {
-            // chunk c+1's DMAs landed for this wave (this chunk's later issues:
-            // chunk c+1's code words and chunk c+2's DMAs, may stay in flight) ...
-            if (dma) wait_vm<2 * PAIRS + NP>();
-            else wait_vm<2 * PAIRS>();
+            // chunk c+1's DMAs landed for this wave (later issues: chunk
+            // c+1's code words and the DMAs of chunks c+2 .. c+NST-1, may
+            // stay in flight) ...
+            wait_landed(C - c - 2 < NST - 2 ? C - c - 2 : NST - 2);
             block_sync_lds();   // ... and for every wave
         }
         step(std::integral_constant<int, 7>());

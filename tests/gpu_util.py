@@ -26,6 +26,27 @@ def upload(w: synth.Weight):
     return q
 
 
+_WS = {}
+
+
+def workspace(q, M):
+    """A GEMM workspace for (q, M) (zero-filled), shared by every call that
+    fits in it."""
+    from block_wise_int4_amd import mnb
+    n = mnb.mnb_gemm_workspace_bytes(q.desc, M)
+    buf = _WS.get("buf")
+    if buf is None or buf.numel() < n:
+        buf = torch().zeros(max(n, 256), dtype=torch().uint8, device="cuda")
+        _WS["buf"] = buf
+    return buf, n
+
+
+def gemm(q, a, M, y, stream=None):
+    from block_wise_int4_amd import mnb
+    ws, n = workspace(q, M)
+    mnb.mnb_gemm(q.desc, q.repacked, a, M, y, ws, n, stream=stream)
+
+
 def host(y) -> np.ndarray:
     torch().cuda.synchronize()
     return y.detach().cpu().numpy().astype(np.float64)

@@ -128,7 +128,7 @@ def test_gemv_parity(mnb, N, K, g, adt, sdt, zp):
     G.assert_within(G.host(y)[None, :], Y, B, "gemv N=%d K=%d g=%d %s" % (N, K, g, adt))
     # mnb_gemm with M = 1 is the same kernel and the same bits
     y2 = t.empty_like(y)
-    mnb.mnb_gemm(q.desc, q.repacked, G.to_dev(A), 1, y2)
+    G.gemm(q, G.to_dev(A), 1, y2)
     assert t.equal(y, y2)
 
 
@@ -240,7 +240,7 @@ def test_prefill_ragged_parity(mnb, M, N, K, g, zp, sdt):
     A = _act(M, K, sigma=0.5)
     q = G.upload(w)
     y = t.empty((M, N), dtype=t.float16, device="cuda")
-    mnb.mnb_gemm(q.desc, q.repacked, G.to_dev(A), M, y)
+    G.gemm(q, G.to_dev(A), M, y)
     assert mnb.mnb_last_variant().startswith("gemm_mfma")
     Y, B, _ = G.oracle_dense(A, w)
     G.assert_within(G.host(y), Y, B, "prefill M=%d N=%d K=%d g=%d" % (M, N, K, g))
@@ -256,7 +256,7 @@ def test_prefill_workload_sampled_parity(mnb):
     A = synth.workload_activation(wl)
     q = G.upload(w)
     y = t.empty((wl.M, wl.N), dtype=t.float16, device="cuda")
-    mnb.mnb_gemm(q.desc, q.repacked, G.to_dev(A), wl.M, y)
+    G.gemm(q, G.to_dev(A), wl.M, y)
     yh = G.host(y)
     rng = np.random.default_rng(5)
     ms = list(rng.integers(0, wl.M, 4000))
@@ -273,6 +273,33 @@ def test_prefill_workload_sampled_parity(mnb):
     assert np.isfinite(yh).all()
 
 
+def test_prefill_mid_size_sampled_parity(mnb):
+    """Mid-size prefill shapes: between one and two rounds of output tiles
+    (M=1000, N=14336: 11 x 56 tiles of 96 x 256) and fewer tiles than the
+    chip holds (M=300, N=1000), asymmetric zero points, g = 64 and 128.
+    Sampled outputs (every row at least once) against the oracle, then the
+    same call again must give identical bits."""
+    t = G.torch()
+    for (M, N, K, g, seed) in ((1000, 14336, 1024, 64, 3), (300, 1000, 2048, 128, 4)):
+        w = _weight(N, K, g, "f16", True, seed=seed, lo=0.002, hi=0.01)
+        A = _act(M, K, sigma=0.5, seed=seed)
+        q = G.upload(w)
+        a = G.to_dev(A)
+        y = t.empty((M, N), dtype=t.float16, device="cuda")
+        G.gemm(q, a, M, y)
+        yh = G.host(y)
+        rng = np.random.default_rng(seed)
+        ms = np.concatenate([rng.integers(0, M, 3000), np.arange(M)])
+        ns = np.concatenate([rng.integers(0, N, 3000), rng.integers(0, N, M)])
+        Y, B = o.matmul_nbits_at(A, w.packed, w.scales, w.zero_points, N, K, g, ms, ns)
+        G.assert_within(yh[ms, ns], Y, B, "mid-size prefill M=%d N=%d K=%d (sampled)" % (M, N, K))
+        assert np.isfinite(yh).all()
+        y2 = t.empty_like(y)
+        G.gemm(q, a, M, y2)
+        t.cuda.synchronize()
+        assert t.equal(y, y2)
+
+
 # ------------------------------------------------------------ properties ----
 
 def test_results_are_deterministic(mnb):
@@ -283,8 +310,8 @@ def test_results_are_deterministic(mnb):
         a = G.to_dev(_act(M, K))
         y1 = t.empty((M, N), dtype=t.float16, device="cuda")
         y2 = t.empty_like(y1)
-        mnb.mnb_gemm(q.desc, q.repacked, a, M, y1)
-        mnb.mnb_gemm(q.desc, q.repacked, a, M, y2)
+        G.gemm(q, a, M, y1)
+        G.gemm(q, a, M, y2)
         t.cuda.synchronize()
         assert t.equal(y1, y2)
 
@@ -298,8 +325,8 @@ def test_absent_zero_points_equal_explicit_eights(mnb):
         q, q8 = G.upload(w), G.upload(w8)
         a = G.to_dev(_act(M, K))
         y, y8 = (t.empty((M, N), dtype=t.float16, device="cuda") for _ in range(2))
-        mnb.mnb_gemm(q.desc, q.repacked, a, M, y)
-        mnb.mnb_gemm(q8.desc, q8.repacked, a, M, y8)
+        G.gemm(q, a, M, y)
+        G.gemm(q8, a, M, y8)
         t.cuda.synchronize()
         assert t.equal(y, y8)
 
@@ -315,7 +342,7 @@ def test_code_equal_to_zero_point_gives_zero(mnb):
                          o.pack_zero_points(z))
         q = G.upload(w)
         y = t.full((M, N), 7.0, dtype=t.float16, device="cuda")
-        mnb.mnb_gemm(q.desc, q.repacked, G.to_dev(_act(M, K)), M, y)
+        G.gemm(q, G.to_dev(_act(M, K)), M, y)
         assert (G.host(y) == 0.0).all()
 
 
@@ -329,7 +356,7 @@ def test_nan_and_inf_propagate(mnb):
             A[M - 1, 100] = np.inf
         q = G.upload(w)
         y = t.empty((M, N), dtype=t.float16, device="cuda")
-        mnb.mnb_gemm(q.desc, q.repacked, G.to_dev(A), M, y)
+        G.gemm(q, G.to_dev(A), M, y)
         Y, B, _ = G.oracle_dense(A, w)
         G.assert_within(G.host(y), Y, B, "nan/inf M=%d" % M)
 
@@ -358,7 +385,7 @@ def test_zero_and_non_finite_scales(mnb):
         for M in (1, 4, 40):
             A = _act(M, K, seed=M)
             y = t.empty((M, N), dtype=t.float16, device="cuda")
-            mnb.mnb_gemm(q.desc, q.repacked, G.to_dev(A), M, y)
+            G.gemm(q, G.to_dev(A), M, y)
             Y, B, _ = G.oracle_dense(A, w2)
             yh = G.host(y)
             G.assert_within(yh, Y, B, "special scales M=%d N=%d K=%d g=%d %s" % (M, N, K, g, sdt))
