@@ -191,21 +191,20 @@ def kernel_source_sha(variant):
 
 
 def counted_traffic(workload, variant):
-    """HBM bytes per launch of `workload`, from the committed counter summary
-    profiles/hbm_traffic.txt (FETCH_SIZE + WRITE_SIZE, each scaled by what the
-    counter reads for the plain copy).  None when no summary covers this
-    workload or its kernel source has changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
-    if not os.path.exists(path):
-        return None
+    """HBM bytes per launch of `workload`, from the committed counter summaries
+    profiles/*.txt (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter
+    reads for the plain copy).  None when no summary covers this workload or
+    its kernel source has changed since the counters were taken."""
+    import glob
     sha = kernel_source_sha(variant)
-    with open(path) as fh:
-        for line in fh:
-            if not line.startswith("traffic|"):
-                continue
-            _, name, src_sha, nbytes = [x.strip() for x in line.split("|")[:4]]
-            if name == workload and src_sha == sha:
-                return int(nbytes)
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.txt"))):
+        with open(path) as fh:
+            for line in fh:
+                if not line.startswith("traffic|"):
+                    continue
+                _, name, src_sha, nbytes = [x.strip() for x in line.split("|")[:4]]
+                if name == workload and src_sha == sha:
+                    return int(nbytes)
     return None
 
 
