@@ -142,7 +142,29 @@ __device__ __forceinline__ float chunk_dot_f16(const ChunkRegs<ST, Q, HAS_ZP>& r
     constexpr int NS = LaneGroups<Q>::NS;
     const uint32_t dw[4] = {r.d.x, r.d.y, r.d.z, r.d.w};
     const f4_t zero = {0.f, 0.f, 0.f, 0.f};
-    f4_t grp = zero;
+    if constexpr (Q <= 4) {
+        // all four operands first, then one independent MFMA chain per
+        // group, then the scales in group order: the chains overlap instead
+        // of each waiting for the one before
+        constexpr int steps = 4 / Q;   // k-steps per group
+        h8_t b[4], a[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int sj = LaneGroups<Q>::sidx(j);
+            const uint32_t z = HAS_ZP ? (r.zw >> (4 * sj)) & 15u : 8u;
+            h2_t q[4];
+            unpack8(dw[j], zp_const(z), q);
+            b[j] = as_h8(q);
+            a[j] = *reinterpret_cast<const h8_t*>(as + c * kChunkK + 32 * j + 8 * h);
+        }
+        f4_t grp[Q];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) grp[j / steps] = mfma16(a[j], b[j], (j % steps == 0) ? zero : grp[j / steps]);
+#pragma unroll
+        for (int gq = 0; gq < Q; ++gq)
+            acc = __builtin_fmaf(grp[gq][0], scale_at<ST, NS>(r.s, LaneGroups<Q>::sidx(gq * steps)), acc);
+        return acc;
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int sj = LaneGroups<Q>::sidx(j);
@@ -151,11 +173,7 @@ __device__ __forceinline__ float chunk_dot_f16(const ChunkRegs<ST, Q, HAS_ZP>& r
         unpack8(dw[j], zp_const(z), q);
         const h8_t b = as_h8(q);
         const h8_t a = *reinterpret_cast<const h8_t*>(as + c * kChunkK + 32 * j + 8 * h);
-        if (Q <= 4) {
-            constexpr int steps = 4 / (Q <= 4 ? Q : 1);   // k-steps per group
-            grp = mfma16(a, b, (j % steps == 0) ? zero : grp);
-            if ((j + 1) % steps == 0) acc = __builtin_fmaf(grp[0], scale_at<ST, NS>(r.s, sj), acc);
-        } else {
+        {
             // group 16: octets 0,1 of the step are group 2j, octets 2,3 group
             // 2j+1.  A lane's scale vector holds the groups of its own octet
             // half (h >> 1), so the other half's scale comes from the lane 32
