@@ -39,7 +39,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--only", default="",
-                   help="comma list of: gemv,gate_up,small_m,prefill (default all); "
+                   help="comma list of: gemv,gate_up,down,small_m,prefill (default all); "
                         "copy adds a plain 256 MiB device copy, the reference kernel "
                         "for scaling the HBM byte counters")
     return p.parse_args()
@@ -210,7 +210,7 @@ def counted_traffic(workload, variant):
 
 def build_workloads(only):
     from block_wise_int4_amd import synth as S
-    sel = set(x for x in only.split(",") if x) or {"gemv", "gate_up", "small_m", "prefill"}
+    sel = set(x for x in only.split(",") if x) or {"gemv", "gate_up", "down", "small_m", "prefill"}
     wl = [CopyWorkload()] if "copy" in sel else []
     if "gemv" in sel:
         c = S.DECODE_GEMV
@@ -219,6 +219,9 @@ def build_workloads(only):
         c = S.GATE_UP_SWIGLU
         g, u = S.workload_weights(c)
         wl.append(Workload(c.name, 1, [g, u], c.K, c.N, c.group, seed=c.seed + (1,)))
+    if "down" in sel:
+        c = S.DOWN_PROJ_GEMV
+        wl.append(Workload(c.name, 1, [S.workload_weights(c)], c.K, c.N, c.group, seed=c.seed + (1,)))
     if "small_m" in sel:
         c = S.SMALL_M_GEMM
         w = S.workload_weights(c)

@@ -56,6 +56,10 @@ SMALL_M_GEMM = Workload("small-M GEMM K=4096 N=14336 g=64 f16 asym-zp", 16, 4096
                         "f16", "f16", (0.005, 0.02), True, seed=(4,))
 PREFILL_GEMM = Workload("prefill GEMM M=2048 K=4096 N=14336 g=128 f16 asym-zp", 2048, 4096, 14336, 128,
                         "f16", "f16", (0.002, 0.01), True, sigma=0.5, seed=(5,))
+# The next measured workload: the MLP's down projection at M=1 (tall and
+# skinny, K > N), the step after the fused gate/up.
+DOWN_PROJ_GEMV = Workload("down-projection GEMV M=1 K=11008 N=4096 g=128 f16", 1, 11008, 4096, 128,
+                          "f16", "f16", (0.002, 0.01), False, seed=(6,))
 SMALL_M_VALUES = (2, 4, 8, 16)
 
 

@@ -132,6 +132,20 @@ def test_gemv_parity(mnb, N, K, g, adt, sdt, zp):
     assert t.equal(y, y2)
 
 
+def test_down_projection_workload_parity(mnb):
+    """The down projection at M=1 (K=11008 > N=4096, g=128, default zero
+    point): the workload's own operands, every output against the oracle."""
+    t = G.torch()
+    wl = synth.DOWN_PROJ_GEMV
+    w = synth.workload_weights(wl)
+    A = synth.workload_activation(wl)
+    q = G.upload(w)
+    y = t.empty(wl.N, dtype=t.float16, device="cuda")
+    mnb.mnb_gemv(q.desc, q.repacked, G.to_dev(A.reshape(-1)), y)
+    Y, B, _ = G.oracle_dense(A, w)
+    G.assert_within(G.host(y)[None, :], Y, B, "down projection")
+
+
 def test_tiny_gemv_workload_exact_match_with_one_hot_rows(mnb):
     """One-hot activations pull single dequantized weights through the f32
     GEMV: the result is the exact product (code - zp) * scale rounded once to
