@@ -24,11 +24,22 @@
  *  [SILU] ferrox-cuda gpu.rs -- kernel silu_mul_f32: silu(g) * u with
  *         silu(x) = x / (1 + e^-x); matmul_nbits.rs (dev.3) --
  *         gate_up_silu_f32 states the same function in a two-branch form.
+ *  [BIAS] onnx-runtime-ep-cuda 0.1.0-dev.3, src/kernels/matmul_nbits.rs --
+ *         the fp16 GEMV bias epilogue (fold_bias_f16) and the bias stage
+ *         records of the GEMV dispatch; marlin_gemm.rs (dev.6) -- the same
+ *         epilogue (fold_bias) with a per-row bias stride.  An optional fp16
+ *         bias b[n] (or, with a row stride, b[m*stride + n]) is added to the
+ *         fp32 accumulator in one of two ways: added in fp32 and rounded once
+ *         to fp16 (the operator's own bias), or rounded to fp16 first and then
+ *         added in fp32 and rounded again (a folded elementwise Add, which
+ *         must stay byte-identical to the two-operator path).
  *
  * Parity pins for every function live in tests/test_oracle.py (worked
  * examples, exhaustive nibble decode, pack/unpack identity, code==zp gives
  * zero, exact-rational brute force, integer special case, fp16 decode against
- * numpy for all 65536 bit patterns, silu against scipy's expit).
+ * numpy for all 65536 bit patterns, silu against scipy's expit, binary16
+ * rounding against numpy's conversion at every value and every tie, the bias
+ * epilogue against numpy binary32 arithmetic and hand-worked cases).
  */
 #include <math.h>
 #include <stdint.h>
@@ -261,4 +272,62 @@ int oracle_max_threads(void)
 #else
     return 1;
 #endif
+}
+
+/* ---- output rounding and the bias epilogue [BIAS] ------------------------ */
+
+/* The binary16 value nearest to x, ties to the even significand (the
+ * standard's default rounding); beyond the largest finite value (65504) the
+ * result is infinity when x is at least 65520 (the tie between 65504 and
+ * 2^16 goes to the even 2^16, which overflows); NaN gives a quiet NaN; the sign
+ * of zero is kept.  Returns the bit pattern. */
+uint16_t oracle_round_f16(double x)
+{
+    if (isnan(x)) return 0x7E00;
+    const uint16_t sign = signbit(x) ? 0x8000 : 0;
+    const double a = fabs(x);
+    if (isinf(a)) return sign | 0x7C00;
+    if (a == 0.0) return sign;
+    int e;
+    frexp(a, &e);                      /* a = f * 2^e, f in [0.5, 1) */
+    /* spacing of binary16 values around a: 2^(e-11) in a normal binade,
+     * 2^-24 among the subnormals and in the lowest normal binade */
+    int ulp = e - 11;
+    if (ulp < -24) ulp = -24;
+    const double q = ldexp(a, -ulp);   /* a in units of that spacing, exact */
+    const double lo = floor(q);
+    const double rest = q - lo;        /* exact */
+    double n = lo;
+    if (rest > 0.5 || (rest == 0.5 && fmod(lo, 2.0) != 0.0)) n = lo + 1.0;
+    const double v = ldexp(n, ulp);    /* the rounded magnitude */
+    if (v > 65504.0) return sign | 0x7C00;
+    if (v < ldexp(1.0, -14)) return sign | (uint16_t)(v * ldexp(1.0, 24));   /* subnormal */
+    int ev;
+    frexp(v, &ev);                     /* v = f * 2^ev: exponent field ev + 14 */
+    const double frac = ldexp(v, 11 - ev) - 1024.0;
+    return sign | (uint16_t)((ev + 14) << 10) | (uint16_t)frac;
+}
+
+void oracle_round_f16_array(const double* x, int64_t count, uint16_t* out)
+{
+    for (int64_t i = 0; i < count; ++i) out[i] = oracle_round_f16(x[i]);
+}
+
+/* One fp16 output with a bias: acc is the binary32 accumulator, b the bias
+ * (binary16 bits).  after_round 0: acc + b in binary32, rounded once to
+ * binary16.  after_round 1: acc rounded to binary16, then + b in binary32,
+ * rounded to binary16 again. */
+uint16_t oracle_bias_f16(float acc, uint16_t b, int after_round)
+{
+    const float bf = (float)oracle_f16_to_f64(b);   /* exact: binary16 is a subset of binary32 */
+    float base = acc;
+    if (after_round) base = (float)oracle_f16_to_f64(oracle_round_f16((double)acc));
+    const float sum = base + bf;                     /* one binary32 addition */
+    return oracle_round_f16((double)sum);
+}
+
+void oracle_bias_f16_array(const float* acc, const uint16_t* b, int64_t count, int after_round,
+                           uint16_t* out)
+{
+    for (int64_t i = 0; i < count; ++i) out[i] = oracle_bias_f16(acc[i], b[i], after_round);
 }

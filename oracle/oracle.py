@@ -71,6 +71,12 @@ def _load():
     lib.oracle_pack_codes.argtypes = [p, i64, i64, i64, p]
     lib.oracle_pack_zero_points.argtypes = [p, i64, i64, p]
     lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_round_f16.argtypes = [ctypes.c_double]
+    lib.oracle_round_f16.restype = ctypes.c_uint16
+    lib.oracle_round_f16_array.argtypes = [p, i64, p]
+    lib.oracle_bias_f16.argtypes = [ctypes.c_float, ctypes.c_uint16, ctypes.c_int]
+    lib.oracle_bias_f16.restype = ctypes.c_uint16
+    lib.oracle_bias_f16_array.argtypes = [p, p, i64, ctypes.c_int, p]
     _lib = lib
     return lib
 
@@ -212,6 +218,35 @@ def pack_zero_points(z: np.ndarray) -> np.ndarray:
     out = np.empty(N * ((kb + 1) // 2), dtype=np.uint8)
     _load().oracle_pack_zero_points(_ptr(z), N, kb, _ptr(out))
     return out.reshape(N, (kb + 1) // 2)
+
+
+# ---- output rounding and the bias epilogue ---------------------------------
+
+def round_f16(x) -> np.ndarray:
+    """binary16 nearest to each value (ties to even), as float16."""
+    x = np.ascontiguousarray(x, np.float64)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().oracle_round_f16_array(_ptr(x), x.size, _ptr(out))
+    return out.view(np.float16)
+
+
+def bias_epilogue_f16(acc, bias, after_round: bool) -> np.ndarray:
+    """fp16 outputs of the bias epilogue from fp32 accumulators and fp16
+    biases (same shape): fp16(acc + b) or, after_round, fp16(fp16(acc) + b)."""
+    acc = np.ascontiguousarray(acc, np.float32)
+    b = np.ascontiguousarray(bias, np.float16).view(np.uint16)
+    assert acc.shape == b.shape
+    out = np.empty(acc.shape, dtype=np.uint16)
+    _load().oracle_bias_f16_array(_ptr(acc), _ptr(b), acc.size, int(bool(after_round)), _ptr(out))
+    return out.view(np.float16)
+
+
+def bias_bound(Y: np.ndarray, Bnd: np.ndarray, bias64: np.ndarray) -> np.ndarray:
+    """Tolerance of a biased fp16 output against Y + b (fp64), a reading: the
+    matmul's own rule for the accumulator, then one binary32 addition and one
+    binary16 rounding of the sum (together at most 2^-10 of its magnitude)."""
+    e = REL_TOL * np.asarray(Bnd, np.float64) + ABS_TOL
+    return e + 2.0 ** -10 * (np.abs(np.asarray(Y, np.float64) + bias64) + e)
 
 
 # ---- acceptance ------------------------------------------------------------

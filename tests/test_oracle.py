@@ -239,10 +239,56 @@ def pin_swiglu():
     assert (o.swiglu(big, np.ones(2)) == big).all()
 
 
+def pin_round_f16_against_numpy():
+    """binary16 rounding: every finite binary16 value is its own rounding;
+    every tie between neighbours (exact in fp64), values just off each tie,
+    and random magnitudes agree with numpy's correctly rounded conversion;
+    the overflow edge (65519.99 -> 65504, 65520 -> inf) and the subnormal
+    ties (2^-25 -> 0, 3*2^-25 -> 2^-23)."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = bits.view(np.float16)
+    fin = np.isfinite(vals)
+    assert (o.round_f16(vals[fin].astype(np.float64)).view(np.uint16) == bits[fin]).all()
+    pos = np.sort(np.unique(vals[fin & (vals > 0)].astype(np.float64)))
+    mids = (pos[:-1] + pos[1:]) / 2.0                      # exact: adjacent binary16 values
+    probes = np.concatenate([mids, -mids, mids * (1 + 2.0 ** -40), mids * (1 - 2.0 ** -40),
+                             np.random.default_rng(3).standard_normal(20000) *
+                             10.0 ** np.random.default_rng(4).uniform(-9, 5, 20000)])
+    ref = probes.astype(np.float16).view(np.uint16)
+    assert (o.round_f16(probes).view(np.uint16) == ref).all()
+    edge = o.round_f16([65519.99, 65520.0, -65520.0, 2.0 ** -25, 3 * 2.0 ** -25]).view(np.uint16)
+    assert edge.tolist() == [0x7BFF, 0x7C00, 0xFC00, 0x0000, 0x0002]
+
+
+def pin_bias_epilogue():
+    """The two bias conventions, by hand and against numpy binary32 arithmetic.
+    By hand: acc = 1 + 2^-11 (exact in fp32), b = 2^-11: fused, the sum
+    1 + 2^-10 is a binary16 value; after rounding, fp16(acc) is the tie 1.0
+    (even) and 1.0 + 2^-11 is again a tie, so 1.0.  acc = 65520, b = -32:
+    fused, 65488 is the tie between 65472 (even) and 65504, so 65472; after
+    rounding, fp16(65520) is already infinity, and inf - 32 stays infinite."""
+    acc = np.array([1 + 2.0 ** -11, 65520.0], np.float32)
+    b = np.array([2.0 ** -11, -32.0], np.float16)
+    assert o.bias_epilogue_f16(acc, b, False).astype(np.float64).tolist() == [1 + 2.0 ** -10, 65472.0]
+    assert o.bias_epilogue_f16(acc, b, True).astype(np.float64).tolist() == [1.0, np.inf]
+    rng = np.random.default_rng(11)
+    n = 50000
+    acc = (rng.standard_normal(n) * 10.0 ** rng.uniform(-4, 3, n)).astype(np.float32)
+    # some accumulators exactly halfway between binary16 neighbours
+    h = rng.standard_normal(n // 10).astype(np.float16)
+    acc[: n // 10] = (h.astype(np.float32) + np.spacing(h).astype(np.float32) / 2)
+    b = (rng.standard_normal(n) * 10.0 ** rng.uniform(-4, 2, n)).astype(np.float16)
+    fused = (acc + b.astype(np.float32)).astype(np.float16)
+    after = (acc.astype(np.float16).astype(np.float32) + b.astype(np.float32)).astype(np.float16)
+    assert (o.bias_epilogue_f16(acc, b, False).view(np.uint16) == fused.view(np.uint16)).all()
+    assert (o.bias_epilogue_f16(acc, b, True).view(np.uint16) == after.view(np.uint16)).all()
+    assert (fused != after).any()
+
+
 PINS = [pin_worked_examples, pin_exhaustive_nibbles, pin_pack_unpack_identity,
         pin_code_equals_zero_point_gives_zero, pin_bruteforce_exact,
         pin_integer_special_case, pin_linear_and_one_hot, pin_fp16_decode_all_patterns,
-        pin_swiglu]
+        pin_swiglu, pin_round_f16_against_numpy, pin_bias_epilogue]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -299,6 +345,11 @@ MUTANTS = {
     "fp16 subnormal scale": ("ldexp((double)frac, -24)", "ldexp((double)frac, -25)"),
     "silu sign": ("(x / (1.0 + exp(-x))) * U[i]", "(x / (1.0 + exp(x))) * U[i]"),
     "magnitude sum signed": ("mag += fabs(p);", "mag += p;"),
+    "binary16 ties away from zero": ("(rest == 0.5 && fmod(lo, 2.0) != 0.0)", "(rest == 0.5)"),
+    "binary16 largest finite treated as overflow": ("if (v > 65504.0) return", "if (v >= 65504.0) return"),
+    "binary16 subnormal spacing": ("if (ulp < -24) ulp = -24;", "if (ulp < -25) ulp = -25;"),
+    "bias added before rounding in both modes": ("if (after_round) base =", "if (0) base ="),
+    "bias rounded before the add in both modes": ("if (after_round) base =", "if (1) base ="),
 }
 
 
