@@ -64,6 +64,9 @@ struct GemmParams {
     uint32_t w_bytes;      // repacked size (buffer range)
     const _Float16* a;
     __half* y;
+    const __half* bias;    // optional, element (m, n) at bias[m * bias_stride + n]
+    int64_t bias_stride;
+    int bias_after_round;
     int M, N, K, C;
     int T;                 // column tiles
     int num_m, num_n;      // workgroup grid
@@ -518,7 +521,9 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int m = m0 + rb * 32 + 8 * (e >> 2) + 4 * oct + (e & 3);
-                if (m < p.M) p.y[(int64_t)m * p.N + n] = __float2half_rn(acc[rb][q][e]);
+                if (m < p.M)
+                    p.y[(int64_t)m * p.N + n] = finish_output(acc[rb][q][e], p.bias, (int64_t)m * p.bias_stride + n,
+                                                              p.bias_after_round);
             }
         }
     }
@@ -551,7 +556,7 @@ hipError_t launch_q(const Layout& L, const GemmParams& p, hipStream_t s)
 int64_t gemm_mfma_max_repacked_bytes() { return (int64_t)0x7FFFFF00; }
 
 hipError_t launch_gemm_mfma(const Layout& L, const WeightView& w, const void* a, int64_t m,
-                            void* y, hipStream_t stream, const char** variant)
+                            const Bias& bias, void* y, hipStream_t stream, const char** variant)
 {
     GemmParams p;
     p.w = w.codes;   // the codes section starts the repacked buffer
@@ -560,6 +565,9 @@ hipError_t launch_gemm_mfma(const Layout& L, const WeightView& w, const void* a,
     p.w_bytes = (uint32_t)L.total;
     p.a = static_cast<const _Float16*>(a);
     p.y = static_cast<__half*>(y);
+    p.bias = static_cast<const __half*>(bias.ptr);
+    p.bias_stride = bias.row_stride;
+    p.bias_after_round = bias.after_round;
     p.M = (int)m;
     p.N = (int)L.N;
     p.K = (int)L.K;

@@ -30,6 +30,9 @@ struct SmallParams {
     const uint8_t* zp;
     const _Float16* a;
     __half* y;
+    const __half* bias;    // optional, element (m, n) at bias[m * bias_stride + n]
+    int64_t bias_stride;
+    int bias_after_round;
     int M, N, K, C;
     int64_t T;
 };
@@ -177,7 +180,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_small_kernel(SmallParams p)
             float v = 0.0f;
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) v += red[w][tt][e];
-            p.y[(int64_t)row * p.N + n] = __float2half_rn(v);
+            p.y[(int64_t)row * p.N + n] = finish_output(v, p.bias, (int64_t)row * p.bias_stride + n,
+                                                        p.bias_after_round);
         }
     }
 }
@@ -206,7 +210,7 @@ hipError_t launch_q(const Layout& L, const SmallParams& p, hipStream_t s)
 size_t gemm_small_workspace(const Layout&, int64_t) { return 0; }
 
 hipError_t launch_gemm_small(const Layout& L, const WeightView& w, const void* a, int64_t m,
-                             void* y, void*, hipStream_t stream, const char** variant)
+                             const Bias& bias, void* y, void*, hipStream_t stream, const char** variant)
 {
     SmallParams p;
     p.codes = reinterpret_cast<const u4_t*>(w.codes);
@@ -214,6 +218,9 @@ hipError_t launch_gemm_small(const Layout& L, const WeightView& w, const void* a
     p.zp = w.zp;
     p.a = static_cast<const _Float16*>(a);
     p.y = static_cast<__half*>(y);
+    p.bias = static_cast<const __half*>(bias.ptr);
+    p.bias_stride = bias.row_stride;
+    p.bias_after_round = bias.after_round;
     p.M = (int)m;
     p.N = (int)L.N;
     p.K = (int)L.K;

@@ -40,6 +40,8 @@ struct GemvParams {
     GemvWeight w[2];
     const void* a;
     void* y;
+    const void* bias;      // optional [N], the output's dtype
+    int bias_after_round;
     int N, K, C;
 };
 
@@ -351,7 +353,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
         if (n < p.N) {
             float out = r[0];
             if (FUSED) out = silu_f32(r[0]) * r[NW - 1];
-            static_cast<AT*>(p.y)[n] = from_f32<AT>(out);
+            static_cast<AT*>(p.y)[n] = finish_output(out, static_cast<const AT*>(p.bias), n, p.bias_after_round);
         }
     }
 }
@@ -401,7 +403,7 @@ int64_t gemv_max_k(bool f16_act)
 }
 
 hipError_t launch_gemv(const Layout& L, const WeightView& gate, const WeightView* up,
-                       const void* a, bool f16_act, void* y, hipStream_t stream,
+                       const void* a, bool f16_act, const Bias& bias, void* y, hipStream_t stream,
                        const char** variant)
 {
     GemvParams p;
@@ -409,6 +411,8 @@ hipError_t launch_gemv(const Layout& L, const WeightView& gate, const WeightView
     p.w[1] = up ? gw(*up) : gw(gate);
     p.a = a;
     p.y = y;
+    p.bias = bias.ptr;
+    p.bias_after_round = bias.after_round;
     p.N = (int)L.N;
     p.K = (int)L.K;
     p.C = (int)L.C;

@@ -177,7 +177,8 @@ mnb_status mnb_repack(const mnb_weight_desc* w, const uint8_t* packed, const voi
 }
 
 static mnb_status gemv_common(const mnb_weight_desc* w, const void* gate, const void* up,
-                              const void* a, int32_t a_dtype, void* y, void* stream)
+                              const void* a, int32_t a_dtype, const mnb::Bias& bias, void* y,
+                              void* stream)
 {
     Layout L;
     MNB_TRY(check_desc(w, &L));
@@ -191,12 +192,13 @@ static mnb_status gemv_common(const mnb_weight_desc* w, const void* gate, const 
     if (up) MNB_TRY(check_ptr(up, 256, "up_repacked"));
     MNB_TRY(check_ptr(a, 16, "a"));
     MNB_TRY(check_ptr(y, f16 ? 2 : 4, "y"));
+    if (bias.ptr) MNB_TRY(check_ptr(bias.ptr, f16 ? 2 : 4, "bias"));
     MNB_TRY(check_device());
     const char* variant = "";
     const mnb::WeightView gv = mnb::view_of(L, gate);
     mnb::WeightView uv;
     if (up) uv = mnb::view_of(L, up);
-    return launched(mnb::launch_gemv(L, gv, up ? &uv : nullptr, a, f16, y,
+    return launched(mnb::launch_gemv(L, gv, up ? &uv : nullptr, a, f16, bias, y,
                                      static_cast<hipStream_t>(stream), &variant),
                     variant);
 }
@@ -204,7 +206,7 @@ static mnb_status gemv_common(const mnb_weight_desc* w, const void* gate, const 
 mnb_status mnb_gemv(const mnb_weight_desc* w, const void* repacked, const void* a, int32_t a_dtype,
                     void* y, void* stream)
 {
-    return gemv_common(w, repacked, nullptr, a, a_dtype, y, stream);
+    return gemv_common(w, repacked, nullptr, a, a_dtype, mnb::Bias(), y, stream);
 }
 
 mnb_status mnb_gemv_gate_up_swiglu(const mnb_weight_desc* w, const void* gate_repacked,
@@ -212,7 +214,7 @@ mnb_status mnb_gemv_gate_up_swiglu(const mnb_weight_desc* w, const void* gate_re
                                    void* y, void* stream)
 {
     if (!up_repacked) return fail(MNB_ERR_INVALID_ARGUMENT, "up_repacked is NULL");
-    return gemv_common(w, gate_repacked, up_repacked, a, a_dtype, y, stream);
+    return gemv_common(w, gate_repacked, up_repacked, a, a_dtype, mnb::Bias(), y, stream);
 }
 
 static size_t workspace_for(const Layout& L, int64_t m)
@@ -233,15 +235,16 @@ size_t mnb_gemm_workspace_bytes(const mnb_weight_desc* w, int64_t m)
     return workspace_for(L, m);
 }
 
-mnb_status mnb_gemm(const mnb_weight_desc* w, const void* repacked, const void* a, int64_t m,
-                    int32_t a_dtype, void* y, void* workspace, size_t workspace_bytes, void* stream)
+static mnb_status gemm_common(const mnb_weight_desc* w, const void* repacked, const void* a, int64_t m,
+                              int32_t a_dtype, const mnb::Bias& bias, void* y, void* workspace,
+                              size_t workspace_bytes, void* stream)
 {
     Layout L;
     MNB_TRY(check_desc(w, &L));
     MNB_TRY(check_act_dtype(a_dtype));
     if (m < 0) return fail(MNB_ERR_INVALID_ARGUMENT, "M must be >= 0 (got %lld)", (long long)m);
     if (m > INT32_MAX) return fail(MNB_ERR_INVALID_ARGUMENT, "M must fit in 32 bits");
-    if (m == 1) return gemv_common(w, repacked, nullptr, a, a_dtype, y, stream);
+    if (m == 1) return gemv_common(w, repacked, nullptr, a, a_dtype, bias, y, stream);
     if (m > 1 && a_dtype != MNB_F16)
         return fail(MNB_ERR_UNSUPPORTED, "M>1 GEMM takes fp16 activations only");
     const size_t need = workspace_for(L, m);
@@ -253,15 +256,42 @@ mnb_status mnb_gemm(const mnb_weight_desc* w, const void* repacked, const void* 
     MNB_TRY(check_ptr(repacked, 256, "repacked"));
     MNB_TRY(check_ptr(a, 16, "a"));
     MNB_TRY(check_ptr(y, 2, "y"));
+    if (bias.ptr) MNB_TRY(check_ptr(bias.ptr, 2, "bias"));
     MNB_TRY(check_device());
     const mnb::WeightView v = mnb::view_of(L, repacked);
     const char* variant = "";
     hipError_t e;
     if (m <= 16)
-        e = mnb::launch_gemm_small(L, v, a, m, y, workspace, static_cast<hipStream_t>(stream), &variant);
+        e = mnb::launch_gemm_small(L, v, a, m, bias, y, workspace, static_cast<hipStream_t>(stream), &variant);
     else
-        e = mnb::launch_gemm_mfma(L, v, a, m, y, static_cast<hipStream_t>(stream), &variant);
+        e = mnb::launch_gemm_mfma(L, v, a, m, bias, y, static_cast<hipStream_t>(stream), &variant);
     return launched(e, variant);
+}
+
+mnb_status mnb_gemm(const mnb_weight_desc* w, const void* repacked, const void* a, int64_t m,
+                    int32_t a_dtype, void* y, void* workspace, size_t workspace_bytes, void* stream)
+{
+    return gemm_common(w, repacked, a, m, a_dtype, mnb::Bias(), y, workspace, workspace_bytes, stream);
+}
+
+mnb_status mnb_gemm_bias(const mnb_weight_desc* w, const void* repacked, const void* a, int64_t m,
+                         int32_t a_dtype, const void* bias, int64_t bias_row_stride,
+                         int32_t bias_mode, void* y, void* workspace, size_t workspace_bytes,
+                         void* stream)
+{
+    if (bias_mode != MNB_BIAS_FUSED && bias_mode != MNB_BIAS_AFTER_ROUND)
+        return fail(MNB_ERR_INVALID_ARGUMENT, "bias_mode must be MNB_BIAS_FUSED or MNB_BIAS_AFTER_ROUND (got %d)",
+                    (int)bias_mode);
+    if (bias_row_stride < 0)
+        return fail(MNB_ERR_INVALID_ARGUMENT, "bias_row_stride must be >= 0 (got %lld)",
+                    (long long)bias_row_stride);
+    if (bias && m > 1 && w && bias_row_stride > (INT64_MAX / 4 - w->n) / (m - 1))
+        return fail(MNB_ERR_INVALID_ARGUMENT, "bias extent (M-1)*%lld + N overflows", (long long)bias_row_stride);
+    mnb::Bias b;
+    b.ptr = bias;
+    b.row_stride = bias_row_stride;
+    b.after_round = bias_mode == MNB_BIAS_AFTER_ROUND ? 1 : 0;
+    return gemm_common(w, repacked, a, m, a_dtype, b, y, workspace, workspace_bytes, stream);
 }
 
 mnb_status mnb_unpack_debug(const mnb_weight_desc* w, const void* repacked, uint8_t* codes,

@@ -66,6 +66,21 @@ template <typename T> __device__ __forceinline__ T from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ __half from_f32<__half>(float x) { return __float2half_rn(x); }
 
+// One output through the bias epilogue (matmul_nbits.rs, fold_bias_f16):
+// no bias: round once; a bias b: fp16(acc + b), or, after_round, fp16(fp16(acc)
+// + b); fp32 outputs add once in either mode.
+__device__ __forceinline__ __half finish_output(float acc, const __half* bias, int64_t i, int after_round)
+{
+    if (!bias) return __float2half_rn(acc);
+    const float b = __half2float(bias[i]);
+    if (after_round) acc = __half2float(__float2half_rn(acc));
+    return __float2half_rn(acc + b);
+}
+__device__ __forceinline__ float finish_output(float acc, const float* bias, int64_t i, int)
+{
+    return bias ? acc + bias[i] : acc;
+}
+
 // A wave-uniform value the compiler can keep in scalar registers.
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 

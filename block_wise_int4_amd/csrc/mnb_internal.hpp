@@ -28,18 +28,27 @@ hipError_t launch_unpack_debug(const Layout& L, const void* repacked, uint8_t* c
 
 // Largest K the decode GEMV stages in LDS, per activation dtype.
 int64_t gemv_max_k(bool f16_act);
+// Optional bias of the output, element (m, n) at ptr[m * row_stride + n], in
+// the output's dtype; after_round selects fp16(fp16(acc) + b) over
+// fp16(acc + b).
+struct Bias {
+    const void* ptr = nullptr;
+    int64_t row_stride = 0;
+    int after_round = 0;
+};
+
 // y = a . dequant(B)^T (up == nullptr) or silu(a . Bg^T) * (a . Bu^T).
 hipError_t launch_gemv(const Layout& L, const WeightView& gate, const WeightView* up,
-                       const void* a, bool f16_act, void* y, hipStream_t stream,
+                       const void* a, bool f16_act, const Bias& bias, void* y, hipStream_t stream,
                        const char** variant);
 
 // 2 <= M <= 16, fp16 activations.
 size_t gemm_small_workspace(const Layout& L, int64_t m);
 hipError_t launch_gemm_small(const Layout& L, const WeightView& w, const void* a, int64_t m,
-                             void* y, void* ws, hipStream_t stream, const char** variant);
+                             const Bias& bias, void* y, void* ws, hipStream_t stream, const char** variant);
 
 // M > 16, fp16 activations.
 hipError_t launch_gemm_mfma(const Layout& L, const WeightView& w, const void* a, int64_t m,
-                            void* y, hipStream_t stream, const char** variant);
+                            const Bias& bias, void* y, hipStream_t stream, const char** variant);
 
 }  // namespace mnb

@@ -22,9 +22,11 @@ MNB_ERR_UNSUPPORTED = 2
 MNB_ERR_DEVICE = 3
 MNB_F32 = 0
 MNB_F16 = 1
+MNB_BIAS_FUSED = 0
+MNB_BIAS_AFTER_ROUND = 1
 
 EXPORTS = ("mnb_repacked_bytes", "mnb_repacked_layout", "mnb_repack", "mnb_gemv",
-           "mnb_gemv_gate_up_swiglu", "mnb_gemm_workspace_bytes", "mnb_gemm",
+           "mnb_gemv_gate_up_swiglu", "mnb_gemm_workspace_bytes", "mnb_gemm", "mnb_gemm_bias",
            "mnb_unpack_debug", "mnb_status_string", "mnb_last_error", "mnb_last_variant")
 
 
@@ -79,6 +81,7 @@ def _load():
         "mnb_gemv_gate_up_swiglu": (ctypes.c_int, [D, P, P, P, i32, P, P]),
         "mnb_gemm_workspace_bytes": (sz, [D, i64]),
         "mnb_gemm": (ctypes.c_int, [D, P, P, i64, i32, P, P, sz, P]),
+        "mnb_gemm_bias": (ctypes.c_int, [D, P, P, i64, i32, P, i64, i32, P, P, sz, P]),
         "mnb_unpack_debug": (ctypes.c_int, [D, P, P, P, P]),
         "mnb_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "mnb_last_error": (ctypes.c_char_p, []),
@@ -191,6 +194,18 @@ def mnb_gemm(w: mnb_weight_desc, repacked: Ptr, a, m: int, y, workspace: Ptr = N
             workspace.numel() * workspace.element_size()
     _check(lib.mnb_gemm(ctypes.byref(w), _ptr(repacked), _ptr(a), m, dt, _ptr(y),
                         _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def mnb_gemm_bias(w: mnb_weight_desc, repacked: Ptr, a, m: int, bias, bias_row_stride: int,
+                  bias_mode: int, y, workspace: Ptr = None, workspace_bytes: Optional[int] = None,
+                  a_dtype: Optional[int] = None, stream=None) -> None:
+    dt = _dtype_code(a) if a_dtype is None else a_dtype
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else \
+            workspace.numel() * workspace.element_size()
+    _check(lib.mnb_gemm_bias(ctypes.byref(w), _ptr(repacked), _ptr(a), m, dt, _ptr(bias),
+                             bias_row_stride, bias_mode, _ptr(y), _ptr(workspace), workspace_bytes,
+                             _stream(stream)))
 
 
 def mnb_unpack_debug(w: mnb_weight_desc, repacked: Ptr, codes: Ptr, w_f32: Ptr, stream=None) -> None:

@@ -179,6 +179,34 @@ mnb_status mnb_gemm(const mnb_weight_desc* w, const void* repacked, const void* 
                     int32_t a_dtype, void* y, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/* Bias epilogue conventions (onnx-runtime-ep-cuda 0.1.0-dev.3,
+ * src/kernels/matmul_nbits.rs, the fp16 GEMV bias epilogue fold_bias_f16 and
+ * its dispatch records; marlin_gemm.rs (dev.6), fold_bias with a per-row
+ * bias stride). */
+typedef enum {
+    /* the operator's own bias: acc + b in fp32, rounded once, fp16(acc + b) */
+    MNB_BIAS_FUSED = 0,
+    /* a folded elementwise Add: the accumulator rounded to fp16 first, then
+     * + b in fp32 and rounded again, fp16(fp16(acc) + b); byte-identical to
+     * the GEMM's output followed by a separate fp16 add */
+    MNB_BIAS_AFTER_ROUND = 1
+} mnb_bias_mode;
+
+/* mnb_gemm followed by a bias, in one pass (any M >= 1, every path):
+ *   y[m,n] = epilogue(acc[m,n], bias[m*bias_row_stride + n]),
+ * acc the fp32 result of mnb_gemm before its output rounding.  bias (device,
+ * a_dtype, element-aligned) holds (M-1)*bias_row_stride + N elements:
+ * bias_row_stride = 0 adds one [N] vector to every row, N (or more) adds a
+ * per-row residual [M, stride].  bias_mode is an mnb_bias_mode; for fp32
+ * outputs (M = 1 with fp32 activations) both modes are acc + b in fp32.
+ * bias = NULL is mnb_gemm.  Every other argument, the workspace and the
+ * error behaviour are as for mnb_gemm; a negative stride or an unknown mode
+ * is MNB_ERR_INVALID_ARGUMENT. */
+mnb_status mnb_gemm_bias(const mnb_weight_desc* w, const void* repacked, const void* a, int64_t m,
+                         int32_t a_dtype, const void* bias, int64_t bias_row_stride,
+                         int32_t bias_mode, void* y, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
 /* Test-only: decode a repacked buffer with the production unpack code.
  * codes: device u8 [N,K] (the stored nibbles); w_f32: device f32 [N,K], the
  * dequantized weights (code - zp) * scale rounded once to fp32.  Either

@@ -138,6 +138,27 @@ def test_argument_validation():
     assert "limit" in _expect(mnb.MNB_ERR_UNSUPPORTED, lib.mnb_gemv, D(big), FAKE, FAKE, 1, FAKE, None)
 
 
+def test_bias_argument_validation():
+    lib = mnb.lib
+    d = mnb.desc(64, 256, 32, True, mnb.MNB_F16)
+    E = mnb.MNB_ERR_INVALID_ARGUMENT
+    F, AR = mnb.MNB_BIAS_FUSED, mnb.MNB_BIAS_AFTER_ROUND
+    assert "bias_mode" in _expect(E, lib.mnb_gemm_bias, D(d), FAKE, FAKE, 40, 1, FAKE, 0, 7, FAKE,
+                                  None, 0, None)
+    assert "bias_row_stride" in _expect(E, lib.mnb_gemm_bias, D(d), FAKE, FAKE, 40, 1, FAKE, -1, F,
+                                        FAKE, None, 0, None)
+    assert "overflows" in _expect(E, lib.mnb_gemm_bias, D(d), FAKE, FAKE, 3, 1, FAKE, 1 << 62, AR,
+                                  FAKE, None, 0, None)
+    # an fp16 bias must be 2-byte aligned, an fp32 one (M = 1, fp32 activations) 4-byte
+    for m in (1, 4, 40):
+        assert "bias" in _expect(E, lib.mnb_gemm_bias, D(d), FAKE, FAKE, m, 1, FAKE + 1, 0, F,
+                                 FAKE, None, 0, None)
+    assert "bias" in _expect(E, lib.mnb_gemm_bias, D(d), FAKE, FAKE, 1, 0, FAKE + 2, 0, F,
+                             FAKE, None, 0, None)
+    # M = 0 stays a no-op with a bias
+    assert lib.mnb_gemm_bias(D(d), None, None, 0, 1, FAKE, 0, AR, None, None, 0, None) == mnb.MNB_OK
+
+
 def test_empty_problems_are_noops_without_a_device():
     lib = mnb.lib
     d = mnb.desc(0, 256, 32, True, mnb.MNB_F16)

@@ -314,6 +314,66 @@ def test_prefill_mid_size_sampled_parity(mnb):
         assert t.equal(y, y2)
 
 
+BIAS_CASES = [
+    # M, N, K, g, activation dtype, zp: every path (GEMV fp16/fp32, small M, prefill)
+    (1, 300, 512, 32, "f16", True), (1, 200, 640, 64, "f32", False),
+    (4, 257, 896, 32, "f16", True), (40, 300, 512, 64, "f16", True),
+    (130, 70, 384, 128, "f16", False),
+]
+
+
+@pytest.mark.parametrize("M,N,K,g,adt,zp", BIAS_CASES)
+def test_bias_epilogue_parity(mnb, M, N, K, g, adt, zp):
+    """The bias epilogue on every path, one bias vector for all rows (stride
+    0) and a per-row residual (stride N + 5).  After-round mode must equal,
+    bit for bit, the oracle's epilogue applied to the unbiased output (the
+    two-operator path); fused mode is checked against Y + b (fp64) under the
+    accumulator's bound plus one fp32 add and one fp16 rounding; a zero bias
+    changes nothing.  fp32 outputs add once in both modes."""
+    t = G.torch()
+    w = _weight(N, K, g, "f16", zp, seed=M)
+    A = _act(M, K, adt, seed=M + 1)
+    q = G.upload(w)
+    odt = t.float16 if adt == "f16" else t.float32
+    ndt = np.float16 if adt == "f16" else np.float32
+    a = G.to_dev(A)
+    y0 = t.empty((M, N), dtype=odt, device="cuda")
+    G.gemm(q, a, M, y0)
+    y0h = y0.cpu().numpy()
+    Y, B, _ = G.oracle_dense(A, w)
+    rng = np.random.default_rng(M * 7 + N)
+    for stride in (0, N + 5):
+        rows = M if stride else 1
+        bias = np.zeros((rows, max(stride, N)), dtype=ndt)
+        bias[:, :N] = (rng.standard_normal((rows, N)) * 2.0).astype(ndt)
+        bias_dev = G.to_dev(bias.reshape(-1))
+        b_mn = np.broadcast_to(bias[:, :N], (M, N)) if stride == 0 else bias[:, :N]
+        ws, n_ws = G.workspace(q, M)
+        outs = {}
+        for mode in (mnb.MNB_BIAS_FUSED, mnb.MNB_BIAS_AFTER_ROUND):
+            y = t.empty((M, N), dtype=odt, device="cuda")
+            mnb.mnb_gemm_bias(q.desc, q.repacked, a, M, bias_dev, stride, mode, y, ws, n_ws)
+            outs[mode] = y.cpu().numpy()
+        yf, ya = outs[mnb.MNB_BIAS_FUSED], outs[mnb.MNB_BIAS_AFTER_ROUND]
+        what = "bias M=%d N=%d K=%d g=%d %s stride=%d" % (M, N, K, g, adt, stride)
+        if adt == "f16":
+            want = o.bias_epilogue_f16(y0h.astype(np.float32), b_mn, True)
+            assert (ya.view(np.uint16) == want.view(np.uint16)).all(), what + " (after-round)"
+        else:
+            assert (yf.view(np.uint32) == ya.view(np.uint32)).all(), what
+            assert (yf == (y0h + b_mn)).all(), what
+        b64 = b_mn.astype(np.float64)
+        ok = np.abs(yf.astype(np.float64) - (Y + b64)) <= o.bias_bound(Y, B, b64)
+        assert ok.all(), "%s (fused): %d of %d outside" % (what, (~ok).sum(), ok.size)
+    # a zero bias is the plain GEMM
+    zb = G.to_dev(np.zeros(N, dtype=ndt))
+    for mode in (mnb.MNB_BIAS_FUSED, mnb.MNB_BIAS_AFTER_ROUND):
+        y = t.empty((M, N), dtype=odt, device="cuda")
+        ws, n_ws = G.workspace(q, M)
+        mnb.mnb_gemm_bias(q.desc, q.repacked, a, M, zb, 0, mode, y, ws, n_ws)
+        assert (y.cpu().numpy() == y0h).all()
+
+
 # ------------------------------------------------------------ properties ----
 
 def test_results_are_deterministic(mnb):
