@@ -39,7 +39,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--only", default="",
-                   help="comma list of: gemv,gate_up,down,small_m,prefill (default all); "
+                   help="comma list of: gemv,gate_up,down,small_m,prefill,bias (default all); "
                         "copy adds a plain 256 MiB device copy, the reference kernel "
                         "for scaling the HBM byte counters")
     return p.parse_args()
@@ -86,7 +86,7 @@ class CopyWorkload:
 class Workload:
     """R rotating device copies of one workload's operands."""
 
-    def __init__(self, name, M, weights, K, N, g, act_fp16=True, sigma=1.0, seed=(0,)):
+    def __init__(self, name, M, weights, K, N, g, act_fp16=True, sigma=1.0, seed=(0,), bias=None):
         import torch
         from block_wise_int4_amd import mnb, synth
         self.name, self.M, self.K, self.N, self.g = name, M, K, N, g
@@ -102,8 +102,18 @@ class Workload:
         zp = weights[0].zero_points is not None
         sb = 2 if weights[0].scales.dtype.itemsize == 2 else 4
         self.bytes = onnx_bytes(M, K, N, g, sb, zp, 2 if act_fp16 else 4, len(weights))
+        # optional bias epilogue: ("vector" | "rows", mode); its fp16 elements
+        # count as algorithmic bytes
+        self.bias = bias
+        bias_rows = 0
+        if bias is not None:
+            bias_rows = M if bias[0] == "rows" else 1
+            self.bias_stride = N if bias[0] == "rows" else 0
+            self.bias_mode = bias[1]
+            self.bytes += bias_rows * N * 2
         self.flops = 2 * M * N * K * len(weights)
-        per_copy = sum(q.repacked.numel() for q in qs) + A.numel() * A.element_size() * 2 + M * N * 2
+        per_copy = (sum(q.repacked.numel() for q in qs) + A.numel() * A.element_size() * 2 + M * N * 2
+                    + bias_rows * N * 2)
         self.R = max(2, -(-COLD_BYTES // per_copy))
         self.desc = qs[0].desc
         self.copies = []
@@ -111,9 +121,13 @@ class Workload:
             ws = [q.repacked.clone() for q in qs]
             a = A.clone()
             y = torch.empty((M, N), dtype=A.dtype, device=dev)
-            self.copies.append((ws, a, y))
+            b = None
+            if bias_rows:
+                gen = torch.Generator().manual_seed(1000 + r)
+                b = torch.randn(bias_rows * N, generator=gen).to(A.dtype).to(dev)
+            self.copies.append((ws, a, y, b))
         self.ws_bytes = mnb.mnb_gemm_workspace_bytes(self.desc, M) if len(qs) == 1 else 0
-        self.workspaces = [torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
+        self.workspaces = [torch.zeros(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
                            for _ in range(self.R)]
         torch.cuda.synchronize()
         self.fused = len(qs) == 2
@@ -122,9 +136,12 @@ class Workload:
 
     def launch_all(self):
         from block_wise_int4_amd import mnb
-        for r, (ws, a, y) in enumerate(self.copies):
+        for r, (ws, a, y, b) in enumerate(self.copies):
             if self.fused:
                 mnb.mnb_gemv_gate_up_swiglu(self.desc, ws[0], ws[1], a, y)
+            elif b is not None:
+                mnb.mnb_gemm_bias(self.desc, ws[0], a, self.M, b, self.bias_stride, self.bias_mode, y,
+                                  self.workspaces[r], self.ws_bytes)
             else:
                 mnb.mnb_gemm(self.desc, ws[0], a, self.M, y, self.workspaces[r], self.ws_bytes)
         self.variant = mnb.mnb_last_variant()
@@ -210,7 +227,7 @@ def counted_traffic(workload, variant):
 
 def build_workloads(only):
     from block_wise_int4_amd import synth as S
-    sel = set(x for x in only.split(",") if x) or {"gemv", "gate_up", "down", "small_m", "prefill"}
+    sel = set(x for x in only.split(",") if x) or {"gemv", "gate_up", "down", "small_m", "prefill", "bias"}
     wl = [CopyWorkload()] if "copy" in sel else []
     if "gemv" in sel:
         c = S.DECODE_GEMV
@@ -232,6 +249,15 @@ def build_workloads(only):
         c = S.PREFILL_GEMM
         wl.append(Workload(c.name, c.M, [S.workload_weights(c)], c.K, c.N, c.group, sigma=c.sigma,
                            seed=c.seed + (c.M,)))
+    if "bias" in sel:
+        from block_wise_int4_amd import mnb
+        c = S.DECODE_GEMV
+        wl.append(Workload(c.name + " + bias [N] fp16(acc+b)", 1, [S.workload_weights(c)], c.K, c.N,
+                           c.group, seed=c.seed + (1,), bias=("vector", mnb.MNB_BIAS_FUSED)))
+        c = S.PREFILL_GEMM
+        wl.append(Workload(c.name + " + bias [N] fp16(fp16(acc)+b)", c.M, [S.workload_weights(c)],
+                           c.K, c.N, c.group, sigma=c.sigma, seed=c.seed + (c.M,),
+                           bias=("vector", mnb.MNB_BIAS_AFTER_ROUND)))
     return wl
 
 

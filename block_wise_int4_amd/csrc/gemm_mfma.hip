@@ -512,6 +512,62 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
 
     // ---- epilogue: lane holds column (lane & 31) of each 32x32 block, rows
     // 8*(e/4) + 4*oct + e%4
+    if (p.bias && p.bias_stride == 0) {
+        // one bias vector for every row: the lane's two columns only
+        float bq[PAIRS];
+#pragma unroll
+        for (int q = 0; q < PAIRS; ++q) {
+            const int n = nb * BN + wave * 64 + q * 32 + (lane & 31);
+            bq[q] = __half2float(p.bias[n < p.N ? n : p.N - 1]);
+        }
+#pragma unroll
+        for (int q = 0; q < PAIRS; ++q) {
+            const int n = nb * BN + wave * 64 + q * 32 + (lane & 31);
+            if (n >= p.N) continue;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int m = m0 + rb * 32 + 8 * (e >> 2) + 4 * oct + (e & 3);
+                    if (m < p.M) p.y[(int64_t)m * p.N + n] = finish_value(acc[rb][q][e], bq[q], p.bias_after_round);
+                }
+        }
+        return;
+    }
+    if (p.bias) {
+        // a per-row bias: all of the lane's bias elements are loaded before
+        // any is used (rows and columns outside the output read an element
+        // inside it)
+        __half bv[PAIRS][RB][16];
+#pragma unroll
+        for (int q = 0; q < PAIRS; ++q) {
+            int n = nb * BN + wave * 64 + q * 32 + (lane & 31);
+            n = n < p.N ? n : p.N - 1;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    int m = m0 + rb * 32 + 8 * (e >> 2) + 4 * oct + (e & 3);
+                    m = m < p.M ? m : p.M - 1;
+                    bv[q][rb][e] = p.bias[(int64_t)m * p.bias_stride + n];
+                }
+        }
+#pragma unroll
+        for (int q = 0; q < PAIRS; ++q) {
+            const int n = nb * BN + wave * 64 + q * 32 + (lane & 31);
+            if (n >= p.N) continue;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int m = m0 + rb * 32 + 8 * (e >> 2) + 4 * oct + (e & 3);
+                    if (m < p.M)
+                        p.y[(int64_t)m * p.N + n] = finish_value(acc[rb][q][e], __half2float(bv[q][rb][e]),
+                                                                 p.bias_after_round);
+                }
+        }
+        return;
+    }
 #pragma unroll
     for (int q = 0; q < PAIRS; ++q) {
         const int n = nb * BN + wave * 64 + q * 32 + (lane & 31);
@@ -521,9 +577,7 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int m = m0 + rb * 32 + 8 * (e >> 2) + 4 * oct + (e & 3);
-                if (m < p.M)
-                    p.y[(int64_t)m * p.N + n] = finish_output(acc[rb][q][e], p.bias, (int64_t)m * p.bias_stride + n,
-                                                              p.bias_after_round);
+                if (m < p.M) p.y[(int64_t)m * p.N + n] = __float2half_rn(acc[rb][q][e]);
             }
         }
     }

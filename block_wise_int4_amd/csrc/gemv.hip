@@ -341,6 +341,12 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
     float* red = reinterpret_cast<float*>(smem + kpad * sizeof(AT));
 #pragma unroll
     for (int x = 0; x < NW; ++x) red[(x * kMaxWaves + wave) * 16 + (lane & 15)] = acc[x];
+    // the store's bias, requested before the barrier so that its latency
+    // overlaps the wait for the other waves and their reduction
+    float bias_f = 0.0f;
+    const int64_t n_out = t * kTileN + lane;
+    if (!FUSED && p.bias && wave == 0 && lane < 16 && n_out < p.N)
+        bias_f = (float)static_cast<const AT*>(p.bias)[n_out];
     __syncthreads();
     if (wave == 0 && lane < 16) {
         float r[NW];
@@ -353,7 +359,12 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
         if (n < p.N) {
             float out = r[0];
             if (FUSED) out = silu_f32(r[0]) * r[NW - 1];
-            static_cast<AT*>(p.y)[n] = finish_output(out, static_cast<const AT*>(p.bias), n, p.bias_after_round);
+            AT v;
+            if constexpr (F16)
+                v = (!FUSED && p.bias) ? finish_value(out, bias_f, p.bias_after_round) : __float2half_rn(out);
+            else
+                v = (!FUSED && p.bias) ? out + bias_f : out;
+            static_cast<AT*>(p.y)[n] = v;
         }
     }
 }

@@ -69,12 +69,15 @@ template <> __device__ __forceinline__ __half from_f32<__half>(float x) { return
 // One output through the bias epilogue (matmul_nbits.rs, fold_bias_f16):
 // no bias: round once; a bias b: fp16(acc + b), or, after_round, fp16(fp16(acc)
 // + b); fp32 outputs add once in either mode.
+__device__ __forceinline__ __half finish_value(float acc, float b, int after_round)
+{
+    if (after_round) acc = __half2float(__float2half_rn(acc));
+    return __float2half_rn(acc + b);
+}
 __device__ __forceinline__ __half finish_output(float acc, const __half* bias, int64_t i, int after_round)
 {
     if (!bias) return __float2half_rn(acc);
-    const float b = __half2float(bias[i]);
-    if (after_round) acc = __half2float(__float2half_rn(acc));
-    return __float2half_rn(acc + b);
+    return finish_value(acc, __half2float(bias[i]), after_round);
 }
 __device__ __forceinline__ float finish_output(float acc, const float* bias, int64_t i, int)
 {
