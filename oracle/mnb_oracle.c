@@ -24,6 +24,13 @@
  *  [SILU] ferrox-cuda gpu.rs -- kernel silu_mul_f32: silu(g) * u with
  *         silu(x) = x / (1 + e^-x); matmul_nbits.rs (dev.3) --
  *         gate_up_silu_f32 states the same function in a two-branch form.
+ *  [GIDX] onnx-runtime-ep-cuda 0.1.0-dev.3, src/kernels/matmul_nbits.rs --
+ *         kernel matmul_nbits_dequant_f32 with group_indices, and the
+ *         g_idx checks of MatMulNBitsFactory (optional input 4, int32 [K],
+ *         every value in 0..k_blocks-1): the code of (n,k) stays where the
+ *         format puts it, the scale and zero point are those of group
+ *         g_idx[k] instead of k/group; a group outside the range dequantizes
+ *         to 0.
  *  [BIAS] onnx-runtime-ep-cuda 0.1.0-dev.3, src/kernels/matmul_nbits.rs --
  *         the fp16 GEMV bias epilogue (fold_bias_f16) and the bias stage
  *         records of the GEMV dispatch; marlin_gemm.rs (dev.6) -- the same
@@ -330,4 +337,26 @@ void oracle_bias_f16_array(const float* acc, const uint16_t* b, int64_t count, i
                            uint16_t* out)
 {
     for (int64_t i = 0; i < count; ++i) out[i] = oracle_bias_f16(acc[i], b[i], after_round);
+}
+
+/* ---- act-order group indices [GIDX] -------------------------------------- */
+
+/* dequant(B)[n,k] = (code[n,k] - zp[n,g_idx[k]]) * scale[n,g_idx[k]] in fp64,
+ * and 0 for a group index outside 0..k_blocks-1. */
+void oracle_dequant_gidx(const uint8_t* packed, const double* scales, const uint8_t* zero_points,
+                         const int32_t* g_idx, int64_t N, int64_t K, int64_t g, double* w)
+{
+    const int64_t kb = k_blocks_of(K, g);
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            const int64_t grp = g_idx[k];
+            if (grp < 0 || grp >= kb) {
+                w[n * K + k] = 0.0;
+                continue;
+            }
+            const int code = oracle_code(packed, n, k, K, g);
+            const int zp = oracle_zero_point(zero_points, n, grp, kb);
+            w[n * K + k] = ((double)code - (double)zp) * scales[n * kb + grp];
+        }
+    }
 }

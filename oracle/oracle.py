@@ -71,6 +71,7 @@ def _load():
     lib.oracle_pack_codes.argtypes = [p, i64, i64, i64, p]
     lib.oracle_pack_zero_points.argtypes = [p, i64, i64, p]
     lib.oracle_max_threads.restype = ctypes.c_int
+    lib.oracle_dequant_gidx.argtypes = [p, p, p, p, i64, i64, i64, p]
     lib.oracle_round_f16.argtypes = [ctypes.c_double]
     lib.oracle_round_f16.restype = ctypes.c_uint16
     lib.oracle_round_f16_array.argtypes = [p, i64, p]
@@ -147,6 +148,23 @@ def dequant(packed: np.ndarray, scales: np.ndarray, zp: Optional[np.ndarray],
         assert zp.size == N * ((kb + 1) // 2)
     w = np.empty((N, K), dtype=np.float64)
     _load().oracle_dequant(_ptr(packed), _ptr(s64), _ptr(zp), N, K, g, _ptr(w))
+    return w
+
+
+def dequant_gidx(packed: np.ndarray, scales: np.ndarray, zp: Optional[np.ndarray],
+                 g_idx: np.ndarray, N: int, K: int, g: int) -> np.ndarray:
+    """fp64 dense W[N,K] = (code - zp[g_idx[k]]) * scale[g_idx[k]] (act order)."""
+    kb = k_blocks(K, g)
+    packed = np.ascontiguousarray(packed, np.uint8)
+    s64 = decode(scales).reshape(-1)
+    assert s64.size == N * kb and packed.size == N * kb * (g // 2)
+    if zp is not None:
+        zp = np.ascontiguousarray(zp, np.uint8)
+        assert zp.size == N * ((kb + 1) // 2)
+    gi = np.ascontiguousarray(g_idx, np.int32)
+    assert gi.size == K
+    w = np.empty((N, K), dtype=np.float64)
+    _load().oracle_dequant_gidx(_ptr(packed), _ptr(s64), _ptr(zp), _ptr(gi), N, K, g, _ptr(w))
     return w
 
 

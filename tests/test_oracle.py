@@ -285,10 +285,44 @@ def pin_bias_epilogue():
     assert (fused != after).any()
 
 
+def pin_group_indices():
+    """act order: g_idx[k] = k // g is the plain dequant; by hand, N = 1,
+    K = 4, g = 2, codes 3,5,7,9, zero points 1 (group 0) and 4 (group 1),
+    scales 0.5 and 2, g_idx = [1,0,0,1]: (3-4)*2, (5-1)*0.5, (7-1)*0.5, (9-4)*2
+    = -2, 2, 3, 10; with g_idx = [1,-1,2,0] a group index outside 0..1 gives 0
+    and the last code uses group 0: -2, 0, 0, (9-1)*0.5 = 4; exact rationals on
+    random act orders with groups of every size."""
+    rng = np.random.default_rng(21)
+    N, K, g = 5, 64, 16
+    kb = K // g
+    packed = rng.integers(0, 256, (N, kb, g // 2), dtype=np.uint8)
+    zp = rng.integers(0, 256, (N, (kb + 1) // 2), dtype=np.uint8)
+    scales = rng.uniform(0.01, 0.02, (N, kb)).astype(np.float16)
+    plain = o.dequant(packed, scales, zp, N, K, g)
+    assert (o.dequant_gidx(packed, scales, zp, np.arange(K) // g, N, K, g) == plain).all()
+    p1 = o.pack_codes(np.array([[3, 5, 7, 9]], np.uint8), 2)
+    z1 = o.pack_zero_points(np.array([[1, 4]], np.uint8))
+    s1 = np.array([[0.5, 2.0]], np.float32)
+    W = o.dequant_gidx(p1, s1, z1, np.array([1, 0, 0, 1]), 1, 4, 2)
+    assert W.tolist() == [[-2.0, 2.0, 3.0, 10.0]]
+    W = o.dequant_gidx(p1, s1, z1, np.array([1, -1, 2, 0]), 1, 4, 2)
+    assert W.tolist() == [[-2.0, 0.0, 0.0, 4.0]]
+    for with_zp in (True, False):
+        codes = rng.integers(0, 16, (N, K), dtype=np.uint8)
+        z = rng.integers(0, 16, (N, kb), dtype=np.uint8) if with_zp else np.full((N, kb), 8, np.uint8)
+        gi = rng.integers(0, kb, K)
+        W = o.dequant_gidx(o.pack_codes(codes, g), scales, o.pack_zero_points(z) if with_zp else None,
+                           gi, N, K, g)
+        for n in range(N):
+            for k in range(K):
+                exact = (int(codes[n, k]) - int(z[n, gi[k]])) * Fraction(float(scales[n, gi[k]]))
+                assert Fraction(W[n, k]) == exact
+
+
 PINS = [pin_worked_examples, pin_exhaustive_nibbles, pin_pack_unpack_identity,
         pin_code_equals_zero_point_gives_zero, pin_bruteforce_exact,
         pin_integer_special_case, pin_linear_and_one_hot, pin_fp16_decode_all_patterns,
-        pin_swiglu, pin_round_f16_against_numpy, pin_bias_epilogue]
+        pin_swiglu, pin_round_f16_against_numpy, pin_bias_epilogue, pin_group_indices]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -350,6 +384,9 @@ MUTANTS = {
     "binary16 subnormal spacing": ("if (ulp < -24) ulp = -24;", "if (ulp < -25) ulp = -25;"),
     "bias added before rounding in both modes": ("if (after_round) base =", "if (0) base ="),
     "bias rounded before the add in both modes": ("if (after_round) base =", "if (1) base ="),
+    "act-order scale by block": ("* scales[n * kb + grp];", "* scales[n * kb + k / g];"),
+    "act-order zero point by block": ("oracle_zero_point(zero_points, n, grp, kb);",
+                                      "oracle_zero_point(zero_points, n, k / g, kb);"),
 }
 
 
