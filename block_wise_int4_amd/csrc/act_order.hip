@@ -1,0 +1,51 @@
+// act_order.hip -- the activation side of act-order weights.
+//
+// Method: onnx-runtime-ep-cuda 0.1.0-dev.3, src/kernels/matmul_nbits.rs --
+// the optional group-index input g_idx (int32 [K], every value a group of
+// the weight) and the dequant kernel that looks up the scale and zero point
+// of group g_idx[k] for the code at k.  Here the repack sorts k by group
+// (mnb_repack_act_order), so the weight looks like an ordinary one with
+// contiguous groups; the product is unchanged when A's columns take the
+// same order, Y = A[:, perm] . dequant(B)[:, perm]^T, which this kernel
+// provides before the ordinary GEMV or GEMM runs.
+#include "mnb_device.hpp"
+#include "mnb_internal.hpp"
+
+namespace mnb {
+
+namespace {
+
+// One thread per output element; consecutive threads write consecutive
+// columns of a row (the reads are a gather within the row).
+template <typename T>
+__global__ __launch_bounds__(256) void permute_columns_kernel(const T* __restrict__ a,
+                                                              const int32_t* __restrict__ perm,
+                                                              T* __restrict__ out, int64_t M,
+                                                              int64_t K)
+{
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= M * K) return;
+    const int64_t m = idx / K;
+    const int64_t k = idx - m * K;
+    int64_t src = perm[k];
+    if (src < 0 || src >= K) src = 0;
+    out[idx] = a[m * K + src];
+}
+
+}  // namespace
+
+hipError_t launch_permute_columns(const void* a, const int32_t* perm, int64_t M, int64_t K,
+                                  int elem_bytes, void* out, hipStream_t stream)
+{
+    const int64_t total = M * K;
+    const unsigned blocks = (unsigned)((total + 255) / 256);
+    if (elem_bytes == 2)
+        permute_columns_kernel<uint16_t><<<blocks, 256, 0, stream>>>(
+            static_cast<const uint16_t*>(a), perm, static_cast<uint16_t*>(out), M, K);
+    else
+        permute_columns_kernel<uint32_t><<<blocks, 256, 0, stream>>>(
+            static_cast<const uint32_t*>(a), perm, static_cast<uint32_t*>(out), M, K);
+    return hipGetLastError();
+}
+
+}  // namespace mnb

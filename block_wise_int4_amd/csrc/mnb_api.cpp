@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/mnb.h"
 #include "mnb_internal.hpp"
@@ -156,8 +157,9 @@ mnb_status mnb_repacked_layout(const mnb_weight_desc* w, mnb_layout* out)
     return MNB_OK;
 }
 
-mnb_status mnb_repack(const mnb_weight_desc* w, const uint8_t* packed, const void* scales,
-                      const uint8_t* zero_points, void* repacked, void* stream)
+static mnb_status repack_common(const mnb_weight_desc* w, const uint8_t* packed, const void* scales,
+                                const uint8_t* zero_points, const int32_t* perm, void* repacked,
+                                void* stream)
 {
     Layout L;
     MNB_TRY(check_desc(w, &L));
@@ -171,9 +173,49 @@ mnb_status mnb_repack(const mnb_weight_desc* w, const uint8_t* packed, const voi
         return fail(MNB_ERR_INVALID_ARGUMENT, "zero_points given but has_zero_points is 0");
     }
     MNB_TRY(check_device());
-    return launched(mnb::launch_repack(L, packed, scales, zero_points, repacked,
+    if (perm) MNB_TRY(check_ptr(perm, 4, "perm"));
+    return launched(mnb::launch_repack(L, packed, scales, zero_points, perm, repacked,
                                        static_cast<hipStream_t>(stream)),
                     "repack");
+}
+
+mnb_status mnb_repack(const mnb_weight_desc* w, const uint8_t* packed, const void* scales,
+                      const uint8_t* zero_points, void* repacked, void* stream)
+{
+    return repack_common(w, packed, scales, zero_points, nullptr, repacked, stream);
+}
+
+mnb_status mnb_act_order_permutation(const mnb_weight_desc* w, const int32_t* g_idx, int32_t* perm)
+{
+    Layout L;
+    MNB_TRY(check_desc(w, &L));
+    if (L.K == 0) return ok("act_order_permutation");
+    if (!g_idx) return fail(MNB_ERR_INVALID_ARGUMENT, "g_idx is NULL");
+    if (!perm) return fail(MNB_ERR_INVALID_ARGUMENT, "perm is NULL");
+    std::vector<int64_t> next(L.kb, 0);
+    for (int64_t k = 0; k < L.K; ++k) {
+        const int32_t grp = g_idx[k];
+        if (grp < 0 || grp >= L.kb)
+            return fail(MNB_ERR_INVALID_ARGUMENT, "g_idx[%lld]=%d is outside 0..%lld", (long long)k, (int)grp,
+                        (long long)(L.kb - 1));
+        ++next[grp];
+    }
+    for (int64_t b = 0; b < L.kb; ++b)
+        if (next[b] != L.g)
+            return fail(MNB_ERR_UNSUPPORTED, "group %lld has %lld members; the repacked layout needs %d per group",
+                        (long long)b, (long long)next[b], (int)L.g);
+    // stable: the members of each group in increasing k
+    for (int64_t b = 0; b < L.kb; ++b) next[b] = b * L.g;
+    for (int64_t k = 0; k < L.K; ++k) perm[next[g_idx[k]]++] = (int32_t)k;
+    return ok("act_order_permutation");
+}
+
+mnb_status mnb_repack_act_order(const mnb_weight_desc* w, const uint8_t* packed, const void* scales,
+                                const uint8_t* zero_points, const int32_t* perm, void* repacked,
+                                void* stream)
+{
+    if (!perm) return fail(MNB_ERR_INVALID_ARGUMENT, "perm is NULL");
+    return repack_common(w, packed, scales, zero_points, perm, repacked, stream);
 }
 
 static mnb_status gemv_common(const mnb_weight_desc* w, const void* gate, const void* up,
@@ -292,6 +334,55 @@ mnb_status mnb_gemm_bias(const mnb_weight_desc* w, const void* repacked, const v
     b.row_stride = bias_row_stride;
     b.after_round = bias_mode == MNB_BIAS_AFTER_ROUND ? 1 : 0;
     return gemm_common(w, repacked, a, m, a_dtype, b, y, workspace, workspace_bytes, stream);
+}
+
+static size_t act_order_a_bytes(const Layout& L, int64_t m, int32_t a_dtype)
+{
+    const int64_t elem = a_dtype == MNB_F32 ? 4 : 2;
+    return (size_t)(((m * L.K * elem) + 255) / 256 * 256);
+}
+
+size_t mnb_gemm_act_order_workspace_bytes(const mnb_weight_desc* w, int64_t m, int32_t a_dtype)
+{
+    Layout L;
+    if (check_desc(w, &L) != MNB_OK) return 0;
+    if (m < 0 || check_act_dtype(a_dtype) != MNB_OK) return 0;
+    if (L.K > 0 && m > INT64_MAX / 4 / L.K) {
+        fail(MNB_ERR_INVALID_ARGUMENT, "M*K overflows");
+        return 0;
+    }
+    g_error.clear();
+    return act_order_a_bytes(L, m, a_dtype) + workspace_for(L, m);
+}
+
+mnb_status mnb_gemm_act_order(const mnb_weight_desc* w, const void* repacked, const void* a, int64_t m,
+                              int32_t a_dtype, const int32_t* perm, void* y, void* workspace,
+                              size_t workspace_bytes, void* stream)
+{
+    Layout L;
+    MNB_TRY(check_desc(w, &L));
+    MNB_TRY(check_act_dtype(a_dtype));
+    if (m < 0) return fail(MNB_ERR_INVALID_ARGUMENT, "M must be >= 0 (got %lld)", (long long)m);
+    if (m == 0 || L.N == 0) return ok("noop");
+    if (L.K > 0 && m > INT64_MAX / 4 / L.K) return fail(MNB_ERR_INVALID_ARGUMENT, "M*K overflows");
+    if (m > 1 && a_dtype != MNB_F16)
+        return fail(MNB_ERR_UNSUPPORTED, "M>1 GEMM takes fp16 activations only");
+    const size_t a_bytes = act_order_a_bytes(L, m, a_dtype);
+    const size_t need = a_bytes + workspace_for(L, m);
+    if (workspace_bytes < need)
+        return fail(MNB_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed",
+                    workspace_bytes, need);
+    MNB_TRY(check_ptr(workspace, 256, "workspace"));
+    if (!perm) return fail(MNB_ERR_INVALID_ARGUMENT, "perm is NULL");
+    MNB_TRY(check_ptr(perm, 4, "perm"));
+    MNB_TRY(check_ptr(a, 16, "a"));
+    MNB_TRY(check_device());
+    // A's columns in the repacked order, then the ordinary call on them
+    const hipError_t e = mnb::launch_permute_columns(a, perm, m, L.K, a_dtype == MNB_F32 ? 4 : 2, workspace,
+                                                     static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return launched(e, "act_order_permute");
+    return gemm_common(w, repacked, workspace, m, a_dtype, mnb::Bias(), y,
+                       static_cast<unsigned char*>(workspace) + a_bytes, workspace_bytes - a_bytes, stream);
 }
 
 mnb_status mnb_unpack_debug(const mnb_weight_desc* w, const void* repacked, uint8_t* codes,

@@ -21,8 +21,14 @@ inline WeightView view_of(const Layout& L, const void* repacked)
     return WeightView{b + L.codes_off, b + L.scales_off, L.has_zp ? b + L.zp_off : nullptr};
 }
 
+// perm: NULL, or the act-order permutation of k (the codes of ONNX position
+// perm[k] go to position k; scales and zero points keep their groups).
 hipError_t launch_repack(const Layout& L, const uint8_t* packed, const void* scales,
-                         const uint8_t* zp, void* repacked, hipStream_t stream);
+                         const uint8_t* zp, const int32_t* perm, void* repacked, hipStream_t stream);
+// out[m, k] = a[m, perm[k]] for an [M, K] matrix of elem_bytes (2 or 4)
+// elements; an index outside 0..K-1 reads column 0.
+hipError_t launch_permute_columns(const void* a, const int32_t* perm, int64_t M, int64_t K,
+                                  int elem_bytes, void* out, hipStream_t stream);
 hipError_t launch_unpack_debug(const Layout& L, const void* repacked, uint8_t* codes, float* w,
                                hipStream_t stream);
 

@@ -48,6 +48,44 @@ __global__ __launch_bounds__(256) void repack_codes_kernel(const uint8_t* __rest
     out[idx] = v;
 }
 
+// The same words for an act-order weight: position k of the repacked order
+// holds the code of ONNX position perm[k] (perm sorts k by group, so every
+// group of the repacked order is contiguous).  An index outside 0..K-1 reads
+// position 0: a wrong permutation gives wrong codes, never a wild read.
+__global__ __launch_bounds__(256) void repack_codes_perm_kernel(const uint8_t* __restrict__ packed,
+                                                                const int32_t* __restrict__ perm,
+                                                                uint32_t* __restrict__ out, int64_t N,
+                                                                int64_t K, int g, int64_t C,
+                                                                int64_t words)
+{
+    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= words) return;
+    const int64_t chunk = idx >> 8;
+    const int within = (int)(idx & 255);
+    const int lane = within >> 2;
+    const int j = within & 3;
+    const int64_t t = chunk / C;
+    const int64_t c = chunk - t * C;
+    const int64_t n = t * kTileN + (lane & 15);
+    const int64_t k0 = c * kChunkK + 32 * j + 8 * (lane >> 4);
+    uint32_t v = 0;
+    if (n < N) {
+        const int64_t kb = K / g;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (k0 + i >= K) break;
+            int64_t ks = perm[k0 + i];
+            if (ks < 0 || ks >= K) ks = 0;
+            const uint32_t byte = packed[(n * kb + ks / g) * (g / 2) + (ks % g) / 2];
+            const uint32_t nib = (ks & 1) ? (byte >> 4) : (byte & 15u);
+            // even offsets to nibble slots 0..3, odd ones to 4..7
+            const int slot = (i & 1) ? 4 + (i >> 1) : (i >> 1);
+            v |= nib << (4 * slot);
+        }
+    }
+    out[idx] = v;
+}
+
 // (column i, in-chunk group q) of a slot; inverse of slot_of().
 __device__ __forceinline__ void slot_inverse(int s, int Q, int& i, int& q)
 {
@@ -170,12 +208,17 @@ void zero_gap(uint8_t* base, int64_t from, int64_t to, hipStream_t stream)
 }  // namespace
 
 hipError_t launch_repack(const Layout& L, const uint8_t* packed, const void* scales,
-                         const uint8_t* zp, void* repacked, hipStream_t stream)
+                         const uint8_t* zp, const int32_t* perm, void* repacked, hipStream_t stream)
 {
     uint8_t* base = static_cast<uint8_t*>(repacked);
     const int64_t words = L.codes_bytes / 4;
-    repack_codes_kernel<<<blocks_for(words), 256, 0, stream>>>(
-        packed, reinterpret_cast<uint32_t*>(base + L.codes_off), L.N, L.K, L.g, L.C, words);
+    if (perm) {
+        repack_codes_perm_kernel<<<blocks_for(words), 256, 0, stream>>>(
+            packed, perm, reinterpret_cast<uint32_t*>(base + L.codes_off), L.N, L.K, L.g, L.C, words);
+    } else {
+        repack_codes_kernel<<<blocks_for(words), 256, 0, stream>>>(
+            packed, reinterpret_cast<uint32_t*>(base + L.codes_off), L.N, L.K, L.g, L.C, words);
+    }
     const int64_t ns = L.T * L.C * kTileN * L.Q;
     if (L.ss == 2) {
         repack_scales_kernel<uint16_t><<<blocks_for(ns), 256, 0, stream>>>(

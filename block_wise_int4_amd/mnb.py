@@ -27,6 +27,8 @@ MNB_BIAS_AFTER_ROUND = 1
 
 EXPORTS = ("mnb_repacked_bytes", "mnb_repacked_layout", "mnb_repack", "mnb_gemv",
            "mnb_gemv_gate_up_swiglu", "mnb_gemm_workspace_bytes", "mnb_gemm", "mnb_gemm_bias",
+           "mnb_act_order_permutation", "mnb_repack_act_order", "mnb_gemm_act_order_workspace_bytes",
+           "mnb_gemm_act_order",
            "mnb_unpack_debug", "mnb_status_string", "mnb_last_error", "mnb_last_variant")
 
 
@@ -82,6 +84,10 @@ def _load():
         "mnb_gemm_workspace_bytes": (sz, [D, i64]),
         "mnb_gemm": (ctypes.c_int, [D, P, P, i64, i32, P, P, sz, P]),
         "mnb_gemm_bias": (ctypes.c_int, [D, P, P, i64, i32, P, i64, i32, P, P, sz, P]),
+        "mnb_act_order_permutation": (ctypes.c_int, [D, P, P]),
+        "mnb_repack_act_order": (ctypes.c_int, [D, P, P, P, P, P, P]),
+        "mnb_gemm_act_order_workspace_bytes": (sz, [D, i64, i32]),
+        "mnb_gemm_act_order": (ctypes.c_int, [D, P, P, i64, i32, P, P, P, sz, P]),
         "mnb_unpack_debug": (ctypes.c_int, [D, P, P, P, P]),
         "mnb_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "mnb_last_error": (ctypes.c_char_p, []),
@@ -206,6 +212,37 @@ def mnb_gemm_bias(w: mnb_weight_desc, repacked: Ptr, a, m: int, bias, bias_row_s
     _check(lib.mnb_gemm_bias(ctypes.byref(w), _ptr(repacked), _ptr(a), m, dt, _ptr(bias),
                              bias_row_stride, bias_mode, _ptr(y), _ptr(workspace), workspace_bytes,
                              _stream(stream)))
+
+
+def mnb_act_order_permutation(w: mnb_weight_desc, g_idx):
+    """Host: the act-order permutation of k for a g_idx (numpy int32 [K])."""
+    import numpy as np
+    g = np.ascontiguousarray(g_idx, np.int32)
+    perm = np.empty(g.size, dtype=np.int32)
+    _check(lib.mnb_act_order_permutation(ctypes.byref(w), g.ctypes.data_as(ctypes.c_void_p),
+                                         perm.ctypes.data_as(ctypes.c_void_p)))
+    return perm
+
+
+def mnb_repack_act_order(w: mnb_weight_desc, packed: Ptr, scales: Ptr, zero_points: Ptr, perm: Ptr,
+                         repacked: Ptr, stream=None) -> None:
+    _check(lib.mnb_repack_act_order(ctypes.byref(w), _ptr(packed), _ptr(scales), _ptr(zero_points),
+                                    _ptr(perm), _ptr(repacked), _stream(stream)))
+
+
+def mnb_gemm_act_order_workspace_bytes(w: mnb_weight_desc, m: int, a_dtype: int = MNB_F16) -> int:
+    return int(lib.mnb_gemm_act_order_workspace_bytes(ctypes.byref(w), m, a_dtype))
+
+
+def mnb_gemm_act_order(w: mnb_weight_desc, repacked: Ptr, a, m: int, perm: Ptr, y, workspace: Ptr,
+                       workspace_bytes: Optional[int] = None, a_dtype: Optional[int] = None,
+                       stream=None) -> None:
+    dt = _dtype_code(a) if a_dtype is None else a_dtype
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else \
+            workspace.numel() * workspace.element_size()
+    _check(lib.mnb_gemm_act_order(ctypes.byref(w), _ptr(repacked), _ptr(a), m, dt, _ptr(perm), _ptr(y),
+                                  _ptr(workspace), workspace_bytes, _stream(stream)))
 
 
 def mnb_unpack_debug(w: mnb_weight_desc, repacked: Ptr, codes: Ptr, w_f32: Ptr, stream=None) -> None:

@@ -207,6 +207,43 @@ mnb_status mnb_gemm_bias(const mnb_weight_desc* w, const void* repacked, const v
                          int32_t bias_mode, void* y, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/* Act-order weights: the optional group-index input g_idx of MatMulNBits
+ * (onnx-runtime-ep-cuda 0.1.0-dev.3, src/kernels/matmul_nbits.rs, the
+ * g_idx checks of MatMulNBitsFactory and the dequant kernel with
+ * group_indices): int32 [K], the code at k keeps its place in the ONNX
+ * layout and takes the scale and zero point of group g_idx[k]:
+ *   dequant(B)[n,k] = (code[n,k] - zp[n, g_idx[k]]) * scale[n, g_idx[k]].
+ * The repack sorts k by group, so every group becomes contiguous, and the
+ * GEMM takes A's columns in the same order; the product is the same sum over
+ * k in another order.  Three steps:
+ *
+ * 1. mnb_act_order_permutation (host only, host pointers, no HIP call):
+ *    checks g_idx (every value in 0..k_blocks-1, else
+ *    MNB_ERR_INVALID_ARGUMENT; every group with exactly group_size members,
+ *    else MNB_ERR_UNSUPPORTED) and writes perm [K]: the positions of group 0
+ *    in increasing k, then those of group 1, and so on. */
+mnb_status mnb_act_order_permutation(const mnb_weight_desc* w, const int32_t* g_idx, int32_t* perm);
+
+/* 2. mnb_repack_act_order: mnb_repack of the same ONNX operands with the
+ *    codes taken in perm order (perm: device int32 [K], from step 1; a
+ *    buffer repacked this way serves only mnb_gemm_act_order with the same
+ *    perm).  Arguments and errors as mnb_repack.  Indices outside 0..K-1 in
+ *    perm give wrong codes, never an out-of-range read. */
+mnb_status mnb_repack_act_order(const mnb_weight_desc* w, const uint8_t* packed, const void* scales,
+                                const uint8_t* zero_points, const int32_t* perm, void* repacked,
+                                void* stream);
+
+/* 3. mnb_gemm_act_order: mnb_gemm on an act-order repacked buffer, any
+ *    M >= 1.  perm: device int32 [K], the one used by the repack.  The
+ *    workspace (device, 256-byte aligned) holds A with its columns in perm
+ *    order, then mnb_gemm's own workspace:
+ *    mnb_gemm_act_order_workspace_bytes(w, m, a_dtype) bytes.  Other
+ *    arguments, dtypes and errors as mnb_gemm. */
+size_t mnb_gemm_act_order_workspace_bytes(const mnb_weight_desc* w, int64_t m, int32_t a_dtype);
+mnb_status mnb_gemm_act_order(const mnb_weight_desc* w, const void* repacked, const void* a, int64_t m,
+                              int32_t a_dtype, const int32_t* perm, void* y, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* Test-only: decode a repacked buffer with the production unpack code.
  * codes: device u8 [N,K] (the stored nibbles); w_f32: device f32 [N,K], the
  * dequantized weights (code - zp) * scale rounded once to fp32.  Either

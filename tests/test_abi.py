@@ -159,6 +159,59 @@ def test_bias_argument_validation():
     assert lib.mnb_gemm_bias(D(d), None, None, 0, 1, FAKE, 0, AR, None, None, 0, None) == mnb.MNB_OK
 
 
+def _act_order_g_idx(K, g, seed):
+    """A random act order: every group gets exactly g positions."""
+    rng = np.random.default_rng(seed)
+    g_idx = np.empty(K, np.int32)
+    g_idx[rng.permutation(K)] = np.arange(K) // g
+    return g_idx
+
+
+def test_act_order_permutation():
+    for (K, g, seed) in ((512, 32, 1), (384, 128, 2), (64, 16, 3)):
+        d = mnb.desc(40, K, g, True, mnb.MNB_F16)
+        g_idx = _act_order_g_idx(K, g, seed)
+        perm = mnb.mnb_act_order_permutation(d, g_idx)
+        # the stable order of k by group (numpy's stable sort) ...
+        assert (perm == np.argsort(g_idx, kind="stable")).all()
+        # ... so position j of the new order belongs to group j // g
+        assert (g_idx[perm] == np.arange(K) // g).all()
+        ident = mnb.mnb_act_order_permutation(d, np.arange(K, dtype=np.int32) // g)
+        assert (ident == np.arange(K)).all()
+    d = mnb.desc(40, 64, 16, False, mnb.MNB_F16)
+    bad = np.arange(64, dtype=np.int32) // 16
+    bad[5] = 4
+    with pytest.raises(mnb.MnbError) as e:
+        mnb.mnb_act_order_permutation(d, bad)
+    assert e.value.status == mnb.MNB_ERR_INVALID_ARGUMENT and "outside" in str(e.value)
+    bad[5] = -1
+    with pytest.raises(mnb.MnbError) as e:
+        mnb.mnb_act_order_permutation(d, bad)
+    assert e.value.status == mnb.MNB_ERR_INVALID_ARGUMENT
+    uneven = np.arange(64, dtype=np.int32) // 16
+    uneven[0] = 1                       # group 0 has 15 members, group 1 has 17
+    with pytest.raises(mnb.MnbError) as e:
+        mnb.mnb_act_order_permutation(d, uneven)
+    assert e.value.status == mnb.MNB_ERR_UNSUPPORTED and "members" in str(e.value)
+
+
+def test_act_order_argument_validation():
+    lib = mnb.lib
+    d = mnb.desc(64, 256, 32, True, mnb.MNB_F16)
+    E = mnb.MNB_ERR_INVALID_ARGUMENT
+    need = lib.mnb_gemm_act_order_workspace_bytes(D(d), 40, mnb.MNB_F16)
+    assert need >= 40 * 256 * 2
+    assert lib.mnb_gemm_act_order_workspace_bytes(D(d), 1, mnb.MNB_F32) >= 256 * 4
+    assert "workspace" in _expect(E, lib.mnb_gemm_act_order, D(d), FAKE, FAKE, 40, 1, FAKE, FAKE,
+                                  FAKE, need - 1, None)
+    assert "perm" in _expect(E, lib.mnb_gemm_act_order, D(d), FAKE, FAKE, 40, 1, None, FAKE,
+                             FAKE, need, None)
+    assert "fp16" in _expect(mnb.MNB_ERR_UNSUPPORTED, lib.mnb_gemm_act_order, D(d), FAKE, FAKE, 8,
+                             mnb.MNB_F32, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert "perm" in _expect(E, lib.mnb_repack_act_order, D(d), FAKE, FAKE, FAKE, None, FAKE, None)
+    assert lib.mnb_gemm_act_order(D(d), None, None, 0, 1, None, None, None, 0, None) == mnb.MNB_OK
+
+
 def test_empty_problems_are_noops_without_a_device():
     lib = mnb.lib
     d = mnb.desc(0, 256, 32, True, mnb.MNB_F16)

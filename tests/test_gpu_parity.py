@@ -374,6 +374,45 @@ def test_bias_epilogue_parity(mnb, M, N, K, g, adt, zp):
         assert (y.cpu().numpy() == y0h).all()
 
 
+ACT_ORDER_CASES = [
+    # M, N, K, g, activation dtype, zp: every path after the column permutation
+    (1, 300, 512, 32, "f16", True), (1, 200, 640, 64, "f32", False),
+    (4, 257, 896, 32, "f16", True), (40, 300, 512, 64, "f16", True),
+    (130, 70, 384, 128, "f16", False),
+]
+
+
+@pytest.mark.parametrize("M,N,K,g,adt,zp", ACT_ORDER_CASES)
+def test_act_order_parity(mnb, M, N, K, g, adt, zp):
+    """Act-order weights (random g_idx, every group of exactly g positions):
+    the repack in permuted order and the GEMM on permuted activation columns,
+    against the oracle's act-order dequant (scale and zero point of group
+    g_idx[k]) and fp64 matmul, on every path."""
+    t = G.torch()
+    w = _weight(N, K, g, "f16", zp, seed=M + 3)
+    rng = np.random.default_rng(M * 31 + K)
+    g_idx = np.empty(K, np.int32)
+    g_idx[rng.permutation(K)] = np.arange(K) // g
+    A = _act(M, K, adt, seed=M + 5)
+    d = mnb.desc(N, K, g, zp, mnb.MNB_F16)
+    perm = mnb.mnb_act_order_permutation(d, g_idx)
+    perm_dev = G.to_dev(perm)
+    rep = t.empty(mnb.mnb_repacked_bytes(d), dtype=t.uint8, device="cuda")
+    mnb.mnb_repack_act_order(d, G.to_dev(w.packed.reshape(-1)), G.to_dev(w.scales.reshape(-1)),
+                             None if w.zero_points is None else G.to_dev(w.zero_points.reshape(-1)),
+                             perm_dev, rep)
+    n_ws = mnb.mnb_gemm_act_order_workspace_bytes(d, M, mnb.MNB_F16 if adt == "f16" else mnb.MNB_F32)
+    ws = t.zeros(n_ws, dtype=t.uint8, device="cuda")
+    y = t.empty((M, N), dtype=t.float16 if adt == "f16" else t.float32, device="cuda")
+    mnb.mnb_gemm_act_order(d, rep, G.to_dev(A), M, perm_dev, y, ws, n_ws)
+    W = o.dequant_gidx(w.packed, w.scales, w.zero_points, g_idx, N, K, g)
+    Y, B = o.matmul(o.decode(A.reshape(-1, K)), W)
+    G.assert_within(G.host(y), Y, B, "act order M=%d N=%d K=%d g=%d %s" % (M, N, K, g, adt))
+    # the plain repack of the same operands is a different weight unless the
+    # order is the identity
+    assert not (perm == np.arange(K)).all()
+
+
 # ------------------------------------------------------------ properties ----
 
 def test_results_are_deterministic(mnb):
