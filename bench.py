@@ -39,7 +39,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--only", default="",
-                   help="comma list of: gemv,gate_up,down,small_m,prefill,bias (default all); "
+                   help="comma list of: gemv,gate_up,down,small_m,prefill,bias,act_order (default all); "
                         "copy adds a plain 256 MiB device copy, the reference kernel "
                         "for scaling the HBM byte counters")
     return p.parse_args()
@@ -86,17 +86,30 @@ class CopyWorkload:
 class Workload:
     """R rotating device copies of one workload's operands."""
 
-    def __init__(self, name, M, weights, K, N, g, act_fp16=True, sigma=1.0, seed=(0,), bias=None):
+    def __init__(self, name, M, weights, K, N, g, act_fp16=True, sigma=1.0, seed=(0,), bias=None,
+                 act_order=False):
         import torch
         from block_wise_int4_amd import mnb, synth
         self.name, self.M, self.K, self.N, self.g = name, M, K, N, g
         dev = torch.device("cuda:0")
         qs = []
+        self.perm = None
         for w in weights:
-            q = mnb.repack(torch.from_numpy(w.packed.reshape(-1)).to(dev),
-                           torch.from_numpy(w.scales.reshape(-1)).to(dev),
-                           None if w.zero_points is None else
-                           torch.from_numpy(w.zero_points.reshape(-1)).to(dev), N, K, g)
+            args = (torch.from_numpy(w.packed.reshape(-1)).to(dev), torch.from_numpy(w.scales.reshape(-1)).to(dev),
+                    None if w.zero_points is None else torch.from_numpy(w.zero_points.reshape(-1)).to(dev))
+            if act_order:
+                # a seeded act order: every group gets exactly g positions
+                import numpy as np
+                rng = np.random.default_rng(seed + (7,))
+                g_idx = np.empty(K, np.int32)
+                g_idx[rng.permutation(K)] = np.arange(K) // g
+                d = mnb.desc(N, K, g, w.zero_points is not None, mnb._dtype_code(args[1]))
+                self.perm = torch.from_numpy(mnb.mnb_act_order_permutation(d, g_idx)).to(dev)
+                out = torch.empty(mnb.mnb_repacked_bytes(d), dtype=torch.uint8, device=dev)
+                mnb.mnb_repack_act_order(d, *args, self.perm, out)
+                q = mnb.QuantWeight(d, out)
+            else:
+                q = mnb.repack(*args, N, K, g)
             qs.append(q)
         A = torch.from_numpy(synth.activation(M, K, "f16" if act_fp16 else "f32", sigma, seed)).to(dev)
         zp = weights[0].zero_points is not None
@@ -111,6 +124,8 @@ class Workload:
             self.bias_stride = N if bias[0] == "rows" else 0
             self.bias_mode = bias[1]
             self.bytes += bias_rows * N * 2
+        if act_order:
+            self.bytes += K * 4                       # the group indices
         self.flops = 2 * M * N * K * len(weights)
         per_copy = (sum(q.repacked.numel() for q in qs) + A.numel() * A.element_size() * 2 + M * N * 2
                     + bias_rows * N * 2)
@@ -127,6 +142,8 @@ class Workload:
                 b = torch.randn(bias_rows * N, generator=gen).to(A.dtype).to(dev)
             self.copies.append((ws, a, y, b))
         self.ws_bytes = mnb.mnb_gemm_workspace_bytes(self.desc, M) if len(qs) == 1 else 0
+        if act_order:
+            self.ws_bytes = mnb.mnb_gemm_act_order_workspace_bytes(self.desc, M)
         self.workspaces = [torch.zeros(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
                            for _ in range(self.R)]
         torch.cuda.synchronize()
@@ -139,6 +156,9 @@ class Workload:
         for r, (ws, a, y, b) in enumerate(self.copies):
             if self.fused:
                 mnb.mnb_gemv_gate_up_swiglu(self.desc, ws[0], ws[1], a, y)
+            elif self.perm is not None:
+                mnb.mnb_gemm_act_order(self.desc, ws[0], a, self.M, self.perm, y, self.workspaces[r],
+                                       self.ws_bytes)
             elif b is not None:
                 mnb.mnb_gemm_bias(self.desc, ws[0], a, self.M, b, self.bias_stride, self.bias_mode, y,
                                   self.workspaces[r], self.ws_bytes)
@@ -227,7 +247,8 @@ def counted_traffic(workload, variant):
 
 def build_workloads(only):
     from block_wise_int4_amd import synth as S
-    sel = set(x for x in only.split(",") if x) or {"gemv", "gate_up", "down", "small_m", "prefill", "bias"}
+    sel = set(x for x in only.split(",") if x) or {"gemv", "gate_up", "down", "small_m", "prefill", "bias",
+                                                   "act_order"}
     wl = [CopyWorkload()] if "copy" in sel else []
     if "gemv" in sel:
         c = S.DECODE_GEMV
@@ -258,6 +279,13 @@ def build_workloads(only):
         wl.append(Workload(c.name + " + bias [N] fp16(fp16(acc)+b)", c.M, [S.workload_weights(c)],
                            c.K, c.N, c.group, sigma=c.sigma, seed=c.seed + (c.M,),
                            bias=("vector", mnb.MNB_BIAS_AFTER_ROUND)))
+    if "act_order" in sel:
+        c = S.DECODE_GEMV
+        wl.append(Workload(c.name + " act-order", 1, [S.workload_weights(c)], c.K, c.N, c.group,
+                           seed=c.seed + (1,), act_order=True))
+        c = S.PREFILL_GEMM
+        wl.append(Workload(c.name + " act-order", c.M, [S.workload_weights(c)], c.K, c.N, c.group,
+                           sigma=c.sigma, seed=c.seed + (c.M,), act_order=True))
     return wl
 
 

@@ -15,21 +15,32 @@ namespace mnb {
 
 namespace {
 
-// One thread per output element; consecutive threads write consecutive
-// columns of a row (the reads are a gather within the row).
+// One thread per 16 output bytes (8 fp16 or 4 fp32 columns of a row, one
+// vector store; the reads gather within the row, which the caches hold).
+// K is a multiple of 16 (the group size), so a vector never straddles rows.
 template <typename T>
 __global__ __launch_bounds__(256) void permute_columns_kernel(const T* __restrict__ a,
                                                               const int32_t* __restrict__ perm,
                                                               T* __restrict__ out, int64_t M,
                                                               int64_t K)
 {
+    constexpr int V = 16 / sizeof(T);
     const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= M * K) return;
-    const int64_t m = idx / K;
-    const int64_t k = idx - m * K;
-    int64_t src = perm[k];
-    if (src < 0 || src >= K) src = 0;
-    out[idx] = a[m * K + src];
+    if (idx >= M * K / V) return;
+    const int64_t e0 = idx * V;
+    const int64_t m = e0 / K;
+    const int64_t k0 = e0 - m * K;
+    const T* row = a + m * K;
+    T v[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+        int64_t src = perm[k0 + i];
+        if (src < 0 || src >= K) src = 0;
+        v[i] = row[src];
+    }
+    u4_t o;
+    __builtin_memcpy(&o, v, 16);
+    reinterpret_cast<u4_t*>(out)[idx] = o;
 }
 
 }  // namespace
@@ -37,7 +48,7 @@ __global__ __launch_bounds__(256) void permute_columns_kernel(const T* __restric
 hipError_t launch_permute_columns(const void* a, const int32_t* perm, int64_t M, int64_t K,
                                   int elem_bytes, void* out, hipStream_t stream)
 {
-    const int64_t total = M * K;
+    const int64_t total = M * K / (16 / elem_bytes);
     const unsigned blocks = (unsigned)((total + 255) / 256);
     if (elem_bytes == 2)
         permute_columns_kernel<uint16_t><<<blocks, 256, 0, stream>>>(

@@ -14,6 +14,8 @@
 // reduce over k; each group's fp32 partial is scaled into an fp32 sum.  fp32
 // activations take a VALU path with fp32 products instead.  Waves reduce
 // through LDS in a fixed order (results are deterministic).
+#include <type_traits>
+
 #include "mnb_device.hpp"
 #include "mnb_internal.hpp"
 
@@ -42,6 +44,7 @@ struct GemvParams {
     void* y;
     const void* bias;      // optional [N], the output's dtype
     int bias_after_round;
+    const int32_t* perm;   // act order: column k of the product is a[perm[k]]
     int N, K, C;
 };
 
@@ -224,7 +227,14 @@ __device__ __forceinline__ float chunk_dot_f32(const ChunkRegs<ST, Q, HAS_ZP>& r
 
 __device__ __forceinline__ float silu_f32(float x) { return x / (1.0f + __expf(-x)); }
 
-template <typename AT, typename ST, int Q, bool HAS_ZP, bool FUSED, int kBatch>
+typedef uint32_t u2_t __attribute__((ext_vector_type(2)));
+
+// LDS behind the staged activation: the per-wave partials of both outputs
+constexpr int kRedBytes = 2 * kMaxWaves * 16 * sizeof(float);
+// act order: index vectors (4 columns each) a thread requests up front
+constexpr int kPermPre = 4;
+
+template <typename AT, typename ST, int Q, bool HAS_ZP, bool FUSED, int kBatch, bool PERM>
 __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
 {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -246,6 +256,20 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
     // count completions in issue order, so the small loads never wait behind
     // the code stream, and chunk u is computed as soon as its own code word
     // is in while the later ones are still streaming.
+
+    // 0. act order: the thread's first column indices, four per vector
+    //    (K is a whole number of groups, so a multiple of 4)
+    const int nq = p.K / 4;
+    const int nq_pad = (int)(kpad / 4);
+    const u4_t* perm_vec = reinterpret_cast<const u4_t*>(p.perm);
+    u4_t pidx[kPermPre];
+    if constexpr (PERM) {
+#pragma unroll
+        for (int j = 0; j < kPermPre; ++j) {
+            const int v = tid + j * (int)blockDim.x;
+            pidx[j] = perm_vec[v < nq ? v : 0];
+        }
+    }
 
     // 1. first activation vector of this thread (16 bytes)
     constexpr int kPerVec = 16 / sizeof(AT);
@@ -291,6 +315,37 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
         s_vec[v] = v < nvec_valid ? a_vec[v] : u4_t{0u, 0u, 0u, 0u};
     block_sync_lds();
 
+    // 3b. act order: gather the staged activation into the codes' column
+    //     order, behind the reduction area (an index outside 0..K-1 reads
+    //     column 0; columns past K stay zero)
+    const unsigned char* act = smem;
+    if constexpr (PERM) {
+        typedef typename std::conditional<F16, uint16_t, uint32_t>::type RT;
+        typedef typename std::conditional<F16, u2_t, u4_t>::type VT;
+        const RT* src = reinterpret_cast<const RT*>(smem);
+        unsigned char* dst = smem + kpad * sizeof(AT) + kRedBytes;
+        auto gather4 = [&](int v, const u4_t& ix) {
+            RT o[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t k = ix[i] < (uint32_t)p.K ? ix[i] : 0u;
+                o[i] = v < nq ? src[k] : RT(0);
+            }
+            VT ov;
+            __builtin_memcpy(&ov, o, sizeof(ov));
+            reinterpret_cast<VT*>(dst)[v] = ov;
+        };
+#pragma unroll
+        for (int j = 0; j < kPermPre; ++j) {
+            const int v = tid + j * (int)blockDim.x;
+            if (v < nq_pad) gather4(v, pidx[j]);
+        }
+        for (int v = tid + kPermPre * (int)blockDim.x; v < nq_pad; v += blockDim.x)
+            gather4(v, perm_vec[v < nq ? v : 0]);
+        block_sync_lds();
+        act = dst;
+    }
+
     // 4. compute a batch while the next one is in flight
     auto compute_batch = [&](Regs (&r)[NW][kBatch], int cb) {
 #pragma unroll
@@ -301,10 +356,10 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
                 for (int x = 0; x < NW; ++x) {
                     if (F16)
                         acc[x] = chunk_dot_f16<ST, Q, HAS_ZP>(
-                            r[x][u], reinterpret_cast<const _Float16*>(smem), c, h, acc[x]);
+                            r[x][u], reinterpret_cast<const _Float16*>(act), c, h, acc[x]);
                     else
                         acc[x] = chunk_dot_f32<ST, Q, HAS_ZP>(
-                            r[x][u], reinterpret_cast<const float*>(smem), c, h, acc[x]);
+                            r[x][u], reinterpret_cast<const float*>(act), c, h, acc[x]);
                 }
             }
         }
@@ -369,14 +424,23 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
     }
 }
 
+template <typename AT, typename ST, int Q, bool HAS_ZP, bool FUSED, bool PERM>
+hipError_t launch_b(const GemvParams& p, int waves, size_t smem, int64_t tiles, hipStream_t s)
+{
+    if (waves > kMaxWaves / 2)
+        gemv_kernel<AT, ST, Q, HAS_ZP, FUSED, 2, PERM><<<dim3((unsigned)tiles), dim3(waves * 64), smem, s>>>(p);
+    else
+        gemv_kernel<AT, ST, Q, HAS_ZP, FUSED, 4, PERM><<<dim3((unsigned)tiles), dim3(waves * 64), smem, s>>>(p);
+    return hipGetLastError();
+}
+
 template <typename AT, typename ST, int Q, bool HAS_ZP, bool FUSED>
 hipError_t launch_t(const GemvParams& p, int waves, size_t smem, int64_t tiles, hipStream_t s)
 {
-    if (waves > kMaxWaves / 2)
-        gemv_kernel<AT, ST, Q, HAS_ZP, FUSED, 2><<<dim3((unsigned)tiles), dim3(waves * 64), smem, s>>>(p);
-    else
-        gemv_kernel<AT, ST, Q, HAS_ZP, FUSED, 4><<<dim3((unsigned)tiles), dim3(waves * 64), smem, s>>>(p);
-    return hipGetLastError();
+    // act order comes without the fused gate/up form
+    if constexpr (!FUSED)
+        if (p.perm) return launch_b<AT, ST, Q, HAS_ZP, false, true>(p, waves, smem, tiles, s);
+    return launch_b<AT, ST, Q, HAS_ZP, FUSED, false>(p, waves, smem, tiles, s);
 }
 
 template <typename AT, typename ST, bool HAS_ZP, bool FUSED>
@@ -408,14 +472,14 @@ GemvWeight gw(const WeightView& v)
 
 }  // namespace
 
-int64_t gemv_max_k(bool f16_act)
+int64_t gemv_max_k(bool f16_act, bool act_order)
 {
-    return kMaxStageBytes / (f16_act ? 2 : 4) / kChunkK * kChunkK;
+    return kMaxStageBytes / (act_order ? 2 : 1) / (f16_act ? 2 : 4) / kChunkK * kChunkK;
 }
 
 hipError_t launch_gemv(const Layout& L, const WeightView& gate, const WeightView* up,
-                       const void* a, bool f16_act, const Bias& bias, void* y, hipStream_t stream,
-                       const char** variant)
+                       const void* a, const int32_t* perm, bool f16_act, const Bias& bias, void* y,
+                       hipStream_t stream, const char** variant)
 {
     GemvParams p;
     p.w[0] = gw(gate);
@@ -424,16 +488,19 @@ hipError_t launch_gemv(const Layout& L, const WeightView& gate, const WeightView
     p.y = y;
     p.bias = bias.ptr;
     p.bias_after_round = bias.after_round;
+    p.perm = up ? nullptr : perm;
     p.N = (int)L.N;
     p.K = (int)L.K;
     p.C = (int)L.C;
     const int max_waves = L.T * kMaxWaves <= kResidentWaves ? kMaxWaves : kMaxWaves / 2;
     int waves = (int)(L.C < max_waves ? L.C : max_waves);
     if (waves < 1) waves = 1;
-    const size_t smem = (size_t)L.C * kChunkK * (f16_act ? 2 : 4) + 2 * kMaxWaves * 16 * sizeof(float);
+    const size_t act_bytes = (size_t)L.C * kChunkK * (f16_act ? 2 : 4);
+    const size_t smem = act_bytes * (p.perm ? 2 : 1) + kRedBytes;
     const bool fused = up != nullptr;
     if (variant) *variant = fused ? (f16_act ? "gemv_gate_up_swiglu_f16" : "gemv_gate_up_swiglu_f32")
-                                  : (f16_act ? "gemv_f16" : "gemv_f32");
+                          : p.perm ? (f16_act ? "gemv_act_order_f16" : "gemv_act_order_f32")
+                                   : (f16_act ? "gemv_f16" : "gemv_f32");
     if (f16_act) {
         return fused ? launch_a<__half, true>(L, p, waves, smem, stream)
                      : launch_a<__half, false>(L, p, waves, smem, stream);

@@ -220,15 +220,15 @@ mnb_status mnb_repack_act_order(const mnb_weight_desc* w, const uint8_t* packed,
 
 static mnb_status gemv_common(const mnb_weight_desc* w, const void* gate, const void* up,
                               const void* a, int32_t a_dtype, const mnb::Bias& bias, void* y,
-                              void* stream)
+                              void* stream, const int32_t* perm = nullptr)
 {
     Layout L;
     MNB_TRY(check_desc(w, &L));
     MNB_TRY(check_act_dtype(a_dtype));
     const bool f16 = a_dtype == MNB_F16;
-    if (L.K > mnb::gemv_max_k(f16))
+    if (L.K > mnb::gemv_max_k(f16, perm != nullptr))
         return fail(MNB_ERR_UNSUPPORTED, "K=%lld exceeds the decode GEMV limit %lld for %s activations",
-                    (long long)L.K, (long long)mnb::gemv_max_k(f16), f16 ? "fp16" : "fp32");
+                    (long long)L.K, (long long)mnb::gemv_max_k(f16, perm != nullptr), f16 ? "fp16" : "fp32");
     if (L.N == 0) return ok("noop");
     MNB_TRY(check_ptr(gate, 256, up ? "gate_repacked" : "repacked"));
     if (up) MNB_TRY(check_ptr(up, 256, "up_repacked"));
@@ -240,7 +240,7 @@ static mnb_status gemv_common(const mnb_weight_desc* w, const void* gate, const 
     const mnb::WeightView gv = mnb::view_of(L, gate);
     mnb::WeightView uv;
     if (up) uv = mnb::view_of(L, up);
-    return launched(mnb::launch_gemv(L, gv, up ? &uv : nullptr, a, f16, bias, y,
+    return launched(mnb::launch_gemv(L, gv, up ? &uv : nullptr, a, perm, f16, bias, y,
                                      static_cast<hipStream_t>(stream), &variant),
                     variant);
 }
@@ -376,6 +376,11 @@ mnb_status mnb_gemm_act_order(const mnb_weight_desc* w, const void* repacked, co
     if (!perm) return fail(MNB_ERR_INVALID_ARGUMENT, "perm is NULL");
     MNB_TRY(check_ptr(perm, 4, "perm"));
     MNB_TRY(check_ptr(a, 16, "a"));
+    // decode: the GEMV gathers A's columns itself while it stages them,
+    // when the two copies fit in its LDS and perm is 16-byte aligned
+    if (m == 1 && L.K <= mnb::gemv_max_k(a_dtype == MNB_F16, true) &&
+        reinterpret_cast<uintptr_t>(perm) % 16 == 0)
+        return gemv_common(w, repacked, nullptr, a, a_dtype, mnb::Bias(), y, stream, perm);
     MNB_TRY(check_device());
     // A's columns in the repacked order, then the ordinary call on them
     const hipError_t e = mnb::launch_permute_columns(a, perm, m, L.K, a_dtype == MNB_F32 ? 4 : 2, workspace,

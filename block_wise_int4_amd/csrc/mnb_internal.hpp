@@ -26,14 +26,16 @@ inline WeightView view_of(const Layout& L, const void* repacked)
 hipError_t launch_repack(const Layout& L, const uint8_t* packed, const void* scales,
                          const uint8_t* zp, const int32_t* perm, void* repacked, hipStream_t stream);
 // out[m, k] = a[m, perm[k]] for an [M, K] matrix of elem_bytes (2 or 4)
-// elements; an index outside 0..K-1 reads column 0.
+// elements; K a multiple of 16, out 16-byte aligned; an index outside
+// 0..K-1 reads column 0.
 hipError_t launch_permute_columns(const void* a, const int32_t* perm, int64_t M, int64_t K,
                                   int elem_bytes, void* out, hipStream_t stream);
 hipError_t launch_unpack_debug(const Layout& L, const void* repacked, uint8_t* codes, float* w,
                                hipStream_t stream);
 
-// Largest K the decode GEMV stages in LDS, per activation dtype.
-int64_t gemv_max_k(bool f16_act);
+// Largest K the decode GEMV stages in LDS, per activation dtype; act order
+// stages a second, gathered copy.
+int64_t gemv_max_k(bool f16_act, bool act_order = false);
 // Optional bias of the output, element (m, n) at ptr[m * row_stride + n], in
 // the output's dtype; after_round selects fp16(fp16(acc) + b) over
 // fp16(acc + b).
@@ -44,9 +46,11 @@ struct Bias {
 };
 
 // y = a . dequant(B)^T (up == nullptr) or silu(a . Bg^T) * (a . Bu^T).
+// perm (act order, up == nullptr only): NULL, or device int32 [K], 16-byte
+// aligned, K a multiple of 4: the product takes a[perm[k]] at column k.
 hipError_t launch_gemv(const Layout& L, const WeightView& gate, const WeightView* up,
-                       const void* a, bool f16_act, const Bias& bias, void* y, hipStream_t stream,
-                       const char** variant);
+                       const void* a, const int32_t* perm, bool f16_act, const Bias& bias, void* y,
+                       hipStream_t stream, const char** variant);
 
 // 2 <= M <= 16, fp16 activations.
 size_t gemm_small_workspace(const Layout& L, int64_t m);

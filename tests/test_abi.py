@@ -210,6 +210,12 @@ def test_act_order_argument_validation():
                              mnb.MNB_F32, FAKE, FAKE, FAKE, 1 << 30, None)
     assert "perm" in _expect(E, lib.mnb_repack_act_order, D(d), FAKE, FAKE, FAKE, None, FAKE, None)
     assert lib.mnb_gemm_act_order(D(d), None, None, 0, 1, None, None, None, 0, None) == mnb.MNB_OK
+    # K is a whole number of groups (the descriptor check every call makes)
+    r = mnb.desc(64, 250, 32, True, mnb.MNB_F16)
+    U = mnb.MNB_ERR_UNSUPPORTED
+    assert "not a multiple" in _expect(U, lib.mnb_repack_act_order, D(r), FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert "not a multiple" in _expect(U, lib.mnb_gemm_act_order, D(r), FAKE, FAKE, 1, 1, FAKE, FAKE, FAKE,
+                                       1 << 30, None)
 
 
 def test_empty_problems_are_noops_without_a_device():

@@ -379,6 +379,9 @@ ACT_ORDER_CASES = [
     (1, 300, 512, 32, "f16", True), (1, 200, 640, 64, "f32", False),
     (4, 257, 896, 32, "f16", True), (40, 300, 512, 64, "f16", True),
     (130, 70, 384, 128, "f16", False),
+    # decode beyond the K at which the GEMV holds both copies of A in LDS:
+    # the separate column permutation, then the plain GEMV
+    (1, 48, 16384, 128, "f16", True), (1, 40, 8192, 64, "f32", False),
 ]
 
 
@@ -411,6 +414,21 @@ def test_act_order_parity(mnb, M, N, K, g, adt, zp):
     # the plain repack of the same operands is a different weight unless the
     # order is the identity
     assert not (perm == np.arange(K)).all()
+    if M == 1:
+        f16 = adt == "f16"
+        gathered = K <= (15872 if f16 else 7936)
+        suffix = "f16" if f16 else "f32"
+        assert mnb.mnb_last_variant() == ("gemv_act_order_" if gathered else "gemv_") + suffix
+        # a perm that is not 16-byte aligned takes the separate permutation;
+        # both paths feed the GEMV the same values, so the results agree bit
+        # for bit
+        shifted = t.zeros(K + 1, dtype=t.int32, device="cuda")
+        shifted[1:] = perm_dev
+        y2 = t.empty_like(y)
+        mnb.mnb_gemm_act_order(d, rep, G.to_dev(A), M, shifted[1:], y2, ws, n_ws)
+        assert mnb.mnb_last_variant() == "gemv_" + suffix
+        t.cuda.synchronize()
+        assert t.equal(y, y2)
 
 
 # ------------------------------------------------------------ properties ----
