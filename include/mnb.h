@@ -237,8 +237,12 @@ mnb_status mnb_repack_act_order(const mnb_weight_desc* w, const uint8_t* packed,
  *    M >= 1.  perm: device int32 [K], the one used by the repack.  The
  *    workspace (device, 256-byte aligned) holds A with its columns in perm
  *    order, then mnb_gemm's own workspace:
- *    mnb_gemm_act_order_workspace_bytes(w, m, a_dtype) bytes.  Other
- *    arguments, dtypes and errors as mnb_gemm. */
+ *    mnb_gemm_act_order_workspace_bytes(w, m, a_dtype) bytes.  At M = 1
+ *    with a 16-byte aligned perm and K <= 15872 (fp16 activations) or
+ *    K <= 7936 (fp32) the GEMV reorders A itself while staging it and the
+ *    workspace goes unused (its size is still checked); both routes give the
+ *    same bits.  Indices outside 0..K-1 in perm give wrong results, never an
+ *    out-of-range read.  Other arguments, dtypes and errors as mnb_gemm. */
 size_t mnb_gemm_act_order_workspace_bytes(const mnb_weight_desc* w, int64_t m, int32_t a_dtype);
 mnb_status mnb_gemm_act_order(const mnb_weight_desc* w, const void* repacked, const void* a, int64_t m,
                               int32_t a_dtype, const int32_t* perm, void* y, void* workspace,
