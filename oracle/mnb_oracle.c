@@ -40,6 +40,16 @@
  *         to fp16 (the operator's own bias), or rounded to fp16 first and then
  *         added in fp32 and rounded again (a folded elementwise Add, which
  *         must stay byte-identical to the two-operator path).
+ *  [ACC4] onnx-runtime-ep-cuda 0.1.0-dev.3, src/kernels/matmul_nbits.rs --
+ *         the accuracy_level=4 path of the fp32 operator (fp32 A, fp32
+ *         scales, fp32 Y): kernel matmul_nbits_accuracy4 (any M, block size,
+ *         zero points) and the M=1 pair matmul_nbits_quantize_accuracy4_block32
+ *         / matmul_nbits_gemv_accuracy4_block32.  Each row of A is quantized
+ *         to int8 with one scale, max|a|/127 in binary32; a code is a*(1/scale)
+ *         in binary32, clamped to [-127, 127] and rounded half away from
+ *         zero; the integer dot of each block, sum q*(code - zp), is scaled
+ *         by that block's weight scale and the row's activation scale; a row
+ *         whose max is 0 gives the bias (or 0).
  *
  * Parity pins for every function live in tests/test_oracle.py (worked
  * examples, exhaustive nibble decode, pack/unpack identity, code==zp gives
@@ -357,6 +367,73 @@ void oracle_dequant_gidx(const uint8_t* packed, const double* scales, const uint
             const int code = oracle_code(packed, n, k, K, g);
             const int zp = oracle_zero_point(zero_points, n, grp, kb);
             w[n * K + k] = ((double)code - (double)zp) * scales[n * kb + grp];
+        }
+    }
+}
+
+/* ---- int8 activations, accuracy_level 4 [ACC4] --------------------------- */
+
+/* One row of A to int8: scale = max|a| / 127 and q[k] = round(clamp(a[k] / scale))
+ * in the binary32 steps of the pages: the maximum skips NaN (as fmaxf does),
+ * the reciprocal and the product are binary32 operations, the clamp keeps the
+ * non-NaN bound (so a NaN activation becomes -127), and the rounding sends
+ * halves away from zero.  A row whose maximum is 0 gets scale 0 and all-zero
+ * codes. */
+void oracle_acc4_quantize_row(const float* a, int64_t K, int8_t* q, float* scale)
+{
+    float max_abs = 0.0f;
+    for (int64_t k = 0; k < K; ++k) max_abs = fmaxf(max_abs, fabsf(a[k]));
+    const float s = max_abs == 0.0f ? 0.0f : max_abs / 127.0f;
+    const float inv = s == 0.0f ? 0.0f : 1.0f / s;
+    for (int64_t k = 0; k < K; ++k) {
+        int v = 0;
+        if (s != 0.0f) {
+            const float x = a[k] * inv;
+            v = (int)roundf(fminf(127.0f, fmaxf(-127.0f, x)));
+        }
+        q[k] = (int8_t)v;
+    }
+    *scale = s;
+}
+
+void oracle_acc4_quantize(const float* a, int64_t M, int64_t K, int8_t* q, float* scale)
+{
+    for (int64_t m = 0; m < M; ++m) oracle_acc4_quantize_row(a + m * K, K, q + m * K, scale + m);
+}
+
+/* Y[m,n] = bias[n] + scale_a[m] * sum_b scale[n,b] * dot[m,n,b] in fp64, with
+ * dot[m,n,b] = sum over k in block b of q[m,k] * (code[n,k] - zp[n,b]), an
+ * exact integer; a row with scale_a 0 gives bias[n] (or 0).  bias may be
+ * NULL; scales are the decoded weight scales [N, k_blocks].  Bnd[m,n] is the
+ * error scale of a binary32 evaluation: sum_b |scale_a * scale[n,b] * dot|
+ * + |bias[n]|.  q and scale_a (the quantized rows, [M,K] and [M]) are
+ * written too. */
+void oracle_acc4_matmul(const float* a, int64_t M, int64_t K, const uint8_t* packed,
+                        const double* scales, const uint8_t* zero_points, int64_t N, int64_t g,
+                        const float* bias, double* Y, double* Bnd, int8_t* q, float* scale_a)
+{
+    const int64_t kb = k_blocks_of(K, g);
+    oracle_acc4_quantize(a, M, K, q, scale_a);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            const double b = bias ? (double)bias[n] : 0.0;
+            const double sa = (double)scale_a[m];
+            double y = 0.0, bnd = 0.0;
+            if (sa != 0.0) {
+                for (int64_t blk = 0; blk < kb; ++blk) {
+                    const int zp = oracle_zero_point(zero_points, n, blk, kb);
+                    int64_t dot = 0;
+                    const int64_t end = (blk + 1) * g < K ? (blk + 1) * g : K;
+                    for (int64_t k = blk * g; k < end; ++k)
+                        dot += (int64_t)q[m * K + k] * (oracle_code(packed, n, k, K, g) - zp);
+                    const double term = sa * scales[n * kb + blk] * (double)dot;
+                    y += term;
+                    bnd += fabs(term);
+                }
+            }
+            Y[m * N + n] = y + b;
+            Bnd[m * N + n] = bnd + fabs(b);
         }
     }
 }

@@ -78,6 +78,8 @@ def _load():
     lib.oracle_bias_f16.argtypes = [ctypes.c_float, ctypes.c_uint16, ctypes.c_int]
     lib.oracle_bias_f16.restype = ctypes.c_uint16
     lib.oracle_bias_f16_array.argtypes = [p, p, i64, ctypes.c_int, p]
+    lib.oracle_acc4_quantize.argtypes = [p, i64, i64, p, p]
+    lib.oracle_acc4_matmul.argtypes = [p, i64, i64, p, p, p, i64, i64, p, p, p, p, p]
     _lib = lib
     return lib
 
@@ -265,6 +267,52 @@ def bias_bound(Y: np.ndarray, Bnd: np.ndarray, bias64: np.ndarray) -> np.ndarray
     binary16 rounding of the sum (together at most 2^-10 of its magnitude)."""
     e = REL_TOL * np.asarray(Bnd, np.float64) + ABS_TOL
     return e + 2.0 ** -10 * (np.abs(np.asarray(Y, np.float64) + bias64) + e)
+
+
+# ---- int8 activations (accuracy_level 4) -----------------------------------
+
+def acc4_quantize(A) -> tuple:
+    """Rows of fp32 A [M,K] to int8 with one binary32 scale each:
+    (q int8 [M,K], scale float32 [M])."""
+    A = np.ascontiguousarray(A, np.float32)
+    M, K = A.shape
+    q = np.empty((M, K), dtype=np.int8)
+    sc = np.empty(M, dtype=np.float32)
+    _load().oracle_acc4_quantize(_ptr(A), M, K, _ptr(q), _ptr(sc))
+    return q, sc
+
+
+def acc4_matmul(A, packed, scales, zp, N: int, K: int, g: int, bias=None) -> tuple:
+    """The accuracy_level=4 product of fp32 A [M,K]: (Y, Bnd) [M,N] in fp64
+    from the int8 rows, plus those rows and their scales (q [M,K], scale [M])."""
+    A = np.ascontiguousarray(A, np.float32).reshape(-1, K)
+    M = A.shape[0]
+    kb = k_blocks(K, g)
+    s64 = decode(scales).reshape(-1)
+    packed = np.ascontiguousarray(packed, np.uint8)
+    assert s64.size == N * kb and packed.size == N * kb * (g // 2)
+    zp = None if zp is None else np.ascontiguousarray(zp, np.uint8)
+    b = None if bias is None else np.ascontiguousarray(bias, np.float32)
+    assert b is None or b.size == N
+    Y = np.empty((M, N), dtype=np.float64)
+    B = np.empty((M, N), dtype=np.float64)
+    q = np.empty((M, K), dtype=np.int8)
+    sc = np.empty(M, dtype=np.float32)
+    _load().oracle_acc4_matmul(_ptr(A), M, K, _ptr(packed), _ptr(s64), _ptr(zp), N, g, _ptr(b),
+                               _ptr(Y), _ptr(B), _ptr(q), _ptr(sc))
+    return Y, B, q, sc
+
+
+def acc4_bound(Bnd, K: int, g: int) -> np.ndarray:
+    """Tolerance of a binary32 evaluation of the int8-activation product, a
+    reading (the stated tolerance is for fp16 arithmetic): every integer block
+    dot is exact, so the only errors are binary32 roundings -- one per block
+    term (dot * scale, or dot * (scale_a * scale): two), the additions of the
+    k_blocks terms in any order, the product with the activation scale and the
+    bias addition: at most (k_blocks + 4) units of 2^-24 of Bnd, plus one
+    smallest subnormal per term for results below the normal range."""
+    kb = k_blocks(K, g)
+    return (kb + 4) * 2.0 ** -24 * np.asarray(Bnd, np.float64) + (kb + 2) * 2.0 ** -149
 
 
 # ---- acceptance ------------------------------------------------------------

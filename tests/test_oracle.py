@@ -319,10 +319,91 @@ def pin_group_indices():
                 assert Fraction(W[n, k]) == exact
 
 
+def pin_acc4_quantize():
+    """int8 activations, by hand: a row whose max is 127 has scale 1 and
+    inverse 1, so every code is the activation rounded half away from zero
+    (2.5 -> 3, -2.5 -> -3, 0.5 -> 1, 126.5 -> 127); a NaN is skipped by the
+    maximum and clamps to -127; a row of zeros (a NaN beside them included)
+    has scale 0 and all-zero codes; a row whose max is so small that 1/scale
+    overflows binary32 follows the binary32 steps: nonzero values give +-127
+    and a zero gives 0*inf = NaN, clamped to -127.  Then, on random rows of
+    every magnitude: the scale is max|a|/127 correctly rounded, the element at
+    the maximum gets +-127, and every code is within 1/2 (plus the binary32
+    error of the reciprocal and product) of a/scale."""
+    row = np.array([127, 2.5, -2.5, 0.5, -0.5, np.float32(1.5) - np.float32(2 ** -23), 126.5,
+                    -126.5, 0.0, np.nan, -0.49], np.float32)
+    q, sc = o.acc4_quantize(row[None])
+    assert sc.tolist() == [1.0]
+    assert q[0].tolist() == [127, 3, -3, 1, -1, 1, 127, -127, 0, -127, 0]
+    q, sc = o.acc4_quantize(np.array([[0.0, np.nan, -0.0]], np.float32))
+    assert sc.tolist() == [0.0] and q.tolist() == [[0, 0, 0]]
+    tiny = np.array([[1e-40, -3e-41, 0.0]], np.float32)
+    q, sc = o.acc4_quantize(tiny)
+    with np.errstate(over="ignore"):
+        assert 0 < sc[0] < 2.0 ** -126 and np.isinf(np.float32(1) / sc[0])
+    assert q.tolist() == [[127, -127, -127]]
+    rng = np.random.default_rng(31)
+    for mag in (1e-30, 1e-3, 1.0, 7.0, 1e4, 1e30):
+        A = (rng.standard_normal((6, 300)) * mag).astype(np.float32)
+        q, sc = o.acc4_quantize(A)
+        for m in range(A.shape[0]):
+            mx = Fraction(float(np.max(np.abs(A[m]))))
+            s = Fraction(float(sc[m]))
+            assert abs(s - mx / 127) <= s * Fraction(1, 2 ** 24)
+            assert abs(int(q[m, np.argmax(np.abs(A[m]))])) == 127
+            err = np.abs(q[m].astype(np.float64) - A[m].astype(np.float64) / float(sc[m]))
+            assert err.max() <= 0.5 + 1e-4, (mag, m, err.max())
+            assert ((np.sign(q[m]) == np.sign(A[m])) | (q[m] == 0)).all()
+            assert np.abs(q[m].astype(int)).max() <= 127
+
+
+def pin_acc4_matmul():
+    """int8-activation product: rows with max |a| = 127 and integer entries
+    have scale 1 and codes a, so with unit weight scales the product is the
+    integer GEMM sum_k a*(code - zp) (numpy int64 matmul over codes minus
+    their block's zero point) plus the bias, exactly; a row of zeros gives the
+    bias; on general operands the result differs from the unquantized product
+    (the pinned plain oracle) by at most the rounding of the codes,
+    sum_k |w[n,k]| * scale_a / 2."""
+    rng = np.random.default_rng(41)
+    for (M, K, N, g, with_zp) in ((3, 64, 5, 16, True), (2, 256, 9, 128, False), (4, 96, 7, 32, True)):
+        kb = K // g
+        codes = rng.integers(0, 16, (N, K), dtype=np.uint8)
+        z = rng.integers(0, 16, (N, kb), dtype=np.uint8) if with_zp else np.full((N, kb), 8, np.uint8)
+        A = rng.integers(-126, 127, (M, K)).astype(np.float32)
+        A[:, 3] = 127 * rng.choice([-1, 1], M)
+        bias = rng.integers(-40, 41, N).astype(np.float32) / 4
+        packed = o.pack_codes(codes, g)
+        zpk = o.pack_zero_points(z) if with_zp else None
+        Y, B, q, sc = o.acc4_matmul(A, packed, np.ones((N, kb), np.float32), zpk, N, K, g, bias)
+        assert (sc == 1).all() and (q == A).all()
+        wint = codes.astype(np.int64) - np.repeat(z.astype(np.int64), g, axis=1)
+        ref = A.astype(np.int64) @ wint.T
+        assert (Y == ref + bias.astype(np.float64)).all()
+        dots = (A.astype(np.int64)[:, None, :] * wint[None]).reshape(M, N, kb, g).sum(-1)
+        assert (B == np.abs(dots).sum(-1) + np.abs(bias)).all()
+        A[1] = 0
+        Y, B, q, sc = o.acc4_matmul(A, packed, np.ones((N, kb), np.float32), zpk, N, K, g, bias)
+        assert sc[1] == 0 and (Y[1] == bias).all() and (B[1] == np.abs(bias)).all()
+        # general scales and activations: within the rounding of the codes of
+        # the unquantized product
+        scales = rng.uniform(0.005, 0.02, (N, kb)).astype(np.float32)
+        Af = (rng.standard_normal((M, K)) * 3).astype(np.float32)
+        Y, B, q, sc = o.acc4_matmul(Af, packed, scales, zpk, N, K, g, None)
+        Yp, _ = o.matmul_nbits(Af, packed, scales, zpk, N, K, g)
+        W = o.dequant(packed, scales, zpk, N, K, g)
+        for m in range(M):
+            lim = np.abs(W).sum(axis=1) * float(sc[m]) * (0.5 + 1e-4)
+            assert (np.abs(Y[m] - Yp[m]) <= lim).all(), m
+            # and not equal to it: the codes do round
+            assert (Y[m] != Yp[m]).any()
+
+
 PINS = [pin_worked_examples, pin_exhaustive_nibbles, pin_pack_unpack_identity,
         pin_code_equals_zero_point_gives_zero, pin_bruteforce_exact,
         pin_integer_special_case, pin_linear_and_one_hot, pin_fp16_decode_all_patterns,
-        pin_swiglu, pin_round_f16_against_numpy, pin_bias_epilogue, pin_group_indices]
+        pin_swiglu, pin_round_f16_against_numpy, pin_bias_epilogue, pin_group_indices,
+        pin_acc4_quantize, pin_acc4_matmul]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -343,6 +424,40 @@ def test_within_bound_semantics():
         [False, True, False, False]
     assert o.within_bound([5.0], [-np.inf], [np.inf]).tolist() == [False]
     assert o.within_bound([1.0 + 1.1e-2], [1.0], [10.0]).tolist() == [False]
+
+
+def test_acc4_bound_covers_the_pages_binary32_orders():
+    """The int8-activation tolerance holds for both binary32 evaluation orders
+    the pages' kernels use (matmul_nbits.rs, matmul_nbits_accuracy4): the sum
+    of dot*scale over blocks times the activation scale at the end, and the
+    sum of dot*(scale_a*scale); each evaluated here in numpy binary32, from
+    the oracle's own codes."""
+    rng = np.random.default_rng(51)
+    for (K, N, g, with_zp) in ((4096, 64, 32, False), (2048, 48, 128, True), (1024, 40, 16, True)):
+        kb = K // g
+        codes = rng.integers(0, 16, (N, K), dtype=np.uint8)
+        z = rng.integers(0, 16, (N, kb), dtype=np.uint8) if with_zp else np.full((N, kb), 8, np.uint8)
+        scales = rng.uniform(0.002, 0.02, (N, kb)).astype(np.float32)
+        A = rng.standard_normal((1, K)).astype(np.float32)
+        bias = rng.standard_normal(N).astype(np.float32)
+        Y, B, q, sc = o.acc4_matmul(A, o.pack_codes(codes, g), scales,
+                                    o.pack_zero_points(z) if with_zp else None, N, K, g, bias)
+        wint = codes.astype(np.int64) - np.repeat(z.astype(np.int64), g, axis=1)
+        dots = (q[0].astype(np.int64)[None, :] * wint).reshape(N, kb, g).sum(-1).astype(np.float32)
+        sa = sc[0]
+        v1 = np.zeros(N, np.float32)
+        v2 = np.zeros(N, np.float32)
+        for b_ in range(kb):
+            v1 = v1 + dots[:, b_] * scales[:, b_]
+            v2 = v2 + dots[:, b_] * (sa * scales[:, b_])
+        y1 = v1 * sa + bias
+        y2 = v2 + bias
+        tol = o.acc4_bound(B[0], K, g)
+        assert (np.abs(y1 - Y[0]) <= tol).all() and (np.abs(y2 - Y[0]) <= tol).all()
+        # a hundred times tighter than the fp16 path's rule (1e-3 of Bnd): a
+        # wrong code moves an output by a few such bounds at most, which is
+        # why the GPU's codes are compared bit for bit on their own
+        assert (tol <= 1e-5 * B[0] + 1e-30).all()
 
 
 def test_oracle_decodes_the_synthetic_workloads():
@@ -387,6 +502,15 @@ MUTANTS = {
     "act-order scale by block": ("* scales[n * kb + grp];", "* scales[n * kb + k / g];"),
     "act-order zero point by block": ("oracle_zero_point(zero_points, n, grp, kb);",
                                       "oracle_zero_point(zero_points, n, k / g, kb);"),
+    "int8 codes ties to even": ("v = (int)roundf(", "v = (int)rintf("),
+    "int8 codes truncated": ("v = (int)roundf(", "v = (int)truncf("),
+    "int8 scale max/128": ("max_abs / 127.0f", "max_abs / 128.0f"),
+    "int8 clamp at -128": ("fmaxf(-127.0f, x)", "fmaxf(-128.0f, x)"),
+    "int8 dot without zero point": ("(oracle_code(packed, n, k, K, g) - zp)", "oracle_code(packed, n, k, K, g)"),
+    "int8 product without activation scale": ("const double term = sa * scales", "const double term = scales"),
+    "int8 weight scale of block 0": ("sa * scales[n * kb + blk]", "sa * scales[n * kb]"),
+    "int8 bias dropped": ("Y[m * N + n] = y + b;", "Y[m * N + n] = y;"),
+    "int8 last k of each block dropped": ("(blk + 1) * g < K ? (blk + 1) * g : K", "(blk + 1) * g - 1"),
 }
 
 
