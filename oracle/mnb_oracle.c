@@ -401,13 +401,16 @@ void oracle_acc4_quantize(const float* a, int64_t M, int64_t K, int8_t* q, float
     for (int64_t m = 0; m < M; ++m) oracle_acc4_quantize_row(a + m * K, K, q + m * K, scale + m);
 }
 
-/* Y[m,n] = bias[n] + scale_a[m] * sum_b scale[n,b] * dot[m,n,b] in fp64, with
- * dot[m,n,b] = sum over k in block b of q[m,k] * (code[n,k] - zp[n,b]), an
- * exact integer; a row with scale_a 0 gives bias[n] (or 0).  bias may be
- * NULL; scales are the decoded weight scales [N, k_blocks].  Bnd[m,n] is the
- * error scale of a binary32 evaluation: sum_b |scale_a * scale[n,b] * dot|
- * + |bias[n]|.  q and scale_a (the quantized rows, [M,K] and [M]) are
- * written too. */
+/* Y[m,n] = scale_a[m] * (sum_b scale[n,b] * dot[m,n,b]) + bias[n] in fp64,
+ * with dot[m,n,b] = sum over k in block b of q[m,k] * (code[n,k] - zp[n,b]),
+ * an exact integer; a row with scale_a 0 gives bias[n] (or 0).  The
+ * activation scale multiplies the sum over blocks, as in the M=1 kernel of
+ * the pages (for finite values the same number as scaling every block; for
+ * an infinite activation, whose scale is infinite, the result is an
+ * infinity of the sum's sign).  bias may be NULL; scales are the decoded
+ * weight scales [N, k_blocks].  Bnd[m,n] is the error scale of a binary32
+ * evaluation: |scale_a| * sum_b |scale[n,b] * dot| + |bias[n]|.  q and
+ * scale_a (the quantized rows, [M,K] and [M]) are written too. */
 void oracle_acc4_matmul(const float* a, int64_t M, int64_t K, const uint8_t* packed,
                         const double* scales, const uint8_t* zero_points, int64_t N, int64_t g,
                         const float* bias, double* Y, double* Bnd, int8_t* q, float* scale_a)
@@ -419,7 +422,7 @@ void oracle_acc4_matmul(const float* a, int64_t M, int64_t K, const uint8_t* pac
         for (int64_t n = 0; n < N; ++n) {
             const double b = bias ? (double)bias[n] : 0.0;
             const double sa = (double)scale_a[m];
-            double y = 0.0, bnd = 0.0;
+            double inner = 0.0, mag = 0.0;
             if (sa != 0.0) {
                 for (int64_t blk = 0; blk < kb; ++blk) {
                     const int zp = oracle_zero_point(zero_points, n, blk, kb);
@@ -427,13 +430,14 @@ void oracle_acc4_matmul(const float* a, int64_t M, int64_t K, const uint8_t* pac
                     const int64_t end = (blk + 1) * g < K ? (blk + 1) * g : K;
                     for (int64_t k = blk * g; k < end; ++k)
                         dot += (int64_t)q[m * K + k] * (oracle_code(packed, n, k, K, g) - zp);
-                    const double term = sa * scales[n * kb + blk] * (double)dot;
-                    y += term;
-                    bnd += fabs(term);
+                    const double term = scales[n * kb + blk] * (double)dot;
+                    inner += term;
+                    mag += fabs(term);
                 }
             }
+            const double y = sa != 0.0 ? sa * inner : 0.0;
             Y[m * N + n] = y + b;
-            Bnd[m * N + n] = bnd + fabs(b);
+            Bnd[m * N + n] = (sa != 0.0 ? fabs(sa) * mag : 0.0) + fabs(b);
         }
     }
 }

@@ -385,6 +385,17 @@ def pin_acc4_matmul():
         A[1] = 0
         Y, B, q, sc = o.acc4_matmul(A, packed, np.ones((N, kb), np.float32), zpk, N, K, g, bias)
         assert sc[1] == 0 and (Y[1] == bias).all() and (B[1] == np.abs(bias)).all()
+        # an infinite activation: the row's scale is infinite, its inverse 0,
+        # so the finite entries get code 0 and the infinity (inf * 0 = NaN,
+        # clamped) -127; the block sum times the infinite scale is an infinity
+        # of the sum's sign
+        Ai = np.zeros((1, K), np.float32)
+        Ai[0, 0], Ai[0, 1] = np.inf, 5.0
+        ones = np.full((1, K), 9, np.uint8)
+        Y1, B1, q1, sc1 = o.acc4_matmul(Ai, o.pack_codes(ones, g), np.ones((1, kb), np.float32), None, 1,
+                                        K, g, None)
+        assert np.isinf(sc1[0]) and q1[0, 0] == -127 and (q1[0, 1:] == 0).all()
+        assert Y1[0, 0] == -np.inf
         # general scales and activations: within the rounding of the codes of
         # the unquantized product
         scales = rng.uniform(0.005, 0.02, (N, kb)).astype(np.float32)
@@ -507,8 +518,8 @@ MUTANTS = {
     "int8 scale max/128": ("max_abs / 127.0f", "max_abs / 128.0f"),
     "int8 clamp at -128": ("fmaxf(-127.0f, x)", "fmaxf(-128.0f, x)"),
     "int8 dot without zero point": ("(oracle_code(packed, n, k, K, g) - zp)", "oracle_code(packed, n, k, K, g)"),
-    "int8 product without activation scale": ("const double term = sa * scales", "const double term = scales"),
-    "int8 weight scale of block 0": ("sa * scales[n * kb + blk]", "sa * scales[n * kb]"),
+    "int8 product without activation scale": ("const double y = sa != 0.0 ? sa * inner", "const double y = sa != 0.0 ? inner"),
+    "int8 weight scale of block 0": ("const double term = scales[n * kb + blk]", "const double term = scales[n * kb]"),
     "int8 bias dropped": ("Y[m * N + n] = y + b;", "Y[m * N + n] = y;"),
     "int8 last k of each block dropped": ("(blk + 1) * g < K ? (blk + 1) * g : K", "(blk + 1) * g - 1"),
 }
