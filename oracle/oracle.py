@@ -48,7 +48,10 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
+    # rebuilt when missing or older than its source, so a test never runs a
+    # stale oracle
+    if not os.path.exists(_LIB_PATH) or (os.path.exists(_SRC) and
+                                         os.path.getmtime(_SRC) > os.path.getmtime(_LIB_PATH)):
         build(force=True)
     lib = ctypes.CDLL(_LIB_PATH)
     p = ctypes.c_void_p
