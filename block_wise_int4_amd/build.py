@@ -15,7 +15,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB_DIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIB_DIR, "libmnb.so")
 
-SOURCES = ["mnb_api.cpp", "repack.hip", "act_order.hip", "gemv.hip", "gemm_small.hip", "gemm_mfma.hip"]
+SOURCES = ["mnb_api.cpp", "repack.hip", "act_order.hip", "gemv.hip", "gemm_small.hip", "gemm_mfma.hip",
+           "acc4.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

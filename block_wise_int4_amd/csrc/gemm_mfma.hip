@@ -34,6 +34,7 @@
 #include <type_traits>
 
 #include "mnb_device.hpp"
+#include "mnb_acc4.hpp"
 #include "mnb_internal.hpp"
 
 namespace mnb {
@@ -67,6 +68,11 @@ struct GemmParams {
     const __half* bias;    // optional, element (m, n) at bias[m * bias_stride + n]
     int64_t bias_stride;
     int bias_after_round;
+    // int8-activation codes as A: fp32 output y32[m, n] = row_scale[m] *
+    // acc (+ bias32[n]) in place of the fp16 output (row_scale non-null)
+    float* y32;
+    const float* row_scale;
+    const float* bias32;
     int M, N, K, C;
     int T;                 // column tiles
     int num_m, num_n;      // workgroup grid
@@ -512,6 +518,37 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
 
     // ---- epilogue: lane holds column (lane & 31) of each 32x32 block, rows
     // 8*(e/4) + 4*oct + e%4
+    if (p.row_scale) {
+        // fp32 outputs: the row's activation scale, then the bias; the
+        // lane's row scales are loaded before any is used
+        float rs[RB][16];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                int m = m0 + rb * 32 + 8 * (e >> 2) + 4 * oct + (e & 3);
+                m = m < p.M ? m : p.M - 1;
+                rs[rb][e] = p.row_scale[m];
+            }
+#pragma unroll
+        for (int q = 0; q < PAIRS; ++q) {
+            const int n = nb * BN + wave * 64 + q * 32 + (lane & 31);
+            if (n >= p.N) continue;
+            const float b = p.bias32 ? p.bias32[n] : 0.0f;
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int m = m0 + rb * 32 + 8 * (e >> 2) + 4 * oct + (e & 3);
+                    if (m < p.M) {
+                        float v = rs[rb][e] != 0.0f ? acc[rb][q][e] * rs[rb][e] : 0.0f;
+                        if (p.bias32) v = v + b;
+                        p.y32[(int64_t)m * p.N + n] = v;
+                    }
+                }
+        }
+        return;
+    }
     if (p.bias && p.bias_stride == 0) {
         // one bias vector for every row: the lane's two columns only
         float bq[PAIRS];
@@ -613,6 +650,9 @@ hipError_t launch_gemm_mfma(const Layout& L, const WeightView& w, const void* a,
                             const Bias& bias, void* y, hipStream_t stream, const char** variant)
 {
     GemmParams p;
+    p.y32 = nullptr;
+    p.row_scale = nullptr;
+    p.bias32 = nullptr;
     p.w = w.codes;   // the codes section starts the repacked buffer
     p.scales_off = L.scales_off;
     p.zp_off = L.zp_off;
@@ -630,6 +670,36 @@ hipError_t launch_gemm_mfma(const Layout& L, const WeightView& w, const void* a,
     p.num_m = (int)((m + BM - 1) / BM);
     p.num_n = (int)((L.N + BN - 1) / BN);
     if (variant) *variant = "gemm_mfma_32x32x16";
+    if (L.ss == 2)
+        return L.has_zp ? launch_q<__half, true>(L, p, stream) : launch_q<__half, false>(L, p, stream);
+    return L.has_zp ? launch_q<float, true>(L, p, stream) : launch_q<float, false>(L, p, stream);
+}
+
+hipError_t launch_gemm_mfma_f32(const Layout& L, const WeightView& w, const void* a16, int64_t m,
+                                const float* row_scale, const float* bias, float* y, hipStream_t stream,
+                                const char** variant)
+{
+    GemmParams p;
+    p.w = w.codes;
+    p.scales_off = L.scales_off;
+    p.zp_off = L.zp_off;
+    p.w_bytes = (uint32_t)L.total;
+    p.a = static_cast<const _Float16*>(a16);
+    p.y = nullptr;
+    p.bias = nullptr;
+    p.bias_stride = 0;
+    p.bias_after_round = 0;
+    p.y32 = y;
+    p.row_scale = row_scale;
+    p.bias32 = bias;
+    p.M = (int)m;
+    p.N = (int)L.N;
+    p.K = (int)L.K;
+    p.C = (int)L.C;
+    p.T = (int)L.T;
+    p.num_m = (int)((m + BM - 1) / BM);
+    p.num_n = (int)((L.N + BN - 1) / BN);
+    if (variant) *variant = "gemm_mfma_32x32x16_accuracy4";
     if (L.ss == 2)
         return L.has_zp ? launch_q<__half, true>(L, p, stream) : launch_q<__half, false>(L, p, stream);
     return L.has_zp ? launch_q<float, true>(L, p, stream) : launch_q<float, false>(L, p, stream);

@@ -16,6 +16,7 @@
 // zero), loaded straight from global memory and reused across the tiles.
 // Waves then reduce through LDS in a fixed order.
 #include "mnb_device.hpp"
+#include "mnb_acc4.hpp"
 #include "mnb_internal.hpp"
 
 namespace mnb {
@@ -33,6 +34,11 @@ struct SmallParams {
     const __half* bias;    // optional, element (m, n) at bias[m * bias_stride + n]
     int64_t bias_stride;
     int bias_after_round;
+    // int8-activation codes as A: fp32 output y32[m, n] = row_scale[m] *
+    // acc (+ bias32[n]) in place of the fp16 output (row_scale non-null)
+    float* y32;
+    const float* row_scale;
+    const float* bias32;
     int M, N, K, C;
     int64_t T;
 };
@@ -180,8 +186,15 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_small_kernel(SmallParams p)
             float v = 0.0f;
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) v += red[w][tt][e];
-            p.y[(int64_t)row * p.N + n] = finish_output(v, p.bias, (int64_t)row * p.bias_stride + n,
-                                                        p.bias_after_round);
+            if (p.row_scale) {
+                const float rs = p.row_scale[row];
+                float o = rs != 0.0f ? v * rs : 0.0f;
+                if (p.bias32) o = o + p.bias32[n];
+                p.y32[(int64_t)row * p.N + n] = o;
+            } else {
+                p.y[(int64_t)row * p.N + n] = finish_output(v, p.bias, (int64_t)row * p.bias_stride + n,
+                                                            p.bias_after_round);
+            }
         }
     }
 }
@@ -213,6 +226,9 @@ hipError_t launch_gemm_small(const Layout& L, const WeightView& w, const void* a
                              const Bias& bias, void* y, void*, hipStream_t stream, const char** variant)
 {
     SmallParams p;
+    p.y32 = nullptr;
+    p.row_scale = nullptr;
+    p.bias32 = nullptr;
     p.codes = reinterpret_cast<const u4_t*>(w.codes);
     p.scales = w.scales;
     p.zp = w.zp;
@@ -227,6 +243,33 @@ hipError_t launch_gemm_small(const Layout& L, const WeightView& w, const void* a
     p.C = (int)L.C;
     p.T = L.T;
     if (variant) *variant = "gemm_small_m";
+    if (L.ss == 2)
+        return L.has_zp ? launch_q<__half, true>(L, p, stream) : launch_q<__half, false>(L, p, stream);
+    return L.has_zp ? launch_q<float, true>(L, p, stream) : launch_q<float, false>(L, p, stream);
+}
+
+hipError_t launch_gemm_small_f32(const Layout& L, const WeightView& w, const void* a16, int64_t m,
+                                 const float* row_scale, const float* bias, float* y, void*,
+                                 hipStream_t stream, const char** variant)
+{
+    SmallParams p;
+    p.codes = reinterpret_cast<const u4_t*>(w.codes);
+    p.scales = w.scales;
+    p.zp = w.zp;
+    p.a = static_cast<const _Float16*>(a16);
+    p.y = nullptr;
+    p.bias = nullptr;
+    p.bias_stride = 0;
+    p.bias_after_round = 0;
+    p.y32 = y;
+    p.row_scale = row_scale;
+    p.bias32 = bias;
+    p.M = (int)m;
+    p.N = (int)L.N;
+    p.K = (int)L.K;
+    p.C = (int)L.C;
+    p.T = L.T;
+    if (variant) *variant = "gemm_small_m_accuracy4";
     if (L.ss == 2)
         return L.has_zp ? launch_q<__half, true>(L, p, stream) : launch_q<__half, false>(L, p, stream);
     return L.has_zp ? launch_q<float, true>(L, p, stream) : launch_q<float, false>(L, p, stream);

@@ -15,6 +15,7 @@
 #include <vector>
 
 #include "../../include/mnb.h"
+#include "mnb_acc4.hpp"
 #include "mnb_internal.hpp"
 
 using mnb::Layout;
@@ -388,6 +389,62 @@ mnb_status mnb_gemm_act_order(const mnb_weight_desc* w, const void* repacked, co
     if (e != hipSuccess) return launched(e, "act_order_permute");
     return gemm_common(w, repacked, workspace, m, a_dtype, mnb::Bias(), y,
                        static_cast<unsigned char*>(workspace) + a_bytes, workspace_bytes - a_bytes, stream);
+}
+
+// int8 activations (accuracy_level 4): the workspace holds the activation
+// scales (fp32 [M]) at offset 0 and the codes (fp16 integers [M, K]) at the
+// next 256-byte boundary, then the small-M GEMM's own workspace.
+static size_t acc4_scale_bytes(int64_t m) { return (size_t)((4 * m + 255) / 256 * 256); }
+static size_t acc4_codes_bytes(const Layout& L, int64_t m) { return (size_t)((2 * m * L.K + 255) / 256 * 256); }
+
+size_t mnb_gemm_accuracy4_workspace_bytes(const mnb_weight_desc* w, int64_t m)
+{
+    Layout L;
+    if (check_desc(w, &L) != MNB_OK) return 0;
+    if (m < 0 || (L.K > 0 && m > INT64_MAX / 4 / L.K)) return 0;
+    g_error.clear();
+    return acc4_scale_bytes(m) + acc4_codes_bytes(L, m) + workspace_for(L, m);
+}
+
+mnb_status mnb_gemm_accuracy4(const mnb_weight_desc* w, const void* repacked, const float* a, int64_t m,
+                              const float* bias, float* y, void* workspace, size_t workspace_bytes,
+                              void* stream)
+{
+    Layout L;
+    MNB_TRY(check_desc(w, &L));
+    if (m < 0) return fail(MNB_ERR_INVALID_ARGUMENT, "M must be >= 0 (got %lld)", (long long)m);
+    if (m > INT32_MAX) return fail(MNB_ERR_INVALID_ARGUMENT, "M must fit in 32 bits");
+    if (m == 0 || L.N == 0) return ok("noop");
+    if (m > INT64_MAX / 4 / L.K) return fail(MNB_ERR_INVALID_ARGUMENT, "M*K overflows");
+    if (m == 1 && L.K > mnb::acc4_gemv_max_k())
+        return fail(MNB_ERR_UNSUPPORTED, "K=%lld exceeds the int8-activation decode limit %lld",
+                    (long long)L.K, (long long)mnb::acc4_gemv_max_k());
+    const size_t need = acc4_scale_bytes(m) + acc4_codes_bytes(L, m) + workspace_for(L, m);
+    // the decode GEMV needs no workspace; given one, it receives the codes
+    if ((m > 1 || workspace) && workspace_bytes < need)
+        return fail(MNB_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed",
+                    workspace_bytes, need);
+    if (m > 1 || workspace) MNB_TRY(check_ptr(workspace, 256, "workspace"));
+    MNB_TRY(check_ptr(repacked, 256, "repacked"));
+    MNB_TRY(check_ptr(a, 16, "a"));
+    MNB_TRY(check_ptr(y, 4, "y"));
+    if (bias) MNB_TRY(check_ptr(bias, 4, "bias"));
+    MNB_TRY(check_device());
+    const mnb::WeightView v = mnb::view_of(L, repacked);
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    float* sc = reinterpret_cast<float*>(ws);
+    _Float16* q = ws ? reinterpret_cast<_Float16*>(ws + acc4_scale_bytes(m)) : nullptr;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const char* variant = "";
+    if (m == 1) return launched(mnb::launch_acc4_gemv(L, v, a, bias, y, q, sc, s, &variant), variant);
+    hipError_t e = mnb::launch_acc4_quantize(a, m, L.K, q, sc, s);
+    if (e != hipSuccess) return launched(e, "accuracy4_quantize");
+    if (m <= 16)
+        e = mnb::launch_gemm_small_f32(L, v, q, m, sc, bias, y, ws + acc4_scale_bytes(m) + acc4_codes_bytes(L, m),
+                                       s, &variant);
+    else
+        e = mnb::launch_gemm_mfma_f32(L, v, q, m, sc, bias, y, s, &variant);
+    return launched(e, variant);
 }
 
 mnb_status mnb_unpack_debug(const mnb_weight_desc* w, const void* repacked, uint8_t* codes,

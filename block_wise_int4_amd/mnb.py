@@ -28,7 +28,7 @@ MNB_BIAS_AFTER_ROUND = 1
 EXPORTS = ("mnb_repacked_bytes", "mnb_repacked_layout", "mnb_repack", "mnb_gemv",
            "mnb_gemv_gate_up_swiglu", "mnb_gemm_workspace_bytes", "mnb_gemm", "mnb_gemm_bias",
            "mnb_act_order_permutation", "mnb_repack_act_order", "mnb_gemm_act_order_workspace_bytes",
-           "mnb_gemm_act_order",
+           "mnb_gemm_act_order", "mnb_gemm_accuracy4_workspace_bytes", "mnb_gemm_accuracy4",
            "mnb_unpack_debug", "mnb_status_string", "mnb_last_error", "mnb_last_variant")
 
 
@@ -88,6 +88,8 @@ def _load():
         "mnb_repack_act_order": (ctypes.c_int, [D, P, P, P, P, P, P]),
         "mnb_gemm_act_order_workspace_bytes": (sz, [D, i64, i32]),
         "mnb_gemm_act_order": (ctypes.c_int, [D, P, P, i64, i32, P, P, P, sz, P]),
+        "mnb_gemm_accuracy4_workspace_bytes": (sz, [D, i64]),
+        "mnb_gemm_accuracy4": (ctypes.c_int, [D, P, P, i64, P, P, P, sz, P]),
         "mnb_unpack_debug": (ctypes.c_int, [D, P, P, P, P]),
         "mnb_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "mnb_last_error": (ctypes.c_char_p, []),
@@ -242,6 +244,19 @@ def mnb_gemm_act_order(w: mnb_weight_desc, repacked: Ptr, a, m: int, perm: Ptr, 
         workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else \
             workspace.numel() * workspace.element_size()
     _check(lib.mnb_gemm_act_order(ctypes.byref(w), _ptr(repacked), _ptr(a), m, dt, _ptr(perm), _ptr(y),
+                                  _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def mnb_gemm_accuracy4_workspace_bytes(w: mnb_weight_desc, m: int) -> int:
+    return int(lib.mnb_gemm_accuracy4_workspace_bytes(ctypes.byref(w), m))
+
+
+def mnb_gemm_accuracy4(w: mnb_weight_desc, repacked: Ptr, a, m: int, bias, y, workspace: Ptr = None,
+                       workspace_bytes: Optional[int] = None, stream=None) -> None:
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None or isinstance(workspace, int) else \
+            workspace.numel() * workspace.element_size()
+    _check(lib.mnb_gemm_accuracy4(ctypes.byref(w), _ptr(repacked), _ptr(a), m, _ptr(bias), _ptr(y),
                                   _ptr(workspace), workspace_bytes, _stream(stream)))
 
 

@@ -248,6 +248,30 @@ mnb_status mnb_gemm_act_order(const mnb_weight_desc* w, const void* repacked, co
                               int32_t a_dtype, const int32_t* perm, void* y, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/* int8 activations: accuracy_level = 4 of the fp32 operator
+ * (onnx-runtime-ep-cuda 0.1.0-dev.3, src/kernels/matmul_nbits.rs, kernels
+ * matmul_nbits_accuracy4, matmul_nbits_quantize_accuracy4_block32 and
+ * matmul_nbits_gemv_accuracy4_block32).  A is fp32 [M, K] (16-byte aligned),
+ * Y fp32 [M, N]; the weight is any repacked buffer (fp16 or fp32 scales, with
+ * or without zero points).  Each row of A is quantized with one binary32
+ * scale s = max|a| / 127 (NaN skipped): q = round(clamp(a * (1/s), -127,
+ * 127)), halves away from zero, in binary32 steps; then
+ *   Y[m,n] = s[m] * sum_b scale[n,b] * sum_{k in b} q[m,k] * (code[n,k] - zp[n,b])
+ *            (+ bias[n]),
+ * the inner sums exact integers; a row with s = 0 gives bias[n] (or 0).
+ * bias: fp32 [N] or NULL.
+ *
+ * Workspace (device, 256-byte aligned), mnb_gemm_accuracy4_workspace_bytes(w,
+ * m) bytes: it receives the scales s (fp32 [M]) at offset 0 and the codes q
+ * (as fp16 integers, [M, K] row-major) at the next 256-byte boundary; the rest
+ * is the library's.  Required for M > 1; optional for M = 1 (NULL: the codes
+ * stay on chip).  M = 1 needs K <= 32768 (else MNB_ERR_UNSUPPORTED).  Errors
+ * otherwise as mnb_gemm. */
+size_t mnb_gemm_accuracy4_workspace_bytes(const mnb_weight_desc* w, int64_t m);
+mnb_status mnb_gemm_accuracy4(const mnb_weight_desc* w, const void* repacked, const float* a, int64_t m,
+                              const float* bias, float* y, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /* Test-only: decode a repacked buffer with the production unpack code.
  * codes: device u8 [N,K] (the stored nibbles); w_f32: device f32 [N,K], the
  * dequantized weights (code - zp) * scale rounded once to fp32.  Either

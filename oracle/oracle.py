@@ -308,14 +308,20 @@ def acc4_matmul(A, packed, scales, zp, N: int, K: int, g: int, bias=None) -> tup
 
 def acc4_bound(Bnd, K: int, g: int) -> np.ndarray:
     """Tolerance of a binary32 evaluation of the int8-activation product, a
-    reading (the stated tolerance is for fp16 arithmetic): every integer block
-    dot is exact, so the only errors are binary32 roundings -- one per block
-    term (dot * scale, or dot * (scale_a * scale): two), the additions of the
-    k_blocks terms in any order, the product with the activation scale and the
-    bias addition: at most (k_blocks + 4) units of 2^-24 of Bnd, plus one
-    smallest subnormal per term for results below the normal range."""
+    reading (the stated tolerance is for fp16 arithmetic).  Every product and
+    every sum of products within a block is an integer below 2^24, exact in
+    binary32; the errors are the roundings of running values, each at most
+    2^-24 of a partial total, itself at most Bnd.  The evaluation with the
+    most of them keeps one accumulator in units of the current block's scale:
+    one rounding per 16-k partial sum added to it, two per block for the
+    change of units (the ratio of scales and the product), then the last
+    block's scale, the activation scale and the bias: k_blocks*(g/16 + 2) + 4
+    roundings, which also covers one rounding per block term (the pages' two
+    binary32 orders).  Plus one smallest subnormal per rounding for results
+    below the normal range."""
     kb = k_blocks(K, g)
-    return (kb + 4) * 2.0 ** -24 * np.asarray(Bnd, np.float64) + (kb + 2) * 2.0 ** -149
+    n = kb * (g // 16 + 2) + 4
+    return n * 2.0 ** -24 * np.asarray(Bnd, np.float64) + n * 2.0 ** -149
 
 
 # ---- acceptance ------------------------------------------------------------

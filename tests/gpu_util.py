@@ -68,7 +68,8 @@ def assert_within(y: np.ndarray, Y: np.ndarray, B: np.ndarray, what: str, bound=
     else:
         tol = bound
         with np.errstate(invalid="ignore"):
-            ok = (np.abs(y - Y) <= tol) | (np.isnan(y) & np.isnan(Y))
+            ok = ((np.abs(y - Y) <= tol) | (np.isnan(y) & np.isnan(Y)) |
+                  (np.isinf(y) & np.isinf(Y) & (np.sign(y) == np.sign(Y))))
     if not ok.all():
         bad = np.argwhere(~ok)
         lines = []

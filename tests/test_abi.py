@@ -19,7 +19,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 def _declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mnb_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(mnb_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_every_declared_symbol_is_exported():
@@ -27,7 +27,7 @@ def test_every_declared_symbol_is_exported():
     assert set(declared) == set(mnb.EXPORTS), declared
     out = subprocess.run(["nm", "-D", "--defined-only", mnb.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
-    exported = set(re.findall(r"\bT (mnb_[a-z_]+)\b", out))
+    exported = set(re.findall(r"\bT (mnb_[a-z0-9_]+)\b", out))
     for name in declared:
         assert name in exported, name
         assert hasattr(mnb.lib, name)
@@ -216,6 +216,32 @@ def test_act_order_argument_validation():
     assert "not a multiple" in _expect(U, lib.mnb_repack_act_order, D(r), FAKE, FAKE, FAKE, FAKE, FAKE, None)
     assert "not a multiple" in _expect(U, lib.mnb_gemm_act_order, D(r), FAKE, FAKE, 1, 1, FAKE, FAKE, FAKE,
                                        1 << 30, None)
+
+
+def test_accuracy4_argument_validation():
+    lib = mnb.lib
+    d = mnb.desc(64, 256, 32, True, mnb.MNB_F32)
+    E, U = mnb.MNB_ERR_INVALID_ARGUMENT, mnb.MNB_ERR_UNSUPPORTED
+    need = lib.mnb_gemm_accuracy4_workspace_bytes(D(d), 40)
+    # scales [40] fp32 in the first 256 bytes, then the codes [40, 256] fp16
+    assert need >= 256 + 40 * 256 * 2
+    assert lib.mnb_gemm_accuracy4_workspace_bytes(D(d), 1) >= 256 + 256 * 2
+    assert "workspace" in _expect(E, lib.mnb_gemm_accuracy4, D(d), FAKE, FAKE, 40, None, FAKE, FAKE,
+                                  need - 1, None)
+    assert "workspace is NULL" in _expect(E, lib.mnb_gemm_accuracy4, D(d), FAKE, FAKE, 40, None, FAKE,
+                                          None, need, None)
+    assert "M must be" in _expect(E, lib.mnb_gemm_accuracy4, D(d), FAKE, FAKE, -1, None, FAKE, FAKE,
+                                  need, None)
+    # a workspace given at M = 1 must be large enough too
+    n1 = lib.mnb_gemm_accuracy4_workspace_bytes(D(d), 1)
+    assert "workspace" in _expect(E, lib.mnb_gemm_accuracy4, D(d), FAKE, FAKE, 1, None, FAKE, FAKE,
+                                  n1 - 1, None)
+    big = mnb.desc(64, 32768 + 128, 128, False, mnb.MNB_F32)
+    assert "decode limit" in _expect(U, lib.mnb_gemm_accuracy4, D(big), FAKE, FAKE, 1, None, FAKE, None,
+                                     0, None)
+    assert "a must be 16-byte aligned" in _expect(E, lib.mnb_gemm_accuracy4, D(d), FAKE, FAKE + 4, 1,
+                                                  None, FAKE, None, 0, None)
+    assert lib.mnb_gemm_accuracy4(D(d), None, None, 0, None, None, None, 0, None) == mnb.MNB_OK
 
 
 def test_empty_problems_are_noops_without_a_device():

@@ -465,10 +465,10 @@ def test_acc4_bound_covers_the_pages_binary32_orders():
         y2 = v2 + bias
         tol = o.acc4_bound(B[0], K, g)
         assert (np.abs(y1 - Y[0]) <= tol).all() and (np.abs(y2 - Y[0]) <= tol).all()
-        # a hundred times tighter than the fp16 path's rule (1e-3 of Bnd): a
-        # wrong code moves an output by a few such bounds at most, which is
-        # why the GPU's codes are compared bit for bit on their own
-        assert (tol <= 1e-5 * B[0] + 1e-30).all()
+        # at least 25 times tighter than the fp16 path's rule (1e-3 of Bnd):
+        # a wrong code can hide inside it, which is why the GPU's codes are
+        # compared bit for bit on their own
+        assert (tol <= 4e-5 * B[0] + 1e-30).all()
 
 
 def test_oracle_decodes_the_synthetic_workloads():
