@@ -39,7 +39,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--only", default="",
-                   help="comma list of: gemv,gate_up,down,small_m,prefill,bias,act_order (default all); "
+                   help="comma list of: gemv,gate_up,down,small_m,prefill,bias,act_order,accuracy4 (default all); "
                         "copy adds a plain 256 MiB device copy, the reference kernel "
                         "for scaling the HBM byte counters")
     return p.parse_args()
@@ -87,7 +87,7 @@ class Workload:
     """R rotating device copies of one workload's operands."""
 
     def __init__(self, name, M, weights, K, N, g, act_fp16=True, sigma=1.0, seed=(0,), bias=None,
-                 act_order=False):
+                 act_order=False, accuracy4=False):
         import torch
         from block_wise_int4_amd import mnb, synth
         self.name, self.M, self.K, self.N, self.g = name, M, K, N, g
@@ -126,9 +126,12 @@ class Workload:
             self.bytes += bias_rows * N * 2
         if act_order:
             self.bytes += K * 4                       # the group indices
+        self.accuracy4 = accuracy4
+        if accuracy4:
+            self.bytes += N * 4                       # the fp32 bias
         self.flops = 2 * M * N * K * len(weights)
-        per_copy = (sum(q.repacked.numel() for q in qs) + A.numel() * A.element_size() * 2 + M * N * 2
-                    + bias_rows * N * 2)
+        per_copy = (sum(q.repacked.numel() for q in qs) + A.numel() * A.element_size() * 2
+                    + M * N * A.element_size() + bias_rows * N * 2)
         self.R = max(2, -(-COLD_BYTES // per_copy))
         self.desc = qs[0].desc
         self.copies = []
@@ -137,13 +140,16 @@ class Workload:
             a = A.clone()
             y = torch.empty((M, N), dtype=A.dtype, device=dev)
             b = None
-            if bias_rows:
+            if bias_rows or accuracy4:
                 gen = torch.Generator().manual_seed(1000 + r)
-                b = torch.randn(bias_rows * N, generator=gen).to(A.dtype).to(dev)
+                b = torch.randn(max(bias_rows, 1) * N, generator=gen).to(A.dtype).to(dev)
             self.copies.append((ws, a, y, b))
         self.ws_bytes = mnb.mnb_gemm_workspace_bytes(self.desc, M) if len(qs) == 1 else 0
         if act_order:
             self.ws_bytes = mnb.mnb_gemm_act_order_workspace_bytes(self.desc, M)
+        if accuracy4:
+            # the decode call keeps the codes on chip (no workspace)
+            self.ws_bytes = mnb.mnb_gemm_accuracy4_workspace_bytes(self.desc, M) if M > 1 else 0
         self.workspaces = [torch.zeros(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
                            for _ in range(self.R)]
         torch.cuda.synchronize()
@@ -156,6 +162,9 @@ class Workload:
         for r, (ws, a, y, b) in enumerate(self.copies):
             if self.fused:
                 mnb.mnb_gemv_gate_up_swiglu(self.desc, ws[0], ws[1], a, y)
+            elif self.accuracy4:
+                mnb.mnb_gemm_accuracy4(self.desc, ws[0], a, self.M, b, y,
+                                       self.workspaces[r] if self.ws_bytes else None, self.ws_bytes)
             elif self.perm is not None:
                 mnb.mnb_gemm_act_order(self.desc, ws[0], a, self.M, self.perm, y, self.workspaces[r],
                                        self.ws_bytes)
@@ -212,7 +221,8 @@ CopyWorkload.finish = Workload.finish
 # shared headers): a counter summary applies only while these are unchanged.
 CSRC = os.path.join(ROOT, "block_wise_int4_amd", "csrc")
 SHARED_HEADERS = ["mnb_device.hpp", "mnb_layout.hpp", "mnb_internal.hpp"]
-VARIANT_SOURCE = {"gemv": "gemv.hip", "gemm_small": "gemm_small.hip", "gemm_mfma": "gemm_mfma.hip"}
+VARIANT_SOURCE = {"gemv_accuracy4": "acc4.hip", "gemv": "gemv.hip", "gemm_small": "gemm_small.hip",
+                  "gemm_mfma": "gemm_mfma.hip"}
 
 
 def kernel_source_sha(variant):
@@ -248,7 +258,7 @@ def counted_traffic(workload, variant):
 def build_workloads(only):
     from block_wise_int4_amd import synth as S
     sel = set(x for x in only.split(",") if x) or {"gemv", "gate_up", "down", "small_m", "prefill", "bias",
-                                                   "act_order"}
+                                                   "act_order", "accuracy4"}
     wl = [CopyWorkload()] if "copy" in sel else []
     if "gemv" in sel:
         c = S.DECODE_GEMV
@@ -279,6 +289,10 @@ def build_workloads(only):
         wl.append(Workload(c.name + " + bias [N] fp16(fp16(acc)+b)", c.M, [S.workload_weights(c)],
                            c.K, c.N, c.group, sigma=c.sigma, seed=c.seed + (c.M,),
                            bias=("vector", mnb.MNB_BIAS_AFTER_ROUND)))
+    if "accuracy4" in sel:
+        for c in (S.ACC4_DECODE, S.ACC4_PREFILL):
+            wl.append(Workload(c.name + " + bias", c.M, [S.workload_weights(c)], c.K, c.N, c.group,
+                               act_fp16=False, seed=c.seed + (c.M,), accuracy4=True))
     if "act_order" in sel:
         c = S.DECODE_GEMV
         wl.append(Workload(c.name + " act-order", 1, [S.workload_weights(c)], c.K, c.N, c.group,

@@ -185,7 +185,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void acc4_gemv_kernel(Acc4Params p)
 #pragma unroll
     for (int u = 0; u < kAV; ++u) {
         const int v = tid + u * bd;
-        av[u] = a4[v < nvk ? v : 0];
+        if (u == 0 || u * bd < nvk) av[u] = a4[v < nvk ? v : 0];   // workgroup-uniform test
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -323,8 +323,12 @@ __global__ __launch_bounds__(kMaxWaves * 64) void acc4_gemv_kernel(Acc4Params p)
 }
 
 // M > 1: one workgroup per row.  The row's maximum, then its codes, written
-// as fp16 integers (exact: |q| <= 127) for the fp16 matrix-core GEMMs.
+// as fp16 integers (exact: |q| <= 127) for the fp16 matrix-core GEMMs.  A
+// thread requests up to kQV of its row's 4-activation vectors at once and
+// keeps them in registers, so the row is read once (longer rows read the
+// rest again for the codes).
 constexpr int kQuantThreads = 256;
+constexpr int kQV = 8;
 
 __global__ __launch_bounds__(kQuantThreads) void acc4_quantize_kernel(const float* __restrict__ a,
                                                                       _Float16* __restrict__ q,
@@ -335,10 +339,21 @@ __global__ __launch_bounds__(kQuantThreads) void acc4_quantize_kernel(const floa
     const f4_t* row = reinterpret_cast<const f4_t*>(a + m * K);
     const int nvk = (int)(K / 4);
     const int tid = threadIdx.x;
+    f4_t x[kQV];
+#pragma unroll
+    for (int u = 0; u < kQV; ++u) {
+        const int v = tid + u * kQuantThreads;
+        if (u == 0 || u * kQuantThreads < nvk) x[u] = row[v < nvk ? v : 0];   // workgroup-uniform test
+    }
     float mx = 0.0f;
-    for (int v = tid; v < nvk; v += kQuantThreads) {
-        const f4_t x = row[v];
-        mx = fmaxf(fmaxf(mx, fabsf(x.x)), fmaxf(fabsf(x.y), fmaxf(fabsf(x.z), fabsf(x.w))));
+#pragma unroll
+    for (int u = 0; u < kQV; ++u) {
+        if (tid + u * kQuantThreads < nvk)
+            mx = fmaxf(fmaxf(mx, fabsf(x[u].x)), fmaxf(fabsf(x[u].y), fmaxf(fabsf(x[u].z), fabsf(x[u].w))));
+    }
+    for (int v = tid + kQV * kQuantThreads; v < nvk; v += kQuantThreads) {
+        const f4_t y = row[v];
+        mx = fmaxf(fmaxf(mx, fabsf(y.x)), fmaxf(fabsf(y.y), fmaxf(fabsf(y.z), fabsf(y.w))));
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
@@ -351,17 +366,22 @@ __global__ __launch_bounds__(kQuantThreads) void acc4_quantize_kernel(const floa
     const float inv = s == 0.0f ? 0.0f : 1.0f / s;
     typedef _Float16 hv4_t __attribute__((ext_vector_type(4)));
     hv4_t* out = reinterpret_cast<hv4_t*>(q + m * K);
-    for (int v = tid; v < nvk; v += kQuantThreads) {
-        const f4_t x = row[v];
+    auto codes4 = [&](const f4_t& y) {
         hv4_t o = {(_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
         if (s != 0.0f) {
-            o[0] = (_Float16)quant1(x.x, inv);
-            o[1] = (_Float16)quant1(x.y, inv);
-            o[2] = (_Float16)quant1(x.z, inv);
-            o[3] = (_Float16)quant1(x.w, inv);
+            o[0] = (_Float16)quant1(y.x, inv);
+            o[1] = (_Float16)quant1(y.y, inv);
+            o[2] = (_Float16)quant1(y.z, inv);
+            o[3] = (_Float16)quant1(y.w, inv);
         }
-        out[v] = o;
+        return o;
+    };
+#pragma unroll
+    for (int u = 0; u < kQV; ++u) {
+        const int v = tid + u * kQuantThreads;
+        if (v < nvk) out[v] = codes4(x[u]);
     }
+    for (int v = tid + kQV * kQuantThreads; v < nvk; v += kQuantThreads) out[v] = codes4(row[v]);
     if (tid == 0) sc[m] = s;
 }
 

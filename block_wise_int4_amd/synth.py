@@ -60,6 +60,13 @@ PREFILL_GEMM = Workload("prefill GEMM M=2048 K=4096 N=14336 g=128 f16 asym-zp", 
 # skinny, K > N), the step after the fused gate/up.
 DOWN_PROJ_GEMV = Workload("down-projection GEMV M=1 K=11008 N=4096 g=128 f16", 1, 11008, 4096, 128,
                           "f16", "f16", (0.002, 0.01), False, seed=(6,))
+# Int8 activations (accuracy_level 4): fp32 activations, scales and outputs;
+# the decode shape with block 32 and no zero points (the symmetric form the
+# pages give their own int8 GEMV), and the prefill shape.
+ACC4_DECODE = Workload("int8-activation decode GEMV M=1 K=4096 N=4096 g=32 f32 sym", 1, 4096, 4096, 32,
+                       "f32", "f32", (0.005, 0.02), False, seed=(7,))
+ACC4_PREFILL = Workload("int8-activation prefill GEMM M=2048 K=4096 N=14336 g=128 f32 asym-zp", 2048, 4096,
+                        14336, 128, "f32", "f32", (0.002, 0.01), True, seed=(8,))
 SMALL_M_VALUES = (2, 4, 8, 16)
 
 
