@@ -126,6 +126,21 @@ def test_accuracy4_special_rows(mnb):
     _check(mnb, w, big, bias, "accuracy4 special rows (prefill GEMM)")
 
 
+def test_accuracy4_decode_at_maximum_k(mnb):
+    """The decode kernel's largest K (32768 codes in LDS) with 16-wide blocks
+    (the most zero-point sums), then one chunk more is refused."""
+    N, K, g = 40, 32768, 16
+    w = _weight(N, K, g, "f32", True, seed=13)
+    A = synth.activation(1, K, "f32", 1.0, (315, K))
+    _check(mnb, w, A, None, "accuracy4 decode at K=%d" % K)
+    t = G.torch()
+    big = synth.weight(N, K + 128, 128, "f32", (0.005, 0.02), False, (316,))
+    q = G.upload(big)
+    y = t.empty((1, N), dtype=t.float32, device="cuda")
+    with pytest.raises(mnb.MnbError, match="decode limit"):
+        mnb.mnb_gemm_accuracy4(q.desc, q.repacked, G.to_dev(np.zeros((1, K + 128), np.float32)), 1, None, y)
+
+
 def test_accuracy4_decode_without_workspace(mnb):
     """M = 1 needs no workspace; the result is the same bits as with one."""
     N, K, g = 300, 1024, 32

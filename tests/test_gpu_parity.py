@@ -164,6 +164,72 @@ def test_tiny_gemv_workload_exact_match_with_one_hot_rows(mnb):
         assert (got.view(np.uint32) == W[:, k].astype(np.float32).view(np.uint32)).all(), k
 
 
+MAX_K_CASES = [
+    # the largest K the decode GEMV stages in LDS (fp16 and fp32 activations),
+    # at every group size's register path: many chunks per wave, the batch loop
+    (40, 31744, 128, "f16", False), (37, 31744, 16, "f16", True), (24, 15872, 32, "f32", True),
+]
+
+
+@pytest.mark.parametrize("N,K,g,adt,zp", MAX_K_CASES)
+def test_gemv_at_maximum_k(mnb, N, K, g, adt, zp):
+    t = G.torch()
+    limit = 31744 if adt == "f16" else 15872
+    assert K == limit
+    w = _weight(N, K, g, "f16", zp, seed=5)
+    A = _act(1, K, adt, seed=5)
+    q = G.upload(w)
+    y = t.empty(N, dtype=t.float16 if adt == "f16" else t.float32, device="cuda")
+    mnb.mnb_gemv(q.desc, q.repacked, G.to_dev(A.reshape(-1)), y)
+    Y, B, _ = G.oracle_dense(A, w)
+    G.assert_within(G.host(y)[None, :], Y, B, "GEMV at K=%d g=%d %s" % (K, g, adt))
+    # one chunk more is refused, not computed some other way
+    big = mnb.desc(N, K + 128, 128, False, mnb.MNB_F16)
+    assert mnb.lib.mnb_gemv(ctypes_byref(big), None, None, 1 if adt == "f16" else 0, None, None) == \
+        mnb.MNB_ERR_UNSUPPORTED
+
+
+def test_gate_up_and_act_order_at_maximum_k(mnb):
+    """The fused gate/up pair at the GEMV's largest K, and act order at the
+    largest K whose two staged copies fit in LDS (its in-LDS gather)."""
+    t = G.torch()
+    N, K, g = 48, 31744, 64
+    wg = _weight(N, K, g, "f16", False, seed=8, lo=0.002, hi=0.01)
+    wu = _weight(N, K, g, "f16", False, seed=9, lo=0.002, hi=0.01)
+    A = _act(1, K, "f16", seed=8)
+    qg, qu = G.upload(wg), G.upload(wu)
+    y = t.empty(N, dtype=t.float16, device="cuda")
+    mnb.mnb_gemv_gate_up_swiglu(qg.desc, qg.repacked, qu.repacked, G.to_dev(A.reshape(-1)), y)
+    Yg, Bg, _ = G.oracle_dense(A, wg)
+    Yu, Bu, _ = G.oracle_dense(A, wu)
+    G.assert_within(G.host(y)[None, :], o.swiglu(Yg, Yu), None, "gate/up at K=%d" % K,
+                    bound=o.swiglu_bound(Yg, Bg, Yu, Bu))
+    K = 15872
+    w = _weight(N, K, 128, "f16", True, seed=10)
+    rng = np.random.default_rng(11)
+    g_idx = np.empty(K, np.int32)
+    g_idx[rng.permutation(K)] = np.arange(K) // 128
+    d = mnb.desc(N, K, 128, True, mnb.MNB_F16)
+    perm_dev = G.to_dev(mnb.mnb_act_order_permutation(d, g_idx))
+    rep = t.empty(mnb.mnb_repacked_bytes(d), dtype=t.uint8, device="cuda")
+    mnb.mnb_repack_act_order(d, G.to_dev(w.packed.reshape(-1)), G.to_dev(w.scales.reshape(-1)),
+                             G.to_dev(w.zero_points.reshape(-1)), perm_dev, rep)
+    A = _act(1, K, "f16", seed=12)
+    n_ws = mnb.mnb_gemm_act_order_workspace_bytes(d, 1, mnb.MNB_F16)
+    ws = t.zeros(n_ws, dtype=t.uint8, device="cuda")
+    y = t.empty((1, N), dtype=t.float16, device="cuda")
+    mnb.mnb_gemm_act_order(d, rep, G.to_dev(A), 1, perm_dev, y, ws, n_ws)
+    assert mnb.mnb_last_variant() == "gemv_act_order_f16"
+    W = o.dequant_gidx(w.packed, w.scales, w.zero_points, g_idx, N, K, 128)
+    Y, B = o.matmul(o.decode(A.reshape(-1, K)), W)
+    G.assert_within(G.host(y), Y, B, "act order at K=%d" % K)
+
+
+def ctypes_byref(x):
+    import ctypes
+    return ctypes.byref(x)
+
+
 # ------------------------------------------------------- gate/up SwiGLU ----
 
 GATE_UP_CASES = [(11008, 4096, 128, "f16"), (4864, 896, 32, "f16"), (70, 384, 64, "f16"),
