@@ -23,7 +23,7 @@ namespace mnb {
 
 namespace {
 
-constexpr int kWaves = 8;
+constexpr int kWaves = 16;   // the K split of a workgroup: more loads in flight per CU
 
 struct SmallParams {
     const u4_t* codes;
