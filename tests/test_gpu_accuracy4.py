@@ -68,6 +68,9 @@ ACC4_CASES = [
     (16, 100, 1024, 16, "f32", True, True),
     (40, 300, 512, 64, "f32", True, True), (130, 70, 384, 128, "f16", False, False),
     (200, 513, 1024, 32, "f32", True, True),
+    # K not a multiple of the 128-k chunk: the last chunk's padding
+    (1, 70, 400, 16, "f32", True, True), (3, 70, 352, 32, "f16", True, False),
+    (33, 70, 400, 16, "f32", True, True), (1, 90, 1088, 64, "f16", False, True),
 ]
 
 

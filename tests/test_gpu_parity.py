@@ -448,6 +448,9 @@ ACT_ORDER_CASES = [
     # decode beyond the K at which the GEMV holds both copies of A in LDS:
     # the separate column permutation, then the plain GEMV
     (1, 48, 16384, 128, "f16", True), (1, 40, 8192, 64, "f32", False),
+    # K not a multiple of the 128-k chunk (the gather's padding) on every path
+    (1, 60, 400, 16, "f16", True), (1, 50, 352, 32, "f32", False), (6, 60, 400, 16, "f16", True),
+    (70, 60, 352, 32, "f16", False),
 ]
 
 
