@@ -365,6 +365,7 @@ mnb_status mnb_gemm_act_order(const mnb_weight_desc* w, const void* repacked, co
     MNB_TRY(check_act_dtype(a_dtype));
     if (m < 0) return fail(MNB_ERR_INVALID_ARGUMENT, "M must be >= 0 (got %lld)", (long long)m);
     if (m == 0 || L.N == 0) return ok("noop");
+    if (m > INT32_MAX) return fail(MNB_ERR_INVALID_ARGUMENT, "M must fit in 32 bits");
     if (L.K > 0 && m > INT64_MAX / 4 / L.K) return fail(MNB_ERR_INVALID_ARGUMENT, "M*K overflows");
     if (m > 1 && a_dtype != MNB_F16)
         return fail(MNB_ERR_UNSUPPORTED, "M>1 GEMM takes fp16 activations only");

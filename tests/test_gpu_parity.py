@@ -451,6 +451,9 @@ ACT_ORDER_CASES = [
     # K not a multiple of the 128-k chunk (the gather's padding) on every path
     (1, 60, 400, 16, "f16", True), (1, 50, 352, 32, "f32", False), (6, 60, 400, 16, "f16", True),
     (70, 60, 352, 32, "f16", False),
+    # rows longer than the LDS a workgroup gets (64 KiB): the gathering
+    # permutation instead of the row-staged one
+    (2, 24, 33280, 128, "f16", True),
 ]
 
 
