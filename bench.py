@@ -342,7 +342,7 @@ def cpu_baseline(seconds):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
+        print("bench.py measures one GPU; --gpus %d is not supported "
               "(multi-GPU sharding is a design note, not a measured path)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)

@@ -9,7 +9,7 @@ naive loops) plus the per-element acceptance rule.  All arithmetic of the
 method lives in the C file; see its header for the passages each function
 follows.  Every function here is pinned by ``tests/test_oracle.py``.
 
-Acceptance rule (the stated tolerance of the method's spec numerics):
+Acceptance rule (the method's stated tolerance):
 an output y is accepted against the fp64 oracle value Y when
 ``|y - Y| <= 1e-3 * sum_k |a_k * w_nk| + 1e-5``; NaN against NaN and equal
 infinities count as agreement (the NaN convention of ferrox-cuda gpu.rs, test
