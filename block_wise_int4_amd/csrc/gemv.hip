@@ -267,7 +267,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
 #pragma unroll
         for (int j = 0; j < kPermPre; ++j) {
             const int v = tid + j * (int)blockDim.x;
-            pidx[j] = perm_vec[v < nq ? v : 0];
+            // workgroup-uniform test: only the vectors that exist are requested
+            pidx[j] = (j == 0 || j * (int)blockDim.x < nq) ? perm_vec[v < nq ? v : 0] : u4_t{0u, 0u, 0u, 0u};
         }
     }
 
