@@ -31,6 +31,10 @@
 //   accumulator are freed for deeper prefetch and for two waves per SIMD.
 // * Workgroup ids are remapped so the tiles resident on one XCD at a time
 //   share A rows and code columns in that XCD's L2.
+// * Epilogues: fp16 outputs (with an optional fp16 bias in either rounding of
+//   matmul_nbits.rs fold_bias_f16), or, for int8 activation codes as A
+//   (accuracy_level 4), fp32 outputs times the row's activation scale plus an
+//   fp32 bias.
 #include <type_traits>
 
 #include "mnb_device.hpp"

@@ -14,7 +14,10 @@
 // 128-k chunk, unpacks it in registers to the B operand of
 // v_mfma_f32_16x16x32_f16 and multiplies it with the A rows (rows >= M are
 // zero), loaded straight from global memory and reused across the tiles.
-// Waves then reduce through LDS in a fixed order.
+// Waves then reduce through LDS in a fixed order.  The epilogue writes fp16
+// (with an optional bias in either rounding) or, for int8 activation codes
+// as A (accuracy_level 4), fp32 times the row's activation scale plus an fp32
+// bias.
 #include "mnb_device.hpp"
 #include "mnb_acc4.hpp"
 #include "mnb_internal.hpp"

@@ -13,7 +13,10 @@
 // the matrix cores multiply them with the activation staged once in LDS and
 // reduce over k; each group's fp32 partial is scaled into an fp32 sum.  fp32
 // activations take a VALU path with fp32 products instead.  Waves reduce
-// through LDS in a fixed order (results are deterministic).
+// through LDS in a fixed order (results are deterministic).  The store takes
+// an optional bias in either rounding of matmul_nbits.rs fold_bias_f16.  For
+// act-order weights (the g_idx input) the workgroup also gathers the staged
+// activation into the codes' column order in LDS before computing.
 #include <type_traits>
 
 #include "mnb_device.hpp"
