@@ -462,9 +462,11 @@ mnb_status mnb_unpack_debug(const mnb_weight_desc* w, const void* repacked, uint
                     "unpack_debug");
 }
 
-const char* mnb_status_string(mnb_status s)
+// Any value is accepted (an int at the boundary, not the enum type): unknown
+// ones give MNB_ERR_UNKNOWN.
+const char* mnb_status_string(int32_t status)
 {
-    switch (s) {
+    switch (status) {
     case MNB_OK: return "MNB_OK";
     case MNB_ERR_INVALID_ARGUMENT: return "MNB_ERR_INVALID_ARGUMENT";
     case MNB_ERR_UNSUPPORTED: return "MNB_ERR_UNSUPPORTED";

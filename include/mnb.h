@@ -280,7 +280,7 @@ mnb_status mnb_unpack_debug(const mnb_weight_desc* w, const void* repacked, uint
                             float* w_f32, void* stream);
 
 /* Static string naming a status. */
-const char* mnb_status_string(mnb_status s);
+const char* mnb_status_string(int32_t status);
 
 /* Reason for the last non-OK status returned in this thread ("" if none). */
 const char* mnb_last_error(void);
