@@ -292,15 +292,14 @@ __global__ __launch_bounds__(kMaxWaves * 64) void acc4_gemv_kernel(Acc4Params p)
     if (wave + stride >= C) {
         if (wave < C) compute_batch(cur, wave);
     } else {
-        for (int cb = wave; cb < C; cb += stride) {
-            Regs nxt[kBatch];
-            const bool more = cb + stride < C;   // wave-uniform
-            if (more) load_batch(nxt, cb + stride);
+        // two register sets in turn, unconditional (clamped) loads: the
+        // waits before each compute count only that batch's loads
+        Regs alt[kBatch];
+        for (int cb = wave; cb < C; cb += 2 * stride) {
+            load_batch(alt, cb + stride);
             compute_batch(cur, cb);
-            if (more) {
-#pragma unroll
-                for (int u = 0; u < kBatch; ++u) cur[u] = nxt[u];
-            }
+            load_batch(cur, cb + 2 * stride);
+            compute_batch(alt, cb + stride);
         }
     }
 

@@ -372,17 +372,19 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
         // one batch per wave (the common decode shapes): straight-line code
         if (wave < C) compute_batch(cur, wave);
     } else {
-        for (int cb = wave; cb < C; cb += stride) {
-            Regs nxt[NW][kBatch];
-            const bool more = cb + stride < C;   // wave-uniform
-            if (more) load_batch(nxt, cb + stride);
+        // two register sets in turn, the loop unrolled by two: the next
+        // batch is requested before the current one is computed, and no
+        // registers are copied, so the waits at the top of each compute count
+        // only that batch's loads (a copy at the back edge would make them
+        // wait for everything in flight).  The loads are unconditional
+        // (load_batch clamps chunks past the end to the last one, which the
+        // compute skips), so every path has the same loads in flight.
+        Regs alt[NW][kBatch];
+        for (int cb = wave; cb < C; cb += 2 * stride) {
+            load_batch(alt, cb + stride);
             compute_batch(cur, cb);
-            if (more) {
-#pragma unroll
-                for (int x = 0; x < NW; ++x)
-#pragma unroll
-                    for (int u = 0; u < kBatch; ++u) cur[x][u] = nxt[x][u];
-            }
+            load_batch(cur, cb + 2 * stride);
+            compute_batch(alt, cb + stride);
         }
     }
 
