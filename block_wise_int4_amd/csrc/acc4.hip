@@ -185,7 +185,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void acc4_gemv_kernel(Acc4Params p)
 #pragma unroll
     for (int u = 0; u < kAV; ++u) {
         const int v = tid + u * bd;
-        if (u == 0 || u * bd < nvk) av[u] = a4[v < nvk ? v : 0];   // workgroup-uniform test
+        // workgroup-uniform test: only the vectors that exist are requested
+        av[u] = (u == 0 || u * bd < nvk) ? a4[v < nvk ? v : 0] : f4_t{0.f, 0.f, 0.f, 0.f};
     }
     __builtin_amdgcn_sched_barrier(0);
 
@@ -342,7 +343,8 @@ __global__ __launch_bounds__(kQuantThreads) void acc4_quantize_kernel(const floa
 #pragma unroll
     for (int u = 0; u < kQV; ++u) {
         const int v = tid + u * kQuantThreads;
-        if (u == 0 || u * kQuantThreads < nvk) x[u] = row[v < nvk ? v : 0];   // workgroup-uniform test
+        // workgroup-uniform test: only the vectors that exist are requested
+        x[u] = (u == 0 || u * kQuantThreads < nvk) ? row[v < nvk ? v : 0] : f4_t{0.f, 0.f, 0.f, 0.f};
     }
     float mx = 0.0f;
 #pragma unroll
