@@ -303,6 +303,35 @@ def build_workloads(only):
     return wl
 
 
+def time_repack():
+    """The offline repack (ONNX bytes to the device layout), timed once per
+    weight apart from the metric: HIP events around 5 calls after one warm-up
+    call, on the current stream."""
+    import torch
+    from block_wise_int4_amd import mnb, synth as S
+    out = []
+    dev = torch.device("cuda:0")
+    for c in (S.DECODE_GEMV, S.PREFILL_GEMM):
+        w = S.workload_weights(c)
+        packed = torch.from_numpy(w.packed.reshape(-1)).to(dev)
+        scales = torch.from_numpy(w.scales.reshape(-1)).to(dev)
+        zp = None if w.zero_points is None else torch.from_numpy(w.zero_points.reshape(-1)).to(dev)
+        q = mnb.repack(packed, scales, zp, c.N, c.K, c.group)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            mnb.mnb_repack(q.desc, packed, scales, zp, q.repacked)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / 5 * 1e3
+        nbytes = packed.numel() + scales.numel() * scales.element_size() + (0 if zp is None else zp.numel()) \
+            + q.repacked.numel()
+        out.append({"weight": "%s (N=%d K=%d g=%d)" % (c.name.split(" M=")[0], c.N, c.K, c.group),
+                    "us": round(us, 2), "GBps_read_plus_written": round(nbytes / (us * 1e-6) / 1e9, 1)})
+    return out
+
+
 def cpu_baseline(seconds):
     """The oracle as it stands (C, fp64, OpenMP over outputs) on the host
     cores: the decode GEMV workload in full, repeated for about `seconds`,
@@ -403,6 +432,7 @@ def main():
         "gemm_TFLOPs": gemm["TFLOPs"] if gemm else None,
         "workloads": list(res.values()),
     }
+    out["repack"] = time_repack()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out))
