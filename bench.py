@@ -352,6 +352,15 @@ def cpu_baseline(seconds):
             break
     gemv_s = (time.perf_counter() - t0) / reps
     bytes_ = onnx_bytes(1, c.K, c.N, c.group, 2, True, 2)
+    # the same call on one thread
+    t0 = time.perf_counter()
+    reps1 = 0
+    while True:
+        o.matmul_nbits(A, w.packed, w.scales, w.zero_points, c.N, c.K, c.group, threads=1)
+        reps1 += 1
+        if time.perf_counter() - t0 > seconds * 0.2:
+            break
+    gemv1_s = (time.perf_counter() - t0) / reps1
     p = S.PREFILL_GEMM
     wp = S.workload_weights(p)
     rows = 8
@@ -363,6 +372,9 @@ def cpu_baseline(seconds):
             "kind": "oracle",
             "sample": "decode GEMV M=1 K=4096 N=4096 g=32 in full, %d repetitions (%.2f ms each)"
                       % (reps, gemv_s * 1e3),
+            "one_thread": {"value": round(bytes_ / gemv1_s / 1e9, 3), "unit": "GB/s",
+                           "sample": "the same call on 1 thread, %d repetitions (%.2f ms each)"
+                                     % (reps1, gemv1_s * 1e3)},
             "gemm": {"value": round(2 * rows * p.N * p.K / gemm_s / 1e12, 5), "unit": "TFLOP/s",
                      "sample": "prefill GEMM rows 0..%d of M=2048 (K=4096 N=14336 g=128), %.2f s"
                                % (rows - 1, gemm_s)}}
