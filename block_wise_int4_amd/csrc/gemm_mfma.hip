@@ -648,7 +648,16 @@ hipError_t launch_q(const Layout& L, const GemmParams& p, hipStream_t s)
 
 }  // namespace
 
-int64_t gemm_mfma_max_repacked_bytes() { return (int64_t)0x7FFFFF00; }
+// Largest K the kernel's 32-bit buffer ranges and offsets cover: a
+// workgroup's BM rows of A (BM * K * 2 bytes) and the code bytes of its
+// BN / 16 tiles (BN / 16 * C * 1024) each stay below 2^31.
+int64_t gemm_mfma_max_k()
+{
+    const int64_t lim = (int64_t(1) << 31) - 1;
+    const int64_t by_a = lim / (2 * BM);
+    const int64_t by_codes = lim / ((BN / 16) * 1024) * kChunkK;
+    return by_a < by_codes ? by_a : by_codes;
+}
 
 hipError_t launch_gemm_mfma(const Layout& L, const WeightView& w, const void* a, int64_t m,
                             const Bias& bias, void* y, hipStream_t stream, const char** variant)

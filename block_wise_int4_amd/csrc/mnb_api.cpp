@@ -278,6 +278,15 @@ size_t mnb_gemm_workspace_bytes(const mnb_weight_desc* w, int64_t m)
     return workspace_for(L, m);
 }
 
+// M > 16 runs the prefill GEMM, whose buffer offsets are 32-bit.
+static mnb_status check_gemm_k(const Layout& L, int64_t m)
+{
+    if (m > 16 && L.K > mnb::gemm_mfma_max_k())
+        return fail(MNB_ERR_UNSUPPORTED, "K=%lld exceeds the prefill GEMM limit %lld (M > 16)", (long long)L.K,
+                    (long long)mnb::gemm_mfma_max_k());
+    return MNB_OK;
+}
+
 static mnb_status gemm_common(const mnb_weight_desc* w, const void* repacked, const void* a, int64_t m,
                               int32_t a_dtype, const mnb::Bias& bias, void* y, void* workspace,
                               size_t workspace_bytes, void* stream)
@@ -292,6 +301,7 @@ static mnb_status gemm_common(const mnb_weight_desc* w, const void* repacked, co
         return fail(MNB_ERR_UNSUPPORTED, "M>1 GEMM takes fp16 activations only");
     const size_t need = workspace_for(L, m);
     if (m == 0 || L.N == 0) return ok("noop");
+    MNB_TRY(check_gemm_k(L, m));
     if (workspace_bytes < need)
         return fail(MNB_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed",
                     workspace_bytes, need);
@@ -369,6 +379,7 @@ mnb_status mnb_gemm_act_order(const mnb_weight_desc* w, const void* repacked, co
     if (L.K > 0 && m > INT64_MAX / 4 / L.K) return fail(MNB_ERR_INVALID_ARGUMENT, "M*K overflows");
     if (m > 1 && a_dtype != MNB_F16)
         return fail(MNB_ERR_UNSUPPORTED, "M>1 GEMM takes fp16 activations only");
+    MNB_TRY(check_gemm_k(L, m));
     const size_t a_bytes = act_order_a_bytes(L, m, a_dtype);
     const size_t need = a_bytes + workspace_for(L, m);
     if (workspace_bytes < need)
@@ -420,6 +431,7 @@ mnb_status mnb_gemm_accuracy4(const mnb_weight_desc* w, const void* repacked, co
     if (m == 1 && L.K > mnb::acc4_gemv_max_k())
         return fail(MNB_ERR_UNSUPPORTED, "K=%lld exceeds the int8-activation decode limit %lld",
                     (long long)L.K, (long long)mnb::acc4_gemv_max_k());
+    MNB_TRY(check_gemm_k(L, m));
     const size_t need = acc4_scale_bytes(m) + acc4_codes_bytes(L, m) + workspace_for(L, m);
     // the decode GEMV needs no workspace; given one, it receives the codes
     if ((m > 1 || workspace) && workspace_bytes < need)

@@ -57,7 +57,8 @@ size_t gemm_small_workspace(const Layout& L, int64_t m);
 hipError_t launch_gemm_small(const Layout& L, const WeightView& w, const void* a, int64_t m,
                              const Bias& bias, void* y, void* ws, hipStream_t stream, const char** variant);
 
-// M > 16, fp16 activations.
+// M > 16, fp16 activations, K up to gemm_mfma_max_k().
+int64_t gemm_mfma_max_k();
 hipError_t launch_gemm_mfma(const Layout& L, const WeightView& w, const void* a, int64_t m,
                             const Bias& bias, void* y, hipStream_t stream, const char** variant);
 

@@ -42,7 +42,8 @@
  *     enum, misalignment, workspace too small, size overflow).
  *   MNB_ERR_UNSUPPORTED: a valid MatMulNBits request this library does not
  *     implement (K not a multiple of group, group outside 16/32/64/128, a
- *     dtype pairing other than the ones below).  The library never computes
+ *     dtype pairing other than the ones below, a K beyond the limit a call
+ *     documents).  The library never computes
  *     something else instead (the "Unsupported" convention of ferrox-cuda
  *     gpu.rs, enum CudaError), and never falls back internally.
  *   MNB_ERR_DEVICE: no usable gfx950 device, or the launch failed.
@@ -144,7 +145,8 @@ mnb_status mnb_repack(const mnb_weight_desc* w, const uint8_t* packed, const voi
  *   y[n] = sum_k a[k] * dequant(B)[n,k]   for n < N,
  * with a (device, [K]) and y (device, [N]) both of a_dtype (MNB_F16 or
  * MNB_F32).  Products accumulate in fp32; fp16 outputs are rounded once
- * (round to nearest even). */
+ * (round to nearest even).  The activation is staged on chip: K <= 31744
+ * for fp16 activations, K <= 15872 for fp32 (else MNB_ERR_UNSUPPORTED). */
 mnb_status mnb_gemv(const mnb_weight_desc* w, const void* repacked, const void* a,
                     int32_t a_dtype, void* y, void* stream);
 
@@ -167,14 +169,16 @@ size_t mnb_gemm_workspace_bytes(const mnb_weight_desc* w, int64_t m);
  * and its split-K form, re-designed for gfx950):
  *   Y[m,n] = sum_k A[m,k] * dequant(B)[n,k],
  * A (device, [M,K]) and Y (device, [M,N]) of a_dtype.  M = 1 runs the decode
- * GEMV; 2 <= M <= 16 a weight-streaming MFMA kernel (with a fixed-order
- * split-K reduction through `workspace` when that fills the chip better);
- * larger M the MFMA prefill GEMM.  The GEMM paths take fp16 A only
+ * GEMV (its K limit applies); 2 <= M <= 16 a weight-streaming MFMA kernel
+ * whose workgroups split K among their waves and reduce in a fixed order;
+ * larger M the MFMA prefill GEMM, for K <= 11184810 (its 32-bit buffer
+ * offsets; else MNB_ERR_UNSUPPORTED).  The GEMM paths take fp16 A only
  * (MNB_ERR_UNSUPPORTED for fp32 A with M > 1).  Products are fp16 x fp16 on
  * the matrix cores with fp32 accumulation; each group's partial sum is
  * multiplied by its scale after that group's accumulation.  `workspace`
- * (device, 16-byte aligned) must hold mnb_gemm_workspace_bytes(w, m) bytes;
- * it may be NULL when that is 0.  Results are deterministic. */
+ * (device, 16-byte aligned) must hold mnb_gemm_workspace_bytes(w, m) bytes
+ * (0 for every shape at present); it may be NULL when that is 0.  Results
+ * are deterministic. */
 mnb_status mnb_gemm(const mnb_weight_desc* w, const void* repacked, const void* a, int64_t m,
                     int32_t a_dtype, void* y, void* workspace, size_t workspace_bytes,
                     void* stream);

@@ -138,6 +138,28 @@ def test_argument_validation():
     assert "limit" in _expect(mnb.MNB_ERR_UNSUPPORTED, lib.mnb_gemv, D(big), FAKE, FAKE, 1, FAKE, None)
 
 
+def test_prefill_k_limit():
+    """M > 16 runs the prefill GEMM, whose buffer offsets are 32-bit: K up to
+    11184810 (96 rows of A below 2^31 bytes) is accepted (without a device
+    the call then stops at the device check), one group more is refused
+    before anything is enqueued, by every entry point that reaches it; the
+    small-M kernel has no such limit."""
+    lib = mnb.lib
+    U, DEV = mnb.MNB_ERR_UNSUPPORTED, mnb.MNB_ERR_DEVICE
+    k_ok = 11184810 // 128 * 128
+    ok, over = mnb.desc(16, k_ok, 128, False, mnb.MNB_F16), mnb.desc(16, k_ok + 128, 128, False, mnb.MNB_F16)
+    assert lib.mnb_gemm(D(ok), FAKE, FAKE, 17, 1, FAKE, None, 0, None) == DEV
+    assert "prefill GEMM limit" in _expect(U, lib.mnb_gemm, D(over), FAKE, FAKE, 17, 1, FAKE, None, 0, None)
+    assert lib.mnb_gemm(D(over), FAKE, FAKE, 16, 1, FAKE, None, 0, None) == DEV
+    assert "prefill GEMM limit" in _expect(U, lib.mnb_gemm_bias, D(over), FAKE, FAKE, 40, 1, FAKE, 0, 0, FAKE,
+                                           None, 0, None)
+    assert "prefill GEMM limit" in _expect(U, lib.mnb_gemm_act_order, D(over), FAKE, FAKE, 17, 1, FAKE, FAKE,
+                                           FAKE, 1 << 40, None)
+    over32 = mnb.desc(16, k_ok + 128, 128, False, mnb.MNB_F32)
+    assert "prefill GEMM limit" in _expect(U, lib.mnb_gemm_accuracy4, D(over32), FAKE, FAKE, 17, None, FAKE,
+                                           FAKE, 1 << 40, None)
+
+
 def test_bias_argument_validation():
     lib = mnb.lib
     d = mnb.desc(64, 256, 32, True, mnb.MNB_F16)
