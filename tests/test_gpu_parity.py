@@ -380,6 +380,51 @@ def test_prefill_mid_size_sampled_parity(mnb):
         assert t.equal(y, y2)
 
 
+def _sparse_row(K, seed):
+    """An fp16 row that is zero except its first and last 128-k chunks and 8
+    random chunks between them (~N(0,1) there): the tolerance stays tight at
+    any K, so a chunk read wrongly at the far end cannot hide in it."""
+    rng = np.random.default_rng(seed)
+    C = K // 128
+    r = np.zeros(K, np.float16)
+    for c in np.concatenate([[0, C - 1], rng.choice(np.arange(1, C - 1), 8, replace=False)]):
+        r[c * 128:(c + 1) * 128] = rng.standard_normal(128).astype(np.float16)
+    return r
+
+
+def test_prefill_at_maximum_k(mnb):
+    """The prefill GEMM at its largest K (11184768 = 87381 chunks): a full
+    96-row block of A is 2^31 bytes less 8 KiB, so the last row's offsets come
+    within 0.4% of the 32-bit limit.  One workgroup (M = 96, N = 32) runs
+    every chunk.  Every row is sparse (_sparse_row, the memory traffic is
+    that of a dense row); rows 0, 1, 47 and 95 are checked against the oracle
+    on every column."""
+    t = G.torch()
+    M, N, g = 96, 32, 128
+    K = 11184810 // 128 * 128
+    w = _weight(N, K, g, "f16", True, seed=21, lo=0.002, hi=0.01)
+    q = G.upload(w)
+    a = t.empty((M, K), dtype=t.float16, device="cuda")
+    rows = [0, 1, 47, 95]
+    kept = {}
+    for m in range(M):
+        r = _sparse_row(K, (210, m))
+        a[m].copy_(t.from_numpy(r))
+        if m in rows:
+            kept[m] = r
+    y = t.empty((M, N), dtype=t.float16, device="cuda")
+    G.gemm(q, a, M, y)
+    assert mnb.mnb_last_variant() == "gemm_mfma_32x32x16"
+    yh = G.host(y)
+    del a
+    t.cuda.empty_cache()
+    A = np.stack([kept[m] for m in rows])
+    ms = np.repeat(np.arange(len(rows)), N)
+    ns = np.tile(np.arange(N), len(rows))
+    Y, B = o.matmul_nbits_at(A, w.packed, w.scales, w.zero_points, N, K, g, ms, ns)
+    G.assert_within(yh[np.array(rows)[ms], ns], Y, B, "prefill at K=%d" % K)
+
+
 BIAS_CASES = [
     # M, N, K, g, activation dtype, zp: every path (GEMV fp16/fp32, small M, prefill)
     (1, 300, 512, 32, "f16", True), (1, 200, 640, 64, "f32", False),
