@@ -80,6 +80,7 @@ struct GemmParams {
     int M, N, K, C;
     int T;                 // column tiles
     int num_m, num_n;      // workgroup grid
+    int vec_store;         // N % 8 == 0 and y 16-byte aligned: 16-byte row stores
 };
 
 // LDS geometry of one pipeline stage for (Q, scale bytes, zero points).
@@ -553,13 +554,39 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
         }
         return;
     }
-    if (p.bias && p.bias_stride == 0) {
-        // one bias vector for every row: the lane's two columns only
-        float bq[PAIRS];
+    // fp16 outputs, value(rb, q, e) for each accumulator element.  With
+    // vec_store (N % 8 == 0, y 16-byte aligned) each wave stages its BM x 64
+    // block in LDS, row-major with 144-byte rows (the two row quads of one
+    // store instruction fall in different banks), then writes 8 columns of
+    // one row per lane: 96 rows in 12 full-line instructions instead of 96
+    // two-byte ones.  A segment is then all inside the output or all
+    // outside.  Otherwise every element is stored on its own.
+    auto store_f16 = [&](auto value) __attribute__((always_inline)) {
+        if (p.vec_store) {
+            constexpr int RS = 144;
+            static_assert(WAVES * BM * RS <= KernelLds<ST, Q, HAS_ZP>::kBytes, "the output block fits the LDS");
+            block_sync_lds();   // every wave is past its last fragment reads
+            unsigned char* ob = lds + wave * (BM * RS);
 #pragma unroll
-        for (int q = 0; q < PAIRS; ++q) {
-            const int n = nb * BN + wave * 64 + q * 32 + (lane & 31);
-            bq[q] = __half2float(p.bias[n < p.N ? n : p.N - 1]);
+            for (int q = 0; q < PAIRS; ++q)
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int row = rb * 32 + 8 * (e >> 2) + 4 * oct + (e & 3);
+                        *reinterpret_cast<__half*>(ob + row * RS + (q * 32 + (lane & 31)) * 2) = value(rb, q, e);
+                    }
+            // the wave reads what its other lanes wrote: LDS keeps a wave's
+            // operations in order; this keeps the compiler from moving them
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            const int n = nb * BN + wave * 64 + (lane & 7) * 8;
+#pragma unroll
+            for (int i = 0; i < BM / 8; ++i) {
+                const int row = (lane >> 3) + 8 * i;
+                const u4_t v = *reinterpret_cast<const u4_t*>(ob + row * RS + (lane & 7) * 16);
+                if (m0 + row < p.M && n < p.N) *reinterpret_cast<u4_t*>(p.y + (int64_t)(m0 + row) * p.N + n) = v;
+            }
+            return;
         }
 #pragma unroll
         for (int q = 0; q < PAIRS; ++q) {
@@ -570,9 +597,19 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int m = m0 + rb * 32 + 8 * (e >> 2) + 4 * oct + (e & 3);
-                    if (m < p.M) p.y[(int64_t)m * p.N + n] = finish_value(acc[rb][q][e], bq[q], p.bias_after_round);
+                    if (m < p.M) p.y[(int64_t)m * p.N + n] = value(rb, q, e);
                 }
         }
+    };
+    if (p.bias && p.bias_stride == 0) {
+        // one bias vector for every row: the lane's two columns only
+        float bq[PAIRS];
+#pragma unroll
+        for (int q = 0; q < PAIRS; ++q) {
+            const int n = nb * BN + wave * 64 + q * 32 + (lane & 31);
+            bq[q] = __half2float(p.bias[n < p.N ? n : p.N - 1]);
+        }
+        store_f16([&](int rb, int q, int e) { return finish_value(acc[rb][q][e], bq[q], p.bias_after_round); });
         return;
     }
     if (p.bias) {
@@ -593,35 +630,12 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
                     bv[q][rb][e] = p.bias[(int64_t)m * p.bias_stride + n];
                 }
         }
-#pragma unroll
-        for (int q = 0; q < PAIRS; ++q) {
-            const int n = nb * BN + wave * 64 + q * 32 + (lane & 31);
-            if (n >= p.N) continue;
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const int m = m0 + rb * 32 + 8 * (e >> 2) + 4 * oct + (e & 3);
-                    if (m < p.M)
-                        p.y[(int64_t)m * p.N + n] = finish_value(acc[rb][q][e], __half2float(bv[q][rb][e]),
-                                                                 p.bias_after_round);
-                }
-        }
+        store_f16([&](int rb, int q, int e) {
+            return finish_value(acc[rb][q][e], __half2float(bv[q][rb][e]), p.bias_after_round);
+        });
         return;
     }
-#pragma unroll
-    for (int q = 0; q < PAIRS; ++q) {
-        const int n = nb * BN + wave * 64 + q * 32 + (lane & 31);
-        if (n >= p.N) continue;
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int m = m0 + rb * 32 + 8 * (e >> 2) + 4 * oct + (e & 3);
-                if (m < p.M) p.y[(int64_t)m * p.N + n] = __float2half_rn(acc[rb][q][e]);
-            }
-        }
-    }
+    store_f16([&](int rb, int q, int e) { return __float2half_rn(acc[rb][q][e]); });
 }
 
 template <typename ST, int Q, bool HAS_ZP>
@@ -682,6 +696,7 @@ hipError_t launch_gemm_mfma(const Layout& L, const WeightView& w, const void* a,
     p.T = (int)L.T;
     p.num_m = (int)((m + BM - 1) / BM);
     p.num_n = (int)((L.N + BN - 1) / BN);
+    p.vec_store = (L.N % 8 == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0) ? 1 : 0;
     if (variant) *variant = "gemm_mfma_32x32x16";
     if (L.ss == 2)
         return L.has_zp ? launch_q<__half, true>(L, p, stream) : launch_q<__half, false>(L, p, stream);
@@ -712,6 +727,7 @@ hipError_t launch_gemm_mfma_f32(const Layout& L, const WeightView& w, const void
     p.T = (int)L.T;
     p.num_m = (int)((m + BM - 1) / BM);
     p.num_n = (int)((L.N + BN - 1) / BN);
+    p.vec_store = 0;
     if (variant) *variant = "gemm_mfma_32x32x16_accuracy4";
     if (L.ss == 2)
         return L.has_zp ? launch_q<__half, true>(L, p, stream) : launch_q<__half, false>(L, p, stream);
