@@ -80,7 +80,7 @@ struct GemmParams {
     int M, N, K, C;
     int T;                 // column tiles
     int num_m, num_n;      // workgroup grid
-    int vec_store;         // N % 8 == 0 and y 16-byte aligned: 16-byte row stores
+    int vec_store;         // 16-byte row stores: y (y32) 16-byte aligned, N % 8 (N % 4) == 0
 };
 
 // LDS geometry of one pipeline stage for (Q, scale bytes, zero points).
@@ -183,7 +183,9 @@ template <typename ST, int Q, bool HAS_ZP> struct KernelLds {
     static constexpr int kBytes = G::kStages * G::kBytes;
 };
 
-template <typename ST, int Q, bool HAS_ZP, bool KTAIL>
+// F32OUT: the int8-activation epilogue (fp32 output, row scale, fp32 bias),
+// its own instantiation so that the fp16 kernel's code is not affected.
+template <typename ST, int Q, bool HAS_ZP, bool KTAIL, bool F32OUT>
 __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmParams p)
 {
     typedef StageGeom<Q, (int)sizeof(ST), HAS_ZP> G;
@@ -523,7 +525,7 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
 
     // ---- epilogue: lane holds column (lane & 31) of each 32x32 block, rows
     // 8*(e/4) + 4*oct + e%4
-    if (p.row_scale) {
+    if constexpr (F32OUT) {
         // fp32 outputs: the row's activation scale, then the bias; the
         // lane's row scales are loaded before any is used
         float rs[RB][16];
@@ -535,21 +537,63 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
                 m = m < p.M ? m : p.M - 1;
                 rs[rb][e] = p.row_scale[m];
             }
+        float bq[PAIRS];
+#pragma unroll
+        for (int q = 0; q < PAIRS; ++q) {
+            const int n = nb * BN + wave * 64 + q * 32 + (lane & 31);
+            bq[q] = p.bias32 ? p.bias32[n < p.N ? n : p.N - 1] : 0.0f;
+        }
+        auto value = [&](int rb, int q, int e) __attribute__((always_inline)) {
+            float v = rs[rb][e] != 0.0f ? acc[rb][q][e] * rs[rb][e] : 0.0f;
+            if (p.bias32) v = v + bq[q];
+            return v;
+        };
+        if (p.vec_store) {
+            // as the fp16 output below, in two passes of 48 rows (the fp32
+            // block of a wave is twice the size); 288-byte rows put the two
+            // row quads of one write instruction in different banks.  With
+            // N % 4 == 0 a 16-byte segment is all inside or all outside.
+            constexpr int RS = 288, HALF = BM / 2;
+            static_assert(WAVES * HALF * RS <= KernelLds<ST, Q, HAS_ZP>::kBytes, "half the fp32 block fits the LDS");
+            block_sync_lds();   // every wave is past its last fragment reads
+            unsigned char* ob = lds + wave * (HALF * RS);
+            const int n = nb * BN + wave * 64 + (lane & 15) * 4;
+#pragma unroll
+            for (int hp = 0; hp < 2; ++hp) {
+                // 8-row block rb*4 + e/4 of the wave's 96 rows is in pass (rb*4 + e/4) / 6
+#pragma unroll
+                for (int q = 0; q < PAIRS; ++q)
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) {
+                            if ((rb * 4 + (e >> 2)) / 6 != hp) continue;
+                            const int row = rb * 32 + 8 * (e >> 2) + 4 * oct + (e & 3) - hp * HALF;
+                            *reinterpret_cast<float*>(ob + row * RS + (q * 32 + (lane & 31)) * 4) = value(rb, q, e);
+                        }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+                for (int i = 0; i < HALF / 4; ++i) {
+                    const int row = (lane >> 4) + 4 * i;
+                    const int m = m0 + hp * HALF + row;
+                    const u4_t v = *reinterpret_cast<const u4_t*>(ob + row * RS + (lane & 15) * 16);
+                    if (m < p.M && n < p.N) *reinterpret_cast<u4_t*>(p.y32 + (int64_t)m * p.N + n) = v;
+                }
+                // the reads are done before the next pass writes
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            }
+            return;
+        }
 #pragma unroll
         for (int q = 0; q < PAIRS; ++q) {
             const int n = nb * BN + wave * 64 + q * 32 + (lane & 31);
             if (n >= p.N) continue;
-            const float b = p.bias32 ? p.bias32[n] : 0.0f;
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int m = m0 + rb * 32 + 8 * (e >> 2) + 4 * oct + (e & 3);
-                    if (m < p.M) {
-                        float v = rs[rb][e] != 0.0f ? acc[rb][q][e] * rs[rb][e] : 0.0f;
-                        if (p.bias32) v = v + b;
-                        p.y32[(int64_t)m * p.N + n] = v;
-                    }
+                    if (m < p.M) p.y32[(int64_t)m * p.N + n] = value(rb, q, e);
                 }
         }
         return;
@@ -638,14 +682,23 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
     store_f16([&](int rb, int q, int e) { return __float2half_rn(acc[rb][q][e]); });
 }
 
-template <typename ST, int Q, bool HAS_ZP>
-hipError_t launch_t(const GemmParams& p, hipStream_t s)
+template <typename ST, int Q, bool HAS_ZP, bool F32OUT>
+void launch_k(const GemmParams& p, hipStream_t s)
 {
     const int blocks = p.num_m * p.num_n;
     if (p.K % kChunkK != 0)
-        gemm_mfma_kernel<ST, Q, HAS_ZP, true><<<dim3(blocks), dim3(WAVES * 64), 0, s>>>(p);
+        gemm_mfma_kernel<ST, Q, HAS_ZP, true, F32OUT><<<dim3(blocks), dim3(WAVES * 64), 0, s>>>(p);
     else
-        gemm_mfma_kernel<ST, Q, HAS_ZP, false><<<dim3(blocks), dim3(WAVES * 64), 0, s>>>(p);
+        gemm_mfma_kernel<ST, Q, HAS_ZP, false, F32OUT><<<dim3(blocks), dim3(WAVES * 64), 0, s>>>(p);
+}
+
+template <typename ST, int Q, bool HAS_ZP>
+hipError_t launch_t(const GemmParams& p, hipStream_t s)
+{
+    if (p.row_scale)
+        launch_k<ST, Q, HAS_ZP, true>(p, s);
+    else
+        launch_k<ST, Q, HAS_ZP, false>(p, s);
     return hipGetLastError();
 }
 
@@ -727,7 +780,7 @@ hipError_t launch_gemm_mfma_f32(const Layout& L, const WeightView& w, const void
     p.T = (int)L.T;
     p.num_m = (int)((m + BM - 1) / BM);
     p.num_n = (int)((L.N + BN - 1) / BN);
-    p.vec_store = 0;
+    p.vec_store = (L.N % 4 == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0) ? 1 : 0;
     if (variant) *variant = "gemm_mfma_32x32x16_accuracy4";
     if (L.ss == 2)
         return L.has_zp ? launch_q<__half, true>(L, p, stream) : launch_q<__half, false>(L, p, stream);
