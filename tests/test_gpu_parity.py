@@ -380,6 +380,43 @@ def test_prefill_mid_size_sampled_parity(mnb):
         assert t.equal(y, y2)
 
 
+def test_prefill_output_alignment_paths_agree(mnb):
+    """The prefill GEMM stores whole 16-byte row segments when N % 8 == 0 and
+    Y is 16-byte aligned, and element by element otherwise: the same product
+    into a Y shifted by one element (2-byte aligned only) gives the same bits,
+    with and without a bias, and for the fp32 output of the int8-activation
+    path (4-byte shift)."""
+    t = G.torch()
+    M, N, K, g = 200, 520, 512, 64
+    w = _weight(N, K, g, "f16", True, seed=31)
+    q = G.upload(w)
+    a = G.to_dev(_act(M, K, seed=31))
+    bias = G.to_dev(_act(1, N, seed=32).reshape(N))
+    for b in (None, bias):
+        outs = []
+        for shift in (0, 1):
+            buf = t.full((M * N + 8,), float("nan"), dtype=t.float16, device="cuda")
+            y = buf[shift:shift + M * N].view(M, N)
+            if b is None:
+                G.gemm(q, a, M, y)
+            else:
+                mnb.mnb_gemm_bias(q.desc, q.repacked, a, M, b, 0, mnb.MNB_BIAS_FUSED, y, None, 0)
+            outs.append(G.host(y))
+        assert (outs[0] == outs[1]).all()
+    w32 = _weight(N, K, g, "f32", True, seed=33)
+    q32 = G.upload(w32)
+    a32 = G.to_dev(_act(M, K, "f32", seed=33))
+    n_ws = mnb.mnb_gemm_accuracy4_workspace_bytes(q32.desc, M)
+    ws = t.zeros(n_ws, dtype=t.uint8, device="cuda")
+    outs = []
+    for shift in (0, 1):
+        buf = t.full((M * N + 8,), float("nan"), dtype=t.float32, device="cuda")
+        y = buf[shift:shift + M * N].view(M, N)
+        mnb.mnb_gemm_accuracy4(q32.desc, q32.repacked, a32, M, None, y, ws, n_ws)
+        outs.append(y.cpu().numpy().copy())
+    assert (outs[0].view(np.uint32) == outs[1].view(np.uint32)).all()
+
+
 def _sparse_row(K, seed):
     """An fp16 row that is zero except its first and last 128-k chunks and 8
     random chunks between them (~N(0,1) there): the tolerance stays tight at
