@@ -326,19 +326,22 @@ def acc4_bound(Bnd, K: int, g: int) -> np.ndarray:
 
 # ---- acceptance ------------------------------------------------------------
 
-def within_bound(y, Y: np.ndarray, Bnd: np.ndarray, rel: float = REL_TOL,
-                 abs_: float = ABS_TOL) -> np.ndarray:
-    """Per-element verdict |y - Y| <= rel*Bnd + abs_, NaN==NaN, equal infs."""
+def within_bound(y, Y: np.ndarray, Bnd, rel: float = REL_TOL,
+                 abs_: float = ABS_TOL, tol=None) -> np.ndarray:
+    """Per-element verdict |y - Y| <= rel*Bnd + abs_ (or <= tol, a per-element
+    tolerance given instead of Bnd), NaN==NaN, equal infs."""
     y = np.asarray(y, dtype=np.float64)
     Y = np.asarray(Y, dtype=np.float64)
-    Bnd = np.asarray(Bnd, dtype=np.float64)
+    if tol is None:
+        tol = rel * np.asarray(Bnd, dtype=np.float64) + abs_
+    tol = np.asarray(tol, dtype=np.float64)
     both_nan = np.isnan(y) & np.isnan(Y)
     same_inf = np.isinf(y) & np.isinf(Y) & (np.sign(y) == np.sign(Y))
     with np.errstate(invalid="ignore"):
         # the distance test applies to finite expected values only: an
         # infinite Y (whose bound is infinite too) is matched only by the
         # same infinity, a NaN only by a NaN
-        ok = np.isfinite(Y) & (np.abs(y - Y) <= rel * Bnd + abs_)
+        ok = np.isfinite(Y) & (np.abs(y - Y) <= tol)
     return ok | both_nan | same_inf
 
 

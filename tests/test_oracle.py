@@ -437,6 +437,32 @@ def test_within_bound_semantics():
     assert o.within_bound([1.0 + 1.1e-2], [1.0], [10.0]).tolist() == [False]
 
 
+def test_custom_bound_rejects_values_against_an_infinite_expectation():
+    # the GPU tests' check with a tolerance of its own (the int8, SwiGLU and
+    # bias bounds) must give the same verdict on infinities as the plain
+    # rule: against Y = [-inf, +inf] with an infinite tolerance, 3.0 and -inf
+    # are both wrong
+    from tests import gpu_util as G
+    Y = np.array([[-np.inf, np.inf]])
+    tol = o.acc4_bound(np.array([[np.inf, np.inf]]), 128, 32)
+    assert np.isinf(tol).all()
+    with pytest.raises(AssertionError):
+        G.assert_within(np.array([[3.0, -np.inf]]), Y, None, "inf", bound=tol)
+    with pytest.raises(AssertionError):
+        G.assert_within(np.array([[-np.inf, 3.0]]), Y, None, "inf", bound=tol)
+    with pytest.raises(AssertionError):
+        G.assert_within(np.array([[np.nan, np.inf]]), Y, None, "inf", bound=tol)
+    G.assert_within(np.array([[-np.inf, np.inf]]), Y, None, "inf", bound=tol)
+    # NaN expected: only NaN agrees, whatever the tolerance
+    with pytest.raises(AssertionError):
+        G.assert_within(np.array([[0.0]]), np.array([[np.nan]]), None, "nan", bound=np.array([[np.inf]]))
+    G.assert_within(np.array([[np.nan]]), np.array([[np.nan]]), None, "nan", bound=np.array([[1.0]]))
+    # finite expectations: the tolerance decides
+    G.assert_within(np.array([[1.5]]), np.array([[1.0]]), None, "fin", bound=np.array([[0.5]]))
+    with pytest.raises(AssertionError):
+        G.assert_within(np.array([[1.6]]), np.array([[1.0]]), None, "fin", bound=np.array([[0.5]]))
+
+
 def test_acc4_bound_covers_the_pages_binary32_orders():
     """The int8-activation tolerance holds for both binary32 evaluation orders
     the pages' kernels use (matmul_nbits.rs, matmul_nbits_accuracy4): the sum
