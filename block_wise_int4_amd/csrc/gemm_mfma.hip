@@ -24,11 +24,18 @@
 // * Per-group scaling with a single accumulator per output: while group g
 //   accumulates, acc holds total / s_g; entering group g+1 it is multiplied
 //   by s_g / s_{g+1}, and after the last group the output is acc * s_last.
-//   The algebra is exact; each rescale adds one fp32 rounding.  A group with
+//   The ratio is a correctly rounded division; each rescale adds two fp32
+//   roundings (the ratio and the product).  A group with
 //   scale 0 gets all-zero B operands (it adds exactly nothing, NaN for
 //   infinite activations as (c - z) * 0 * a does) and keeps the units; the
 //   padding past K is such a group.  Half the registers of a separate group
 //   accumulator are freed for deeper prefetch and for two waves per SIMD.
+//   This needs the range class the repack records per tile: nonzero scales
+//   in [2^-100, 2^100] and within 2^64 of each other per column, so that
+//   total / s_g stays inside binary32 for any fp16 activations.  A workgroup
+//   with a tile outside that class computes its whole tile the plain way
+//   instead: a fresh fp32 partial per group, multiplied by the group's scale
+//   into the total with an fma (slower, any scales).
 // * Workgroup ids are remapped so the tiles resident on one XCD at a time
 //   share A rows and code columns in that XCD's L2.
 // * Epilogues: fp16 outputs (with an optional fp16 bias in either rounding of
@@ -81,6 +88,7 @@ struct GemmParams {
     int T;                 // column tiles
     int num_m, num_n;      // workgroup grid
     int vec_store;         // 16-byte row stores: y (y32) 16-byte aligned, N % 8 (N % 4) == 0
+    int64_t flags_off;     // the per-tile scale range classes
 };
 
 // LDS geometry of one pipeline stage for (Q, scale bytes, zero points).
@@ -235,6 +243,12 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
         (void*)(p.w + (HAS_ZP ? p.zp_off : 0) + (int64_t)t0 * C * (G::kZpDw * 4)), (short)0,
         (int)zp_bytes, 0x00020000);
 
+    // The range classes of the workgroup's tiles (one byte each; the 16
+    // bytes from t0 lie inside the flags section, whose size is rounded up to
+    // 256), requested before any DMA so that they have landed when chunk 0
+    // has.
+    const u4_t tile_flags = *reinterpret_cast<const u4_t*>(p.w + p.flags_off + t0);
+
     // The LDS DMAs of one chunk, one "piece" (one instruction) at a time, so
     // they can be spread over the compute of an earlier chunk: pieces
     // 0 .. A_DMA-1 copy A rows, then the scale records and the zero-point
@@ -337,7 +351,7 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
             for (int g = 0; g < Q; ++g) {
                 const int sl = slot_of(i, g, Q);
                 const float sg = to_f32(srec[sl]);
-                rt[q][g] = sg != 0.f ? unit[q] * __builtin_amdgcn_rcpf(sg) : 1.f;
+                rt[q][g] = sg != 0.f ? __fdiv_rn(unit[q], sg) : 1.f;
                 unit[q] = sg != 0.f ? sg : unit[q];
                 uint32_t zv = 8u;
                 if (HAS_ZP) {
@@ -403,6 +417,74 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
     u4_t bqA[PAIRS][2], bqB[PAIRS][2];
     h8_t bop[2][PAIRS];
 
+    // The plain per-group evaluation, for tiles outside the range class of
+    // the rescaled accumulator: one 32x32 block at a time, A fragments and
+    // code words straight from memory (rows and k outside the operand read
+    // zero), a fresh fp32 partial per group, and the total += partial * scale
+    // in fp32.  A group whose scale is 0 adds 0 (NaN for a non-finite
+    // partial, as (c - z) * 0 * a does).
+    auto fallback_tile = [&]() {
+        constexpr int SREC = G::kScaleDw * 4, ZREC = G::kZpDw * 4;
+#pragma unroll
+        for (int q = 0; q < PAIRS; ++q) {
+            const int tt = wave * TPW + 2 * q + half;   // the lane's tile in the workgroup
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                f16v_t tot, grp;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) tot[e] = 0.f;
+                const uint32_t arow = (uint32_t)(rb * 32 + (lane & 31)) * (uint32_t)K * 2u;
+                for (int c = 0; c < C; ++c) {
+                    u4_t bq[2];
+#pragma unroll
+                    for (int ph = 0; ph < 2; ++ph)
+                        bq[ph] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                            c_rsrc, b_voff[q][ph], (uint32_t)c * 1024u, 0));
+                    float sg[Q];
+                    uint32_t zg[Q];
+#pragma unroll
+                    for (int g = 0; g < Q; ++g) {
+                        const int sl = slot_of(i, g, Q);
+                        const uint32_t rec = (uint32_t)(tt * C + c);
+                        if constexpr (sizeof(ST) == 2)
+                            sg[g] = (float)__builtin_bit_cast(_Float16, (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(
+                                s_rsrc, rec * SREC + sl * 2, 0, 0));
+                        else
+                            sg[g] = __builtin_bit_cast(float, (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(
+                                s_rsrc, rec * SREC + sl * 4, 0, 0));
+                        zg[g] = 8u;
+                        if constexpr (HAS_ZP)
+                            zg[g] = ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(z_rsrc, rec * ZREC + (sl >> 1), 0, 0) >>
+                                     (4 * (sl & 1))) & 15u;
+                    }
+#pragma unroll
+                    for (int hs = 0; hs < 8; ++hs) {
+                        const int k = c * kChunkK + 16 * hs + 8 * oct;
+                        h8_t a;
+                        if (!KTAIL || k < K)
+                            a = __builtin_bit_cast(h8_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                a_rsrc, arow + (uint32_t)k * 2u, 0, 0));
+                        else
+                            a = h8_t{};
+                        h2_t u[4];
+                        unpack8(bq[hs & 1][hs >> 1], zp_const(zg[hs / HS_PER_GROUP]), u);
+                        if (hs % HS_PER_GROUP == 0) {
+#pragma unroll
+                            for (int e = 0; e < 16; ++e) grp[e] = 0.f;
+                        }
+                        grp = mfma32(a, as_h8(u), grp);
+                        if (hs % HS_PER_GROUP == HS_PER_GROUP - 1) {
+                            const float sc = sg[hs / HS_PER_GROUP];
+#pragma unroll
+                            for (int e = 0; e < 16; ++e) tot[e] = __builtin_fmaf(grp[e], sc, tot[e]);
+                        }
+                    }
+                }
+                acc[rb][q] = tot;
+            }
+        }
+    };
+
     // ---- prologue: chunks 0 .. NST-2 in flight, chunk 0 read in ----
     const int npre = C < NST - 1 ? C : NST - 1;
 #pragma unroll
@@ -416,6 +498,20 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
     // chunk 0's DMAs landed for this wave (later issues may stay in flight)
     wait_landed(npre - 1);
     block_sync_lds();
+
+    // every wave of the workgroup reads the same bytes: a uniform decision
+    bool tiles_safe = true;
+#pragma unroll
+    for (int j = 0; j < BN / 16; ++j)
+        if (j < tiles_here && ((tile_flags[j >> 2] >> (8 * (j & 3))) & 0xFFu) != 1u) tiles_safe = false;
+    tiles_safe = uniform(tiles_safe ? 1 : 0) != 0;
+
+    if (!tiles_safe) {
+        // the plain way: let the prologue's DMAs land (the epilogue reuses
+        // the LDS), then each 32x32 block of the wave on its own
+        wait_vm<0>();
+        fallback_tile();
+    } else {
     read_meta(0, ratioA, zcA);
     load_afr(0, afr[0], 0);
     {
@@ -522,6 +618,7 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[rb][q][e] *= unit[q];
+    }   // tiles_safe
 
     // ---- epilogue: lane holds column (lane & 31) of each 32x32 block, rows
     // 8*(e/4) + 4*oct + e%4
@@ -750,6 +847,7 @@ hipError_t launch_gemm_mfma(const Layout& L, const WeightView& w, const void* a,
     p.num_m = (int)((m + BM - 1) / BM);
     p.num_n = (int)((L.N + BN - 1) / BN);
     p.vec_store = (L.N % 8 == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0) ? 1 : 0;
+    p.flags_off = L.flags_off;
     if (variant) *variant = "gemm_mfma_32x32x16";
     if (L.ss == 2)
         return L.has_zp ? launch_q<__half, true>(L, p, stream) : launch_q<__half, false>(L, p, stream);
@@ -781,6 +879,7 @@ hipError_t launch_gemm_mfma_f32(const Layout& L, const WeightView& w, const void
     p.num_m = (int)((m + BM - 1) / BM);
     p.num_n = (int)((L.N + BN - 1) / BN);
     p.vec_store = (L.N % 4 == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0) ? 1 : 0;
+    p.flags_off = L.flags_off;
     if (variant) *variant = "gemm_mfma_32x32x16_accuracy4";
     if (L.ss == 2)
         return L.has_zp ? launch_q<__half, true>(L, p, stream) : launch_q<__half, false>(L, p, stream);

@@ -88,37 +88,77 @@ template <typename ST, int Q, bool HAS_ZP> struct ChunkRegs {
     uint32_t zw;
 };
 
-// The scales and zero points of one chunk (small loads, issued ahead of the
-// code stream so that their wait does not cover the code loads).
+// One tile's sections of a repacked weight as buffer resources: chunk c of
+// the tile is at c times the chunk's record size, and a chunk past the tile's
+// C chunks lies outside the range, where a buffer load returns zeros without
+// a memory access.  So a wave's loads can be unconditional (all in flight at
+// once) without reading any chunk twice.
+struct TileRsrc {
+    __amdgpu_buffer_rsrc_t codes, scales, zp;
+};
+
+template <typename ST, int Q>
+__device__ __forceinline__ TileRsrc tile_rsrc(const GemvWeight& w, int64_t t, int C)
+{
+    constexpr int SREC = kTileN * Q * (int)sizeof(ST), ZREC = kTileN / 2 * Q;
+    TileRsrc r;
+    r.codes = __builtin_amdgcn_make_buffer_rsrc((void*)(w.codes + t * C * 64), (short)0, C * kChunkBytes,
+                                                0x00020000);
+    r.scales = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(static_cast<const uint8_t*>(w.scales) + t * C * SREC), (short)0, C * SREC, 0x00020000);
+    r.zp = __builtin_amdgcn_make_buffer_rsrc((void*)(w.zp ? w.zp + t * C * ZREC : reinterpret_cast<const uint8_t*>(w.codes)), (short)0,
+                                             w.zp ? C * ZREC : 0, 0x00020000);
+    return r;
+}
+
+template <typename T> __device__ __forceinline__ T buf_load(__amdgpu_buffer_rsrc_t r, int voff, int soff);
+template <> __device__ __forceinline__ uint16_t buf_load<uint16_t>(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+template <> __device__ __forceinline__ uint32_t buf_load<uint32_t>(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+template <> __device__ __forceinline__ uint64_t buf_load<uint64_t>(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+{
+    return __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+template <> __device__ __forceinline__ u4_t buf_load<u4_t>(__amdgpu_buffer_rsrc_t r, int voff, int soff)
+{
+    return __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// The scales and zero points of chunk c of the tile (small loads, issued
+// ahead of the code stream so that their wait does not cover the code loads).
 template <typename ST, int Q, bool HAS_ZP>
-__device__ __forceinline__ void load_meta(const GemvWeight& w, int64_t chunk, int lane,
-                                          ChunkRegs<ST, Q, HAS_ZP>& r)
+__device__ __forceinline__ void load_meta(const TileRsrc& tr, int c, int lane, ChunkRegs<ST, Q, HAS_ZP>& r)
 {
     constexpr int NS = LaneGroups<Q>::NS;
+    typedef typename ScaleVec<ST, NS>::raw RawS;
     const int i = lane & 15, h = lane >> 4;
     const int sbase = Q <= 4 ? i * Q : ((h >> 1) * 16 + i) * 4;
-    const ST* sp = static_cast<const ST*>(w.scales) + chunk * kTileN * Q + sbase;
-    r.s = *reinterpret_cast<const typename ScaleVec<ST, NS>::raw*>(sp);
+    r.s = buf_load<RawS>(tr.scales, sbase * (int)sizeof(ST), c * (kTileN * Q * (int)sizeof(ST)));
     if (HAS_ZP) {
-        const uint8_t* zp = w.zp + chunk * (kTileN / 2) * Q;
+        const int zoff = c * (kTileN / 2 * Q);
         if (Q == 1) {
-            r.zw = (zp[i >> 1] >> (4 * (i & 1))) & 15u;
+            r.zw = (__builtin_amdgcn_raw_buffer_load_b8(tr.zp, i >> 1, zoff, 0) >> (4 * (i & 1))) & 15u;
         } else if (Q == 2) {
-            r.zw = zp[i];
+            r.zw = __builtin_amdgcn_raw_buffer_load_b8(tr.zp, i, zoff, 0);
         } else {
-            r.zw = *reinterpret_cast<const uint16_t*>(zp + sbase / 2);
+            r.zw = buf_load<uint16_t>(tr.zp, sbase / 2, zoff);
         }
     } else {
         r.zw = 0;
     }
 }
 
-// The chunk's code words: one 16-byte load per lane, a contiguous 1 KiB per wave.
+// Chunk c's code words: one 16-byte load per lane, a contiguous 1 KiB per
+// wave, nontemporal (each word is read once).
 template <typename ST, int Q, bool HAS_ZP>
-__device__ __forceinline__ void load_codes(const GemvWeight& w, int64_t chunk, int lane,
-                                           ChunkRegs<ST, Q, HAS_ZP>& r)
+__device__ __forceinline__ void load_codes(const TileRsrc& tr, int c, int lane, ChunkRegs<ST, Q, HAS_ZP>& r)
 {
-    r.d = __builtin_nontemporal_load(w.codes + chunk * 64 + lane);
+    r.d = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(tr.codes, lane * 16, c * kChunkBytes, 2));
 }
 
 // fp16 activations: the four 32-k steps of one chunk on the matrix cores.
@@ -237,7 +277,11 @@ constexpr int kRedBytes = 2 * kMaxWaves * 16 * sizeof(float);
 // act order: index vectors (4 columns each) a thread requests up front
 constexpr int kPermPre = 4;
 
-template <typename AT, typename ST, int Q, bool HAS_ZP, bool FUSED, int kBatch, bool PERM>
+// kBatch chunks per wave are in flight together.  LOOP = false: every chunk of
+// the tile fits in one batch per wave (waves * kBatch >= C), so the kernel is
+// straight-line code holding one register set; LOOP = true: batches alternate
+// between two register sets.
+template <typename AT, typename ST, int Q, bool HAS_ZP, bool FUSED, int kBatch, bool PERM, bool LOOP>
 __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
 {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -289,29 +333,29 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
     for (int x = 0; x < NW; ++x) acc[x] = 0.0f;
 
     // 2. the wave's chunks c = wave + nw*u, a batch of kBatch at a time.
-    //    Chunk indices are clamped so a batch's loads are unconditional and
-    //    all in flight together; the compute is guarded instead.
+    //    A batch's loads are unconditional and all in flight together (a
+    //    chunk past the tile reads zeros without a memory access); the
+    //    compute is guarded instead.
     const int stride = nw * kBatch;
+    TileRsrc tr[NW];
+#pragma unroll
+    for (int x = 0; x < NW; ++x) tr[x] = tile_rsrc<ST, Q>(p.w[x], t, C);
     auto load_batch = [&](Regs (&r)[NW][kBatch], int cb) {
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            int c = cb + nw * u;
-            c = c < C ? c : C - 1;
 #pragma unroll
-            for (int x = 0; x < NW; ++x) load_meta<ST, Q, HAS_ZP>(p.w[x], t * C + c, lane, r[x][u]);
+            for (int x = 0; x < NW; ++x) load_meta<ST, Q, HAS_ZP>(tr[x], cb + nw * u, lane, r[x][u]);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
-            int c = cb + nw * u;
-            c = c < C ? c : C - 1;
 #pragma unroll
-            for (int x = 0; x < NW; ++x) load_codes<ST, Q, HAS_ZP>(p.w[x], t * C + c, lane, r[x][u]);
+            for (int x = 0; x < NW; ++x) load_codes<ST, Q, HAS_ZP>(tr[x], cb + nw * u, lane, r[x][u]);
         }
         __builtin_amdgcn_sched_barrier(0);
     };
     Regs cur[NW][kBatch];
-    load_batch(cur, wave < C ? wave : 0);
+    load_batch(cur, wave);
 
     // 3. stage the activation in LDS (zero beyond K) while the codes stream in
     if (tid < nvec) s_vec[tid] = tid < nvec_valid ? first : u4_t{0u, 0u, 0u, 0u};
@@ -368,17 +412,17 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
             }
         }
     };
-    if (wave + stride >= C) {
+    if (!LOOP || wave + stride >= C) {
         // one batch per wave (the common decode shapes): straight-line code
         if (wave < C) compute_batch(cur, wave);
-    } else {
+    } else if constexpr (LOOP) {
         // two register sets in turn, the loop unrolled by two: the next
         // batch is requested before the current one is computed, and no
         // registers are copied, so the waits at the top of each compute count
         // only that batch's loads (a copy at the back edge would make them
         // wait for everything in flight).  The loads are unconditional
-        // (load_batch clamps chunks past the end to the last one, which the
-        // compute skips), so every path has the same loads in flight.
+        // (chunks past the end read zeros, and the compute skips them), so
+        // every path has the same loads in flight.
         Regs alt[NW][kBatch];
         for (int cb = wave; cb < C; cb += 2 * stride) {
             load_batch(alt, cb + stride);
@@ -430,13 +474,30 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
     }
 }
 
+// Chunks per wave: when the tile's C chunks fit in one batch of at most
+// kMaxBatch per wave, the smallest batch size of {1, 2, 4} that covers them
+// (every load of the wave in flight before its first wait, one register set);
+// else the two-set loop with batches of 2 (16 waves) or 4 (8 waves).  Larger
+// single batches (6 or 8 chunks in flight per wave) measured slower: the
+// loads finish sooner, but every chunk of a wave then lands near the end of
+// the stream and the unpack work runs after it instead of beside it.
+constexpr int kMaxBatch = 4;
+
 template <typename AT, typename ST, int Q, bool HAS_ZP, bool FUSED, bool PERM>
 hipError_t launch_b(const GemvParams& p, int waves, size_t smem, int64_t tiles, hipStream_t s)
 {
-    if (waves > kMaxWaves / 2)
-        gemv_kernel<AT, ST, Q, HAS_ZP, FUSED, 2, PERM><<<dim3((unsigned)tiles), dim3(waves * 64), smem, s>>>(p);
+    const dim3 grid((unsigned)tiles), block(waves * 64);
+    const int per_wave = (p.C + waves - 1) / waves;
+    if (per_wave <= 1)
+        gemv_kernel<AT, ST, Q, HAS_ZP, FUSED, 1, PERM, false><<<grid, block, smem, s>>>(p);
+    else if (per_wave <= 2)
+        gemv_kernel<AT, ST, Q, HAS_ZP, FUSED, 2, PERM, false><<<grid, block, smem, s>>>(p);
+    else if (per_wave <= kMaxBatch)
+        gemv_kernel<AT, ST, Q, HAS_ZP, FUSED, kMaxBatch, PERM, false><<<grid, block, smem, s>>>(p);
+    else if (waves > kMaxWaves / 2)
+        gemv_kernel<AT, ST, Q, HAS_ZP, FUSED, 2, PERM, true><<<grid, block, smem, s>>>(p);
     else
-        gemv_kernel<AT, ST, Q, HAS_ZP, FUSED, 4, PERM><<<dim3((unsigned)tiles), dim3(waves * 64), smem, s>>>(p);
+        gemv_kernel<AT, ST, Q, HAS_ZP, FUSED, 4, PERM, true><<<grid, block, smem, s>>>(p);
     return hipGetLastError();
 }
 

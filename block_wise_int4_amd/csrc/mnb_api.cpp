@@ -153,6 +153,8 @@ mnb_status mnb_repacked_layout(const mnb_weight_desc* w, mnb_layout* out)
     out->scales_bytes = L.scales_bytes;
     out->zero_points_offset = L.zp_off;
     out->zero_points_bytes = L.zp_bytes;
+    out->range_flags_offset = L.flags_off;
+    out->range_flags_bytes = L.flags_bytes;
     out->total_bytes = L.total;
     g_error.clear();
     return MNB_OK;
@@ -418,9 +420,9 @@ size_t mnb_gemm_accuracy4_workspace_bytes(const mnb_weight_desc* w, int64_t m)
     return acc4_scale_bytes(m) + acc4_codes_bytes(L, m) + workspace_for(L, m);
 }
 
-mnb_status mnb_gemm_accuracy4(const mnb_weight_desc* w, const void* repacked, const float* a, int64_t m,
-                              const float* bias, float* y, void* workspace, size_t workspace_bytes,
-                              void* stream)
+static mnb_status accuracy4_common(const mnb_weight_desc* w, const void* repacked, const float* a, int64_t m,
+                                   const float* bias, float* y, void* workspace, size_t workspace_bytes,
+                                   void* stream)
 {
     Layout L;
     MNB_TRY(check_desc(w, &L));
@@ -458,6 +460,13 @@ mnb_status mnb_gemm_accuracy4(const mnb_weight_desc* w, const void* repacked, co
     else
         e = mnb::launch_gemm_mfma_f32(L, v, q, m, sc, bias, y, s, &variant);
     return launched(e, variant);
+}
+
+mnb_status mnb_gemm_accuracy4(const mnb_weight_desc* w, const void* repacked, const float* a, int64_t m,
+                              const float* bias, float* y, void* workspace, size_t workspace_bytes,
+                              void* stream)
+{
+    return accuracy4_common(w, repacked, a, m, bias, y, workspace, workspace_bytes, stream);
 }
 
 mnb_status mnb_unpack_debug(const mnb_weight_desc* w, const void* repacked, uint8_t* codes,

@@ -37,6 +37,7 @@ struct Layout {
     int64_t codes_off, codes_bytes;
     int64_t scales_off, scales_bytes;
     int64_t zp_off, zp_bytes;
+    int64_t flags_off, flags_bytes;   // one byte per tile: its scales' range class
     int64_t total;
 };
 
@@ -65,9 +66,19 @@ MNB_HD Layout make_layout(int64_t N, int64_t K, int g, bool has_zp, bool f16_sca
         L.zp_off = 0;
         L.zp_bytes = 0;
     }
-    L.total = align_up(end, kAlign);
+    L.flags_off = align_up(end, kAlign);
+    L.flags_bytes = L.T;
+    L.total = align_up(L.flags_off + L.flags_bytes, kAlign);
     return L;
 }
+
+// Range class of a tile's scales (the byte of the tile in the flags
+// section): 1 when every scale of its columns that is neither zero nor NaN
+// has magnitude in [2^-100, 2^100] and, per column, the largest such magnitude
+// is at most 2^64 times the smallest; 0 otherwise (an infinite, subnormal,
+// tiny or huge scale, or a wider spread).  Finite fp16 scales are always in
+// class 1.
+constexpr float kScaleLo = 0x1p-100f, kScaleHi = 0x1p100f, kScaleSpread = 0x1p64f;
 
 // Slot of (column i in tile, group q in chunk) inside a chunk's 16*Q scale /
 // zero-point record.  For Q <= 4 the groups of one column are adjacent; for

@@ -121,6 +121,42 @@ __global__ __launch_bounds__(256) void repack_scales_kernel(const S* __restrict_
     out[idx] = v;
 }
 
+__device__ __forceinline__ float scale_value(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+__device__ __forceinline__ float scale_value(uint32_t b) { return __builtin_bit_cast(float, b); }
+
+// The range class of each tile's scales (see kScaleLo in mnb_layout.hpp):
+// one wave per tile; lane l takes column l % 16 and every fourth group from
+// l / 16, then the four lanes of a column combine their extremes.
+template <typename S>
+__global__ __launch_bounds__(64) void scale_range_kernel(const S* __restrict__ scales,
+                                                         uint8_t* __restrict__ flags, int64_t N,
+                                                         int64_t kb)
+{
+    const int lane = threadIdx.x;
+    const int64_t n = (int64_t)blockIdx.x * kTileN + (lane & 15);
+    float lo = __builtin_inff(), hi = 0.0f;
+    bool bad = false;
+    if (n < N) {
+        for (int64_t b = lane >> 4; b < kb; b += 4) {
+            const float a = __builtin_fabsf(scale_value(scales[n * kb + b]));
+            if (a == 0.0f || a != a) continue;   // zero or NaN: not part of the range
+            bad = bad || !(a >= kScaleLo && a <= kScaleHi);
+            lo = a < lo ? a : lo;
+            hi = a > hi ? a : hi;
+        }
+    }
+#pragma unroll
+    for (int d = 16; d < 64; d *= 2) {
+        const float lo2 = __shfl_xor(lo, d), hi2 = __shfl_xor(hi, d);
+        lo = lo2 < lo ? lo2 : lo;
+        hi = hi2 > hi ? hi2 : hi;
+    }
+    // a column with no range-bounded scale has lo = inf, hi = 0: fine
+    bad = bad || (hi > lo * kScaleSpread);
+    const bool any_bad = __any(bad);
+    if (lane == 0) flags[blockIdx.x] = any_bad ? 0 : 1;
+}
+
 __global__ __launch_bounds__(256) void repack_zp_kernel(const uint8_t* __restrict__ zp,
                                                         uint8_t* __restrict__ out, int64_t N,
                                                         int64_t kb, int Q, int64_t C,
@@ -233,14 +269,20 @@ hipError_t launch_repack(const Layout& L, const uint8_t* packed, const void* sca
         repack_zp_kernel<<<blocks_for(L.zp_bytes), 256, 0, stream>>>(
             zp, base + L.zp_off, L.N, L.kb, L.Q, L.C, L.zp_bytes);
     }
+    if (L.T > 0) {
+        if (L.ss == 2)
+            scale_range_kernel<uint16_t><<<(unsigned)L.T, 64, 0, stream>>>(static_cast<const uint16_t*>(scales),
+                                                                        base + L.flags_off, L.N, L.kb);
+        else
+            scale_range_kernel<uint32_t><<<(unsigned)L.T, 64, 0, stream>>>(static_cast<const uint32_t*>(scales),
+                                                                        base + L.flags_off, L.N, L.kb);
+    }
     zero_gap(base, L.codes_off + L.codes_bytes, L.scales_off, stream);
     const int64_t scales_end = L.scales_off + L.scales_bytes;
-    if (L.has_zp) {
-        zero_gap(base, scales_end, L.zp_off, stream);
-        zero_gap(base, L.zp_off + L.zp_bytes, L.total, stream);
-    } else {
-        zero_gap(base, scales_end, L.total, stream);
-    }
+    const int64_t meta_end = L.has_zp ? L.zp_off + L.zp_bytes : scales_end;
+    if (L.has_zp) zero_gap(base, scales_end, L.zp_off, stream);
+    zero_gap(base, meta_end, L.flags_off, stream);
+    zero_gap(base, L.flags_off + L.flags_bytes, L.total, stream);
     return hipGetLastError();
 }
 

@@ -47,7 +47,8 @@ class mnb_weight_desc(ctypes.Structure):
 class mnb_layout(ctypes.Structure):
     _fields_ = [(name, ctypes.c_int64) for name in (
         "tiles", "chunks", "groups_per_chunk", "codes_offset", "codes_bytes", "scales_offset",
-        "scales_bytes", "zero_points_offset", "zero_points_bytes", "total_bytes")]
+        "scales_bytes", "zero_points_offset", "zero_points_bytes", "range_flags_offset",
+        "range_flags_bytes", "total_bytes")]
 
 
 def _hip_runtimes_mapped():

@@ -76,7 +76,16 @@
  *   Z0 = align(S0 + T*C*16*Q*ss), T*C*8*Q bytes.  Chunk (t,c) owns bytes
  *   [((t*C)+c)*8Q, +8Q); the zero point of slot s is the nibble of byte s/2,
  *   low nibble for even s.  Padding holds 0.
- * Total size mnb_repacked_bytes() = align(end of the last section).
+ * Section RANGE_FLAGS, offset F0 = align(end of the last section above), T
+ *   bytes: byte t is 1 when tile t's scales are in the range class of the
+ *   prefill GEMM's single rescaled accumulator, else 0.  The class: every
+ *   scale of the tile's columns that is neither zero nor NaN has magnitude
+ *   in [2^-100, 2^100], and in each column the largest such magnitude is at
+ *   most 2^64 times the smallest (finite fp16 scales always qualify).  The
+ *   prefill GEMM computes a workgroup with a tile outside the class by a
+ *   slower path with a fresh partial per group; results meet the same bound
+ *   either way.
+ * Total size mnb_repacked_bytes() = align(F0 + T).
  * The 16-lane x 8-k ownership is the B-operand distribution of the gfx950
  * v_mfma_f32_16x16x32_f16 instruction, so the same bytes feed the decode
  * GEMVs (one 128-bit load per lane per chunk) and the MFMA GEMMs.
@@ -118,6 +127,7 @@ typedef struct {
     int64_t codes_offset, codes_bytes;
     int64_t scales_offset, scales_bytes;
     int64_t zero_points_offset, zero_points_bytes; /* 0, 0 without zero points */
+    int64_t range_flags_offset, range_flags_bytes;
     int64_t total_bytes;
 } mnb_layout;
 

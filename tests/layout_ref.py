@@ -20,7 +20,26 @@ def geometry(N, K, g, has_zp, f16_scales):
     S0 = _align(T * C * 1024)
     Z0 = _align(S0 + T * C * 16 * Q * ss)
     end = (Z0 + T * C * 8 * Q) if has_zp else (S0 + T * C * 16 * Q * ss)
-    return dict(T=T, C=C, Q=Q, ss=ss, S0=S0, Z0=Z0 if has_zp else 0, total=_align(end))
+    F0 = _align(end)
+    return dict(T=T, C=C, Q=Q, ss=ss, S0=S0, Z0=Z0 if has_zp else 0, F0=F0, total=_align(F0 + T))
+
+
+def range_flags(scales, N):
+    """Byte per 16-column tile: 1 when every scale of its columns that is
+    neither zero nor NaN has magnitude in [2^-100, 2^100] and each column's
+    largest such magnitude is at most 2^64 times its smallest (the range class
+    stated in the header), else 0."""
+    T = -(-N // 16)
+    a = np.abs(np.asarray(scales, np.float64)).reshape(N, -1)
+    live = (a != 0) & ~np.isnan(a)
+    out = np.ones(T, dtype=np.uint8)
+    for n in range(N):
+        v = a[n][live[n]]
+        if v.size == 0:
+            continue
+        if (v < 2.0 ** -100).any() or (v > 2.0 ** 100).any() or v.max() > v.min() * 2.0 ** 64:
+            out[n // 16] = 0
+    return out
 
 
 # nibble slot p(i) of k-offset i
@@ -70,6 +89,7 @@ def repack_ref(codes, z, scales, g, has_zp):
         zr = zrec.reshape(-1)
         zb = (zr[0::2] | (zr[1::2] << 4)).astype(np.uint8)
         out[G["Z0"]:G["Z0"] + zb.size] = zb
+    out[G["F0"]:G["F0"] + T] = range_flags(scales, N)
     return out
 
 

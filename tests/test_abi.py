@@ -53,12 +53,13 @@ def test_repacked_size_and_layout_match_the_documented_formula(N, K, g, zp, f16)
     assert L["codes_offset"] == 0 and L["codes_bytes"] == G["T"] * G["C"] * 1024
     assert L["scales_offset"] == G["S0"]
     assert L["zero_points_offset"] == G["Z0"]
+    assert L["range_flags_offset"] == G["F0"] and L["range_flags_bytes"] == G["T"]
     assert L["total_bytes"] == G["total"]
     # no expansion beyond tile padding: ONNX bytes vs repacked bytes
     kb = K // g
     onnx = N * K // 2 + N * kb * (2 if f16 else 4) + (N * ((kb + 1) // 2) if zp else 0)
     padded = G["T"] * 16 * G["C"] * 128
-    assert G["total"] <= onnx * padded / (N * K) + 3 * 256 + G["T"] * G["C"] * 16 * 128 // 8
+    assert G["total"] <= onnx * padded / (N * K) + 4 * 256 + G["T"] * G["C"] * 16 * 128 // 8 + G["T"]
 
 
 def test_host_layout_model_is_a_bijection():
@@ -75,6 +76,30 @@ def test_host_layout_model_is_a_bijection():
         G = layout_ref.geometry(N, K, g, True, True)
         nib = np.concatenate([buf[:G["T"] * G["C"] * 1024] & 15, buf[:G["T"] * G["C"] * 1024] >> 4])
         assert np.bincount(nib, minlength=16)[1:].sum() == np.count_nonzero(codes)
+
+
+def test_range_class_model_at_its_edges():
+    # the host model of the repack's per-tile range byte, at the edges of the
+    # stated class: magnitudes in [2^-100, 2^100], spread at most 2^64 per
+    # column, zeros and NaNs not counted, infinities outside
+    def flag(col):
+        s = np.full((16, len(col)), 1.0, np.float64)
+        s[5] = col
+        return int(layout_ref.range_flags(s, 16)[0])
+    assert flag([2.0 ** -100, 2.0 ** -100]) == 1
+    assert flag([2.0 ** -101, 1.0]) == 0
+    assert flag([2.0 ** 100, 2.0 ** 36]) == 1
+    assert flag([2.0 ** 100 * 1.0000001, 1.0]) == 0
+    assert flag([1.0, 2.0 ** 64]) == 1
+    assert flag([1.0, 2.0 ** 64 * (1 + 2 ** -20)]) == 0
+    assert flag([0.0, np.nan, 3.0]) == 1
+    assert flag([np.inf, 1.0]) == 0
+    assert flag([-np.inf, 0.0]) == 0
+    assert flag([-1e-30, 2e-30]) == 1
+    assert flag([1e-39, 1.0]) == 0            # a binary32 subnormal
+    # finite fp16 scales are always in the class
+    h = np.array([[6.0e-8, 65504.0, -1.0, 0.0]], np.float16)
+    assert layout_ref.range_flags(h, 1).tolist() == [1]
 
 
 def _expect(status, call, *args):

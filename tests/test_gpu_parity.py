@@ -677,6 +677,72 @@ def test_zero_and_non_finite_scales(mnb):
             assert (yh[:, 3] == 0).all()
 
 
+def _extreme_scales(N, kb, base, big=False):
+    """fp32 scales [N, kb] from `base` with columns whose groups span extreme
+    ranges: a tiny scale beside ordinary ones (ratio about 2^90), a
+    subnormal one, one at the smallest normal binary32 value beside 0.02, a
+    spread of exactly 2^64 and one of 2^60 (inside the prefill's range
+    class), and with big=True a 1e30 scale beside 1e-30."""
+    s = base.astype(np.float64).copy()
+    s[17, 0] = 1e-30                      # tile 1: ratio ~2^90
+    s[33, 1 % kb] = 1e-39                 # tile 2: subnormal
+    s[66, 0] = 1.1754944e-38              # tile 4: smallest normal beside 0.02
+    s[66, kb - 1] = 0.02
+    s[80, :] = 0.01                       # tile 5: spread exactly 2^64
+    s[80, 0] = 0.01 * 2.0 ** -64
+    s[50, ::2] = 0.01 * 2.0 ** -60        # tile 3: spread 2^60, alternating
+    if big:
+        s[90, 0], s[90, kb - 1] = 1e30, 1e-30
+    return s.astype(np.float32)
+
+
+@pytest.mark.parametrize("K,g", [(512, 128), (512, 32), (400, 16)])
+def test_extreme_scale_ranges(mnb, K, g):
+    """fp32 scales whose magnitudes within a column differ by up to 2^121, or
+    are subnormal, on every path: the GEMV and small-M kernels apply each
+    group's scale to a fresh partial; the prefill GEMM keeps one rescaled
+    accumulator for tiles in its range class (recorded by the repack, checked
+    here against the host model) and computes the other tiles with fresh
+    partials.  Outputs within the bound everywhere."""
+    t = G.torch()
+    N = 96
+    kb = K // g
+    w = _weight(N, K, g, "f32", seed=11)
+    s = _extreme_scales(N, kb, w.scales)
+    w2 = synth.Weight(N, K, g, w.packed, s, w.zero_points)
+    q = G.upload(w2)
+    flags = layout_ref.range_flags(s, N)
+    assert flags.tolist() == [1, 0, 0, 1, 0, 1]
+    Gm = layout_ref.geometry(N, K, g, True, False)
+    assert (q.repacked.cpu().numpy()[Gm["F0"]:Gm["F0"] + Gm["T"]] == flags).all()
+    for M in (1, 8, 40, 200):
+        A = _act(M, K, seed=M + 5)
+        y = t.empty((M, N), dtype=t.float16, device="cuda")
+        G.gemm(q, G.to_dev(A), M, y)
+        Y, B, _ = G.oracle_dense(A, w2)
+        G.assert_within(G.host(y), Y, B, "extreme scales M=%d K=%d g=%d (%s)" % (M, K, g, mnb.mnb_last_variant()))
+
+
+@pytest.mark.parametrize("K,g", [(512, 128), (400, 16)])
+def test_extreme_scale_ranges_int8_activations(mnb, K, g):
+    """The same extreme scales, plus a 1e30 scale beside a 1e-30 one, through
+    the int8-activation product (fp32 outputs hold the large values)."""
+    t = G.torch()
+    N = 96
+    kb = K // g
+    w = _weight(N, K, g, "f32", seed=12)
+    w2 = synth.Weight(N, K, g, w.packed, _extreme_scales(N, kb, w.scales, big=True), w.zero_points)
+    q = G.upload(w2)
+    for M in (1, 8, 40, 200):
+        A = synth.activation(M, K, "f32", 1.0, (205, M, K))
+        ws = t.zeros(max(mnb.mnb_gemm_accuracy4_workspace_bytes(q.desc, M), 256), dtype=t.uint8, device="cuda")
+        y = t.empty((M, N), dtype=t.float32, device="cuda")
+        mnb.mnb_gemm_accuracy4(q.desc, q.repacked, G.to_dev(A), M, None, y, ws, ws.numel())
+        Y, B, _, _ = o.acc4_matmul(A, w2.packed, w2.scales, w2.zero_points, N, K, g)
+        G.assert_within(G.host(y), Y, B, "int8 activations, extreme scales M=%d K=%d g=%d" % (M, K, g),
+                        bound=o.acc4_bound(B, K, g))
+
+
 def test_empty_and_unsupported_requests(mnb):
     t = G.torch()
     w = _weight(64, 256, 32)
