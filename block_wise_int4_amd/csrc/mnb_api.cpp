@@ -469,6 +469,35 @@ mnb_status mnb_gemm_accuracy4(const mnb_weight_desc* w, const void* repacked, co
     return accuracy4_common(w, repacked, a, m, bias, y, workspace, workspace_bytes, stream);
 }
 
+}  // extern "C"
+
+extern "C" {
+
+mnb_status mnb_gemm_accuracy4_noalloc(const mnb_weight_desc* w, const void* repacked, const float* a, int64_t m,
+                                      const float* bias, float* y, void* stream)
+{
+    Layout L;
+    MNB_TRY(check_desc(w, &L));
+    if (m < 0) return fail(MNB_ERR_INVALID_ARGUMENT, "M must be >= 0 (got %lld)", (long long)m);
+    if (m == 0 || L.N == 0) return ok("noop");
+    if (m > INT32_MAX) return fail(MNB_ERR_INVALID_ARGUMENT, "M must fit in 32 bits");
+    if (m > INT64_MAX / 4 / L.K) return fail(MNB_ERR_INVALID_ARGUMENT, "M*K overflows");
+    // the decode GEMV keeps the codes on chip and needs no workspace
+    if (m == 1) return accuracy4_common(w, repacked, a, m, bias, y, nullptr, 0, stream);
+    const size_t need = acc4_scale_bytes(m) + acc4_codes_bytes(L, m) + workspace_for(L, m);
+    if (need > (size_t)MNB_NOALLOC_SCRATCH_BYTES)
+        return fail(MNB_ERR_UNSUPPORTED, "the request needs %zu bytes of workspace; the no-allocation form holds %zu",
+                    need, (size_t)MNB_NOALLOC_SCRATCH_BYTES);
+    MNB_TRY(check_device());
+    int dev = -1;
+    (void)hipGetDevice(&dev);
+    void* ws = nullptr;
+    const hipError_t e = mnb::noalloc_scratch(dev, &ws);
+    if (e != hipSuccess) return fail(MNB_ERR_DEVICE, "cannot locate the scratch array on device %d: %s", dev,
+                                     hipGetErrorString(e));
+    return accuracy4_common(w, repacked, a, m, bias, y, ws, (size_t)MNB_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 mnb_status mnb_unpack_debug(const mnb_weight_desc* w, const void* repacked, uint8_t* codes,
                             float* w_f32, void* stream)
 {

@@ -62,4 +62,9 @@ int64_t gemm_mfma_max_k();
 hipError_t launch_gemm_mfma(const Layout& L, const WeightView& w, const void* a, int64_t m,
                             const Bias& bias, void* y, hipStream_t stream, const char** variant);
 
+// Device address of the no-allocation scratch array on device `dev` (which
+// must be current), MNB_NOALLOC_SCRATCH_BYTES bytes; looked up on the first
+// call per device, then cached.
+hipError_t noalloc_scratch(int dev, void** out);
+
 }  // namespace mnb

@@ -29,6 +29,7 @@ EXPORTS = ("mnb_repacked_bytes", "mnb_repacked_layout", "mnb_repack", "mnb_gemv"
            "mnb_gemv_gate_up_swiglu", "mnb_gemm_workspace_bytes", "mnb_gemm", "mnb_gemm_bias",
            "mnb_act_order_permutation", "mnb_repack_act_order", "mnb_gemm_act_order_workspace_bytes",
            "mnb_gemm_act_order", "mnb_gemm_accuracy4_workspace_bytes", "mnb_gemm_accuracy4",
+           "mnb_gemm_accuracy4_noalloc",
            "mnb_unpack_debug", "mnb_status_string", "mnb_last_error", "mnb_last_variant")
 
 
@@ -91,6 +92,7 @@ def _load():
         "mnb_gemm_act_order": (ctypes.c_int, [D, P, P, i64, i32, P, P, P, sz, P]),
         "mnb_gemm_accuracy4_workspace_bytes": (sz, [D, i64]),
         "mnb_gemm_accuracy4": (ctypes.c_int, [D, P, P, i64, P, P, P, sz, P]),
+        "mnb_gemm_accuracy4_noalloc": (ctypes.c_int, [D, P, P, i64, P, P, P]),
         "mnb_unpack_debug": (ctypes.c_int, [D, P, P, P, P]),
         "mnb_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "mnb_last_error": (ctypes.c_char_p, []),
@@ -259,6 +261,14 @@ def mnb_gemm_accuracy4(w: mnb_weight_desc, repacked: Ptr, a, m: int, bias, y, wo
             workspace.numel() * workspace.element_size()
     _check(lib.mnb_gemm_accuracy4(ctypes.byref(w), _ptr(repacked), _ptr(a), m, _ptr(bias), _ptr(y),
                                   _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+MNB_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def mnb_gemm_accuracy4_noalloc(w: mnb_weight_desc, repacked: Ptr, a, m: int, bias, y, stream=None) -> None:
+    _check(lib.mnb_gemm_accuracy4_noalloc(ctypes.byref(w), _ptr(repacked), _ptr(a), m, _ptr(bias), _ptr(y),
+                                          _stream(stream)))
 
 
 def mnb_unpack_debug(w: mnb_weight_desc, repacked: Ptr, codes: Ptr, w_f32: Ptr, stream=None) -> None:

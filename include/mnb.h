@@ -286,6 +286,24 @@ mnb_status mnb_gemm_accuracy4(const mnb_weight_desc* w, const void* repacked, co
                               const float* bias, float* y, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/* mnb_gemm_accuracy4 without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments (less the workspace),
+ * same kernels, same results.  For M > 1 the int8 codes and row scales go to
+ * a scratch array the library keeps in device memory,
+ * MNB_NOALLOC_SCRATCH_BYTES per device, held until the process ends; its
+ * device address is looked up on the first call on each device (that call
+ * must have the device current, as every call does).  A request whose
+ * workspace (mnb_gemm_accuracy4_workspace_bytes) exceeds the array returns
+ * MNB_ERR_UNSUPPORTED before any HIP call.  No call allocates or frees
+ * memory.  All calls on one device share the array and each leaves its
+ * contents behind: calls that overlap on one device (other streams or
+ * threads) race and give wrong results; calls on different devices do not
+ * interact. */
+#define MNB_NOALLOC_SCRATCH_BYTES (32u << 20)
+mnb_status mnb_gemm_accuracy4_noalloc(const mnb_weight_desc* w, const void* repacked, const float* a,
+                                      int64_t m, const float* bias, float* y, void* stream);
+
 /* Test-only: decode a repacked buffer with the production unpack code.
  * codes: device u8 [N,K] (the stored nibbles); w_f32: device f32 [N,K], the
  * dequantized weights (code - zp) * scale rounded once to fp32.  Either

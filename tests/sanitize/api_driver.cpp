@@ -37,6 +37,7 @@ hipError_t launch_gemm_small_f32(const Layout&, const WeightView&, const void*, 
                                  const float*, float*, void*, hipStream_t, const char**) { std::abort(); }
 hipError_t launch_gemm_mfma_f32(const Layout&, const WeightView&, const void*, int64_t, const float*,
                                 const float*, float*, hipStream_t, const char**) { std::abort(); }
+hipError_t noalloc_scratch(int, void**) { std::abort(); }
 }  // namespace mnb
 
 static int failures = 0;
@@ -118,6 +119,14 @@ int main()
                               nullptr, ws4, nullptr), INV, "int8 workspace NULL");
     expect(mnb_gemm_accuracy4(&d, fake, static_cast<const float*>(fake), 1, nullptr, static_cast<float*>(fake),
                               nullptr, 0, nullptr), DEV, "valid int8 decode without a device");
+    // the no-allocation form: validation, then the size limit, then the device
+    const float* fa = static_cast<const float*>(fake);
+    float* fy = static_cast<float*>(fake);
+    expect(mnb_gemm_accuracy4_noalloc(&d, fake, fa, -1, nullptr, fy, nullptr), INV, "no-alloc negative M");
+    expect(mnb_gemm_accuracy4_noalloc(&d, fake, fa, 0, nullptr, fy, nullptr), MNB_OK, "no-alloc M = 0");
+    expect(mnb_gemm_accuracy4_noalloc(&d, fake, fa, 1 << 20, nullptr, fy, nullptr), UNS, "no-alloc beyond scratch");
+    expect(mnb_gemm_accuracy4_noalloc(&d, fake, fa, 40, nullptr, fy, nullptr), DEV, "no-alloc without a device");
+    expect(mnb_gemm_accuracy4_noalloc(&d, fake, fa, 1, nullptr, fy, nullptr), DEV, "no-alloc decode without a device");
     const size_t wsa = mnb_gemm_act_order_workspace_bytes(&d, 40, MNB_F16);
     expect(mnb_gemm_act_order(&d, fake, fake, 40, MNB_F16, nullptr, fake, fake, wsa, nullptr), INV, "perm NULL");
     expect(mnb_gemm_act_order(&d, fake, fake, 40, MNB_F16, static_cast<const int32_t*>(fake), fake, fake, wsa - 1,
