@@ -4,21 +4,42 @@
 One step = one pass of the whole hot path over the measured workloads, each
 launched on R rotating copies of its operands (weights, activations, outputs)
 so the working set (> 1 GiB per workload) defeats the 256 MB Infinity Cache:
-  decode GEMV      M=1  K=4096 N=4096  g=32  fp16, asymmetric zero points
-  gate/up SwiGLU   M=1  K=4096 N=11008 g=128 fp16 (two weights, fused)
-  small-M GEMM     M=2,4,8,16 K=4096 N=14336 g=64 fp16, asymmetric zero points
+
   prefill GEMM     M=2048 K=4096 N=14336 g=128 fp16, asymmetric zero points
+  (+ the same with an fp16 bias, with act order, and with int8 activations)
+  small-M GEMM     M=2,4,8,16 K=4096 N=14336 g=64 fp16, asymmetric zero points
+  down projection  M=1 K=11008 N=4096 g=128 fp16
+  gate/up SwiGLU   M=1 K=4096 N=11008 g=128 fp16 (two weights, fused)
+  (decode GEMV with act order, with int8 activations, with a bias)
+  tiny GEMV        M=1 K=256 N=256 g=32 fp32 (256 copies: launch-bound)
+  decode GEMV      M=1 K=4096 N=4096 g=32 fp16, asymmetric zero points
+
+The compute-bound GEMMs run first and the decode GEMV last: right after the
+prefill's milliseconds of matrix work the chip runs memory-bound kernels about
+0.8 us slower per launch (its clocks recover over the next milliseconds), so
+the memory-bound kernels that measure the headline run furthest from it.
+
 Each workload's R launches are recorded once into a HIP graph; every step
-replays the graphs, timed with HIP events on the replay stream, so the
-figures are back-to-back GPU time (kernel plus dispatch gap), not the host's
-launch rate.  The headline value is the decode GEMV's effective bandwidth: algorithmic bytes
-(ONNX-layout codes + scales + zero points + A + Y) per launch over the
-average launch duration.  The prefill GEMM is reported in TFLOP/s (2MNK).
-Prints one JSON line.
+replays the graphs, timed with HIP events on the replay stream, so the figures
+are back-to-back GPU time (kernel plus dispatch gap), not the host's launch
+rate.  The headline value is the decode GEMV's effective bandwidth:
+algorithmic bytes (ONNX-layout codes + scales + zero points + A + Y) per
+launch over the average launch duration.  The prefill GEMM is reported in
+TFLOP/s (2MNK).
+
+After the timed steps, outside them: every memory-bound workload's graph is
+replayed alone ("isolated_us"), and a plain streaming read of the same number
+of bytes over as many rotating buffers ("floor_us", the yardstick library) is
+timed the same way; frac_of_floor = floor_us / isolated_us.  The CPU baseline
+leg times the oracle on a bounded sample of each measured configuration and
+checks the GPU's outputs of the timed run on that sample (max |err| / bound,
+pass).  Prints one JSON line.
 """
 import argparse
+import ctypes
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -29,6 +50,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 matrix
 COLD_BYTES = 1 << 30           # rotation working set per workload
+TINY_COPIES = 256              # the 43 KB tiny GEMV is launch-bound
 
 
 def parse():
@@ -37,10 +59,12 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--no-isolated", action="store_true",
+                   help="skip the isolated replays and the streaming-read floors")
+    p.add_argument("--cpu-seconds", type=float, default=8.0)
     p.add_argument("--only", default="",
-                   help="comma list of: gemv,gate_up,down,small_m,prefill,bias,act_order,accuracy4 (default all); "
-                        "copy adds a plain 256 MiB device copy, the reference kernel "
+                   help="comma list of: prefill,small_m,down,gate_up,gemv,tiny,bias,act_order,accuracy4 "
+                        "(default all); copy adds a plain 256 MiB device copy, the reference kernel "
                         "for scaling the HBM byte counters")
     return p.parse_args()
 
@@ -52,6 +76,37 @@ def onnx_bytes(M, K, N, g, scale_bytes, zp, act_bytes, n_weights=1, out_n=None):
     return n_weights * w + M * K * act_bytes + M * out_n * act_bytes
 
 
+def _graph_of(launch):
+    """A HIP graph of launch() recorded on a side stream (first-call setup
+    outside the capture)."""
+    import torch
+    launch()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            launch()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    return graph
+
+
+def _time_isolated(graph, R, reps=6):
+    """us per launch of a graph of R launches replayed alone, back to back."""
+    import torch
+    for _ in range(2):
+        graph.replay()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * R)
+
+
 class CopyWorkload:
     """A plain streaming kernel of known size: torch's elementwise negation
     of a 256 MiB fp16 tensor into another, which reads 256 MiB and writes
@@ -59,13 +114,16 @@ class CopyWorkload:
     scaled by what the same counters read for it (its kernel name is unique
     in the run, unlike the runtime's blit copies)."""
 
+    config = "copy"
+    memory_bound = False
+
     def __init__(self, nbytes=256 << 20):
         import torch
         self.name, self.variant = "plain copy %d MiB" % (nbytes >> 20), "torch neg (copy)"
         self.src = torch.ones(nbytes // 2, dtype=torch.float16, device="cuda:0")
         self.dst = torch.empty_like(self.src)
         self.bytes, self.flops, self.R = 2 * nbytes, 0, 1
-        self.times_ms, self.events = [], []
+        self.events = []
 
     def capture(self):
         pass
@@ -80,29 +138,35 @@ class CopyWorkload:
         if timed:
             self.events.append((e0, e1))
 
-    finish = None  # set below (shares Workload.finish)
+    def keep_output(self):
+        pass
 
 
 class Workload:
-    """R rotating device copies of one workload's operands."""
+    """R rotating device copies of one workload's operands, plus the host
+    operands of copy 0 and, after the run, its output (for the parity check
+    of the CPU baseline leg)."""
 
-    def __init__(self, name, M, weights, K, N, g, act_fp16=True, sigma=1.0, seed=(0,), bias=None,
-                 act_order=False, accuracy4=False):
+    def __init__(self, name, config, M, weights, K, N, g, act="f16", sigma=1.0, seed=(0,), bias=None,
+                 act_order=False, accuracy4=False, copies=None):
+        import numpy as np
         import torch
         from block_wise_int4_amd import mnb, synth
-        self.name, self.M, self.K, self.N, self.g = name, M, K, N, g
+        self.name, self.config, self.M, self.K, self.N, self.g = name, config, M, K, N, g
+        self.weights = weights
         dev = torch.device("cuda:0")
         qs = []
         self.perm = None
+        self.g_idx = None
         for w in weights:
             args = (torch.from_numpy(w.packed.reshape(-1)).to(dev), torch.from_numpy(w.scales.reshape(-1)).to(dev),
                     None if w.zero_points is None else torch.from_numpy(w.zero_points.reshape(-1)).to(dev))
             if act_order:
                 # a seeded act order: every group gets exactly g positions
-                import numpy as np
                 rng = np.random.default_rng(seed + (7,))
                 g_idx = np.empty(K, np.int32)
                 g_idx[rng.permutation(K)] = np.arange(K) // g
+                self.g_idx = g_idx
                 d = mnb.desc(N, K, g, w.zero_points is not None, mnb._dtype_code(args[1]))
                 self.perm = torch.from_numpy(mnb.mnb_act_order_permutation(d, g_idx)).to(dev)
                 out = torch.empty(mnb.mnb_repacked_bytes(d), dtype=torch.uint8, device=dev)
@@ -111,10 +175,12 @@ class Workload:
             else:
                 q = mnb.repack(*args, N, K, g)
             qs.append(q)
-        A = torch.from_numpy(synth.activation(M, K, "f16" if act_fp16 else "f32", sigma, seed)).to(dev)
+        self.A_host = synth.activation(M, K, act, sigma, seed)
+        A = torch.from_numpy(self.A_host).to(dev)
         zp = weights[0].zero_points is not None
         sb = 2 if weights[0].scales.dtype.itemsize == 2 else 4
-        self.bytes = onnx_bytes(M, K, N, g, sb, zp, 2 if act_fp16 else 4, len(weights))
+        ab = 2 if act == "f16" else 4
+        self.bytes = onnx_bytes(M, K, N, g, sb, zp, ab, len(weights))
         # optional bias epilogue: ("vector" | "rows", mode); its fp16 elements
         # count as algorithmic bytes
         self.bias = bias
@@ -132,9 +198,10 @@ class Workload:
         self.flops = 2 * M * N * K * len(weights)
         per_copy = (sum(q.repacked.numel() for q in qs) + A.numel() * A.element_size() * 2
                     + M * N * A.element_size() + bias_rows * N * 2)
-        self.R = max(2, -(-COLD_BYTES // per_copy))
+        self.R = copies if copies is not None else max(2, -(-COLD_BYTES // per_copy))
         self.desc = qs[0].desc
         self.copies = []
+        self.bias_host = None
         for r in range(self.R):
             ws = [q.repacked.clone() for q in qs]
             a = A.clone()
@@ -142,7 +209,10 @@ class Workload:
             b = None
             if bias_rows or accuracy4:
                 gen = torch.Generator().manual_seed(1000 + r)
-                b = torch.randn(max(bias_rows, 1) * N, generator=gen).to(A.dtype).to(dev)
+                bh = torch.randn(max(bias_rows, 1) * N, generator=gen).to(A.dtype)
+                if r == 0:
+                    self.bias_host = bh.numpy()
+                b = bh.to(dev)
             self.copies.append((ws, a, y, b))
         self.ws_bytes = mnb.mnb_gemm_workspace_bytes(self.desc, M) if len(qs) == 1 else 0
         if act_order:
@@ -154,8 +224,10 @@ class Workload:
                            for _ in range(self.R)]
         torch.cuda.synchronize()
         self.fused = len(qs) == 2
-        self.times_ms = []
+        self.memory_bound = M <= 16
+        self.events = []
         self.variant = ""
+        self.y_host = None
 
     def launch_all(self):
         from block_wise_int4_amd import mnb
@@ -178,17 +250,7 @@ class Workload:
     def capture(self):
         """Record the R launches into one HIP graph, so a replay measures the
         GPU (back-to-back kernels) rather than the host's launch rate."""
-        import torch
-        self.launch_all()                      # first-call setup outside capture
-        torch.cuda.synchronize()
-        self.graph = torch.cuda.CUDAGraph()
-        s = torch.cuda.Stream()
-        s.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(s):
-            with torch.cuda.graph(self.graph, stream=s):
-                self.launch_all()
-        torch.cuda.current_stream().wait_stream(s)
-        torch.cuda.synchronize()
+        self.graph = _graph_of(self.launch_all)
 
     def run(self, timed):
         import torch
@@ -199,26 +261,31 @@ class Workload:
         self.graph.replay()
         if timed:
             e1.record()
-            self.events = getattr(self, "events", []) + [(e0, e1)]
+            self.events.append((e0, e1))
 
-    def finish(self):
-        from block_wise_int4_amd import mnb
-        total = sum(a.elapsed_time(b) for a, b in self.events)
-        self.avg_launch_ms = total / (len(self.events) * self.R)
-        s = self.avg_launch_ms * 1e-3
-        return {"workload": self.name, "variant": self.variant, "avg_launch_us": round(s * 1e6, 3),
-                "kernel_source": kernel_source_sha(self.variant),
-                "rotating_copies": self.R, "algorithmic_bytes": self.bytes, "flops": self.flops,
-                "GBps": round(self.bytes / s / 1e9, 1),
-                "hbm_frac": round(self.bytes / s / 1e9 / HBM_PEAK_GBS, 4),
-                "TFLOPs": round(self.flops / s / 1e12, 2),
-                "mfma_frac": round(self.flops / s / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
+    def keep_output(self):
+        import torch
+        torch.cuda.synchronize()
+        self.y_host = self.copies[0][2].float().cpu().numpy().astype("float64")
 
 
-CopyWorkload.finish = Workload.finish
+def finish(w):
+    total = sum(a.elapsed_time(b) for a, b in w.events)
+    s = total / (len(w.events) * w.R) * 1e-3
+    out = {"workload": w.name, "config": w.config, "variant": w.variant, "avg_launch_us": round(s * 1e6, 3),
+           "kernel_source": kernel_source_sha(w.variant), "rotating_copies": w.R,
+           "algorithmic_bytes": w.bytes, "flops": w.flops,
+           "GBps": round(w.bytes / s / 1e9, 1), "hbm_frac": round(w.bytes / s / 1e9 / HBM_PEAK_GBS, 4),
+           "TFLOPs": round(w.flops / s / 1e12, 2),
+           "mfma_frac": round(w.flops / s / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)}
+    kt = kernel_trace(w.name, w.variant)
+    if kt is not None:
+        out["kernel_trace_us"] = kt
+    return out
+
 
 # Source files each variant's kernel is compiled from (its own file plus the
-# shared headers): a counter summary applies only while these are unchanged.
+# shared headers): a profile summary applies only while these are unchanged.
 CSRC = os.path.join(ROOT, "block_wise_int4_amd", "csrc")
 SHARED_HEADERS = ["mnb_device.hpp", "mnb_layout.hpp", "mnb_internal.hpp"]
 VARIANT_SOURCE = {"gemv_accuracy4": "acc4.hip", "gemv": "gemv.hip", "gemm_small": "gemm_small.hip",
@@ -237,70 +304,141 @@ def kernel_source_sha(variant):
     return h.hexdigest()[:16]
 
 
+def _profile_lines(tag):
+    import glob
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.txt"))):
+        with open(path) as fh:
+            for line in fh:
+                if line.startswith(tag + "|"):
+                    yield [x.strip() for x in line.split("|")[1:]]
+
+
 def counted_traffic(workload, variant):
     """HBM bytes per launch of `workload`, from the committed counter summaries
     profiles/*.txt (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter
     reads for the plain copy).  None when no summary covers this workload or
     its kernel source has changed since the counters were taken."""
-    import glob
     sha = kernel_source_sha(variant)
-    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.txt"))):
-        with open(path) as fh:
-            for line in fh:
-                if not line.startswith("traffic|"):
-                    continue
-                _, name, src_sha, nbytes = [x.strip() for x in line.split("|")[:4]]
-                if name == workload and src_sha == sha:
-                    return int(nbytes)
+    for f in _profile_lines("traffic"):
+        if f[0] == workload and f[1] == sha:
+            return int(f[2])
+    return None
+
+
+def kernel_trace(workload, variant):
+    """The rocprofv3 kernel-trace figures (us per dispatch: median, mean) of
+    `workload` from the committed summaries, while its kernel source is
+    unchanged; else None."""
+    sha = kernel_source_sha(variant)
+    for f in _profile_lines("ktrace"):
+        if f[0] == workload and f[1] == sha:
+            return {"median": float(f[2]) / 1e3, "mean": float(f[3]) / 1e3, "dispatches": int(f[4])}
     return None
 
 
 def build_workloads(only):
+    from block_wise_int4_amd import mnb
     from block_wise_int4_amd import synth as S
-    sel = set(x for x in only.split(",") if x) or {"gemv", "gate_up", "down", "small_m", "prefill", "bias",
-                                                   "act_order", "accuracy4"}
+    sel = set(x for x in only.split(",") if x) or {"prefill", "small_m", "down", "gate_up", "gemv", "tiny",
+                                                   "bias", "act_order", "accuracy4"}
     wl = [CopyWorkload()] if "copy" in sel else []
-    if "gemv" in sel:
-        c = S.DECODE_GEMV
-        wl.append(Workload(c.name, 1, [S.workload_weights(c)], c.K, c.N, c.group, seed=c.seed + (1,)))
-    if "gate_up" in sel:
-        c = S.GATE_UP_SWIGLU
-        g, u = S.workload_weights(c)
-        wl.append(Workload(c.name, 1, [g, u], c.K, c.N, c.group, seed=c.seed + (1,)))
-    if "down" in sel:
-        c = S.DOWN_PROJ_GEMV
-        wl.append(Workload(c.name, 1, [S.workload_weights(c)], c.K, c.N, c.group, seed=c.seed + (1,)))
+    # compute-bound GEMMs first ...
+    if "prefill" in sel:
+        c = S.PREFILL_GEMM
+        wl.append(Workload(c.name, "c5", c.M, [S.workload_weights(c)], c.K, c.N, c.group, sigma=c.sigma,
+                           seed=c.seed + (c.M,)))
+    if "bias" in sel:
+        c = S.PREFILL_GEMM
+        wl.append(Workload(c.name + " + bias [N] fp16(fp16(acc)+b)", "N2", c.M, [S.workload_weights(c)],
+                           c.K, c.N, c.group, sigma=c.sigma, seed=c.seed + (c.M,),
+                           bias=("vector", mnb.MNB_BIAS_AFTER_ROUND)))
+    if "act_order" in sel:
+        c = S.PREFILL_GEMM
+        wl.append(Workload(c.name + " act-order", "N3", c.M, [S.workload_weights(c)], c.K, c.N, c.group,
+                           sigma=c.sigma, seed=c.seed + (c.M,), act_order=True))
+    if "accuracy4" in sel:
+        c = S.ACC4_PREFILL
+        wl.append(Workload(c.name + " + bias", "N4", c.M, [S.workload_weights(c)], c.K, c.N, c.group,
+                           act="f32", seed=c.seed + (c.M,), accuracy4=True))
+    # ... then the memory-bound ones, the decode GEMV last
     if "small_m" in sel:
         c = S.SMALL_M_GEMM
         w = S.workload_weights(c)
         for M in S.SMALL_M_VALUES:
-            wl.append(Workload(c.name.replace("small-M", "small-M M=%d" % M), M, [w], c.K, c.N,
+            wl.append(Workload(c.name.replace("small-M", "small-M M=%d" % M), "c4", M, [w], c.K, c.N,
                                c.group, seed=c.seed + (M,)))
-    if "prefill" in sel:
-        c = S.PREFILL_GEMM
-        wl.append(Workload(c.name, c.M, [S.workload_weights(c)], c.K, c.N, c.group, sigma=c.sigma,
-                           seed=c.seed + (c.M,)))
-    if "bias" in sel:
-        from block_wise_int4_amd import mnb
-        c = S.DECODE_GEMV
-        wl.append(Workload(c.name + " + bias [N] fp16(acc+b)", 1, [S.workload_weights(c)], c.K, c.N,
-                           c.group, seed=c.seed + (1,), bias=("vector", mnb.MNB_BIAS_FUSED)))
-        c = S.PREFILL_GEMM
-        wl.append(Workload(c.name + " + bias [N] fp16(fp16(acc)+b)", c.M, [S.workload_weights(c)],
-                           c.K, c.N, c.group, sigma=c.sigma, seed=c.seed + (c.M,),
-                           bias=("vector", mnb.MNB_BIAS_AFTER_ROUND)))
-    if "accuracy4" in sel:
-        for c in (S.ACC4_DECODE, S.ACC4_PREFILL):
-            wl.append(Workload(c.name + " + bias", c.M, [S.workload_weights(c)], c.K, c.N, c.group,
-                               act_fp16=False, seed=c.seed + (c.M,), accuracy4=True))
+    if "down" in sel:
+        c = S.DOWN_PROJ_GEMV
+        wl.append(Workload(c.name, "N1", 1, [S.workload_weights(c)], c.K, c.N, c.group, seed=c.seed + (1,)))
+    if "gate_up" in sel:
+        c = S.GATE_UP_SWIGLU
+        g, u = S.workload_weights(c)
+        wl.append(Workload(c.name, "c3", 1, [g, u], c.K, c.N, c.group, seed=c.seed + (1,)))
     if "act_order" in sel:
         c = S.DECODE_GEMV
-        wl.append(Workload(c.name + " act-order", 1, [S.workload_weights(c)], c.K, c.N, c.group,
+        wl.append(Workload(c.name + " act-order", "N3", 1, [S.workload_weights(c)], c.K, c.N, c.group,
                            seed=c.seed + (1,), act_order=True))
-        c = S.PREFILL_GEMM
-        wl.append(Workload(c.name + " act-order", c.M, [S.workload_weights(c)], c.K, c.N, c.group,
-                           sigma=c.sigma, seed=c.seed + (c.M,), act_order=True))
+    if "accuracy4" in sel:
+        c = S.ACC4_DECODE
+        wl.append(Workload(c.name + " + bias", "N4", c.M, [S.workload_weights(c)], c.K, c.N, c.group,
+                           act="f32", seed=c.seed + (c.M,), accuracy4=True))
+    if "bias" in sel:
+        c = S.DECODE_GEMV
+        wl.append(Workload(c.name + " + bias [N] fp16(acc+b)", "N2", 1, [S.workload_weights(c)], c.K, c.N,
+                           c.group, seed=c.seed + (1,), bias=("vector", mnb.MNB_BIAS_FUSED)))
+    if "tiny" in sel:
+        c = S.TINY_GEMV
+        wl.append(Workload(c.name, "c1", 1, [S.workload_weights(c)], c.K, c.N, c.group, act="f32",
+                           seed=c.seed + (1,), copies=TINY_COPIES))
+    if "gemv" in sel:
+        c = S.DECODE_GEMV
+        wl.append(Workload(c.name, "c2", 1, [S.workload_weights(c)], c.K, c.N, c.group, seed=c.seed + (1,)))
     return wl
+
+
+class Yardstick:
+    """bench's streaming-read floor: the plain read kernel of
+    libmnb_yardstick.so over R rotating buffers of a workload's byte count,
+    recorded into a HIP graph and replayed alone, at a few grid shapes (the
+    best counts)."""
+
+    GRIDS = ((512, 512), (1024, 512), (2048, 512), (2048, 1024))
+
+    def __init__(self):
+        import torch
+        from block_wise_int4_amd import build as B
+        if not os.path.exists(B.YARDSTICK_LIB):
+            raise ImportError("libmnb_yardstick.so is not built; run `python -m block_wise_int4_amd.build`")
+        self.lib = ctypes.CDLL(B.YARDSTICK_LIB)
+        self.lib.mnb_yardstick_read.restype = ctypes.c_int
+        self.lib.mnb_yardstick_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                                                ctypes.c_int32, ctypes.c_void_p]
+        self.sink = torch.zeros(4096, dtype=torch.int32, device="cuda:0")
+        self.cache = {}
+
+    def floor_us(self, nbytes):
+        import torch
+        nbytes = nbytes // 16 * 16
+        if nbytes in self.cache:
+            return self.cache[nbytes]
+        R = max(2, -(-COLD_BYTES // nbytes)) if nbytes >= (1 << 20) else TINY_COPIES
+        bufs = [torch.ones(nbytes // 4, dtype=torch.int32, device="cuda:0") for _ in range(R)]
+        best = None
+        for blocks, threads in self.GRIDS:
+            def launch():
+                s = torch.cuda.current_stream().cuda_stream
+                for b in bufs:
+                    rc = self.lib.mnb_yardstick_read(ctypes.c_void_p(b.data_ptr()), nbytes,
+                                                     ctypes.c_void_p(self.sink.data_ptr()), blocks, threads,
+                                                     ctypes.c_void_p(s))
+                    if rc != 0:
+                        raise RuntimeError("yardstick launch failed (%d)" % rc)
+            us = _time_isolated(_graph_of(launch), R)
+            best = us if best is None or us < best else best
+        del bufs
+        torch.cuda.empty_cache()
+        self.cache[nbytes] = round(best, 3)
+        return self.cache[nbytes]
 
 
 def time_repack():
@@ -332,10 +470,30 @@ def time_repack():
     return out
 
 
-def cpu_baseline(seconds):
+def _cpu_model():
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(seconds, workloads):
     """The oracle as it stands (C, fp64, OpenMP over outputs) on the host
-    cores: the decode GEMV workload in full, repeated for about `seconds`,
-    and a bounded row sample of the prefill GEMM."""
+    cores: the decode GEMV in full, repeated for about `seconds` (and on one
+    thread), then a bounded sample of each measured configuration, each timed
+    and compared with the GPU's outputs of the timed run on the same outputs
+    (max |err| / bound and pass, under the tests' bounds)."""
     import numpy as np
     from block_wise_int4_amd import synth as S
     from oracle import oracle as o
@@ -352,7 +510,6 @@ def cpu_baseline(seconds):
             break
     gemv_s = (time.perf_counter() - t0) / reps
     bytes_ = onnx_bytes(1, c.K, c.N, c.group, 2, True, 2)
-    # the same call on one thread
     t0 = time.perf_counter()
     reps1 = 0
     while True:
@@ -361,23 +518,57 @@ def cpu_baseline(seconds):
         if time.perf_counter() - t0 > seconds * 0.2:
             break
     gemv1_s = (time.perf_counter() - t0) / reps1
-    p = S.PREFILL_GEMM
-    wp = S.workload_weights(p)
-    rows = 8
-    Ap = S.activation(rows, p.K, "f16", p.sigma, p.seed + (rows,))
-    t0 = time.perf_counter()
-    o.matmul_nbits(Ap, wp.packed, wp.scales, wp.zero_points, p.N, p.K, p.group, threads=threads)
-    gemm_s = time.perf_counter() - t0
+
+    rng = np.random.default_rng(99)
+    per_config = []
+    gemm_rate = None
+    for wk in workloads:
+        if not isinstance(wk, Workload) or wk.y_host is None or wk.config not in ("c1", "c2", "c3", "c4", "c5", "N1"):
+            continue
+        ws = wk.weights
+        t0 = time.perf_counter()
+        if wk.fused:
+            Yg, Bg = o.matmul_nbits(wk.A_host, ws[0].packed, ws[0].scales, ws[0].zero_points, wk.N, wk.K, wk.g,
+                                    threads=threads)
+            Yu, Bu = o.matmul_nbits(wk.A_host, ws[1].packed, ws[1].scales, ws[1].zero_points, wk.N, wk.K, wk.g,
+                                    threads=threads)
+            Y = o.swiglu(Yg, Yu)
+            tol = o.swiglu_bound(Yg, Bg, Yu, Bu)
+            got, sample = wk.y_host, "every output"
+        elif wk.M > 16:
+            # the first 8 rows in full and 4096 outputs drawn from the rest
+            rows = 8
+            ms = np.concatenate([np.repeat(np.arange(rows), wk.N), rng.integers(rows, wk.M, 4096)])
+            ns = np.concatenate([np.tile(np.arange(wk.N), rows), rng.integers(0, wk.N, 4096)])
+            Y, B = o.matmul_nbits_at(wk.A_host, ws[0].packed, ws[0].scales, ws[0].zero_points, wk.N, wk.K, wk.g,
+                                     ms, ns, threads=threads)
+            tol = o.REL_TOL * B + o.ABS_TOL
+            got, sample = wk.y_host[ms, ns], "rows 0..%d in full and 4096 random outputs" % (rows - 1)
+            gemm_rate = 2.0 * ms.size * wk.K / (time.perf_counter() - t0) / 1e12
+        else:
+            Y, B = o.matmul_nbits(wk.A_host, ws[0].packed, ws[0].scales, ws[0].zero_points, wk.N, wk.K, wk.g,
+                                  threads=threads)
+            tol = o.REL_TOL * B + o.ABS_TOL
+            got, sample = wk.y_host, "every output"
+        secs = time.perf_counter() - t0
+        got = np.asarray(got, np.float64).reshape(np.shape(Y))
+        ok = o.within_bound(got, Y, None, tol=tol)
+        fin = np.isfinite(Y) & (tol > 0)
+        r = float(np.max(np.abs(got[fin] - Y[fin]) / tol[fin])) if fin.any() else 0.0
+        per_config.append({"workload": wk.name, "config": wk.config, "oracle_s": round(secs, 3),
+                           "sample": sample, "outputs": int(np.size(Y)), "of": wk.M * wk.N,
+                           "max_err_over_bound": round(r, 4), "pass": bool(ok.all())})
     return {"value": round(bytes_ / gemv_s / 1e9, 3), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": _cpu_model(),
             "sample": "decode GEMV M=1 K=4096 N=4096 g=32 in full, %d repetitions (%.2f ms each)"
                       % (reps, gemv_s * 1e3),
             "one_thread": {"value": round(bytes_ / gemv1_s / 1e9, 3), "unit": "GB/s",
                            "sample": "the same call on 1 thread, %d repetitions (%.2f ms each)"
                                      % (reps1, gemv1_s * 1e3)},
-            "gemm": {"value": round(2 * rows * p.N * p.K / gemm_s / 1e12, 5), "unit": "TFLOP/s",
-                     "sample": "prefill GEMM rows 0..%d of M=2048 (K=4096 N=14336 g=128), %.2f s"
-                               % (rows - 1, gemm_s)}}
+            "gemm": None if gemm_rate is None else
+            {"value": round(gemm_rate, 5), "unit": "TFLOP/s",
+             "sample": "the prefill GEMM's parity sample below (2K FLOPs per output)"},
+            "configs": per_config}
 
 
 def main():
@@ -403,10 +594,22 @@ def main():
             w.run(timed=True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    res = {w.name: w.finish() for w in wls}
+    for w in wls:
+        w.keep_output()
+    res = {w.name: finish(w) if isinstance(w, Workload) else finish_copy(w) for w in wls}
 
-    head = next((r for r in res.values() if r["workload"].startswith("decode GEMV")), None)
-    gemm = next((r for r in res.values() if r["workload"].startswith("prefill GEMM")), None)
+    # outside the timed steps: each memory-bound workload alone, and its floor
+    if not args.no_isolated:
+        yard = Yardstick()
+        for w in wls:
+            if isinstance(w, Workload) and w.memory_bound:
+                r = res[w.name]
+                r["isolated_us"] = round(_time_isolated(w.graph, w.R), 3)
+                r["floor_us"] = yard.floor_us(w.bytes)
+                r["frac_of_floor"] = round(r["floor_us"] / r["isolated_us"], 4)
+
+    head = next((r for r in res.values() if r["config"] == "c2"), None)
+    gemm = next((r for r in res.values() if r["config"] == "c5"), None)
 
     def roof(r, bound):
         if r is None:
@@ -446,8 +649,21 @@ def main():
     }
     out["repack"] = time_repack()
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        cb = cpu_baseline(args.cpu_seconds, wls)
+        out["cpu_baseline"] = cb
+        by_name = {c["workload"]: c for c in cb["configs"]}
+        for r in out["workloads"]:
+            c = by_name.get(r["workload"])
+            if c is not None:
+                r["parity"] = {k: c[k] for k in ("outputs", "of", "max_err_over_bound", "pass")}
     print(json.dumps(out))
+
+
+def finish_copy(w):
+    total = sum(a.elapsed_time(b) for a, b in w.events)
+    s = total / len(w.events) * 1e-3
+    return {"workload": w.name, "config": w.config, "variant": w.variant, "avg_launch_us": round(s * 1e6, 3),
+            "algorithmic_bytes": w.bytes, "GBps": round(w.bytes / s / 1e9, 1)}
 
 
 if __name__ == "__main__":

@@ -31,7 +31,7 @@ def _asm(src, tmp):
 
 @pytest.mark.skipif(not os.path.exists(B.HIPCC) and shutil.which("hipcc") is None, reason="hipcc missing")
 def test_generated_code_keeps_the_rules(tmp_path):
-    srcs = [os.path.join(B.CSRC, f) for f in B.SOURCES if f.endswith(".hip")]
+    srcs = [os.path.join(B.CSRC, f) for f in B.SOURCES + [B.YARDSTICK_SRC] if f.endswith(".hip")]
     with cf.ThreadPoolExecutor(max_workers=min(len(srcs), 8)) as ex:
         outs = list(ex.map(lambda s: _asm(s, str(tmp_path)), srcs))
     bad = []
