@@ -373,25 +373,56 @@ void oracle_dequant_gidx(const uint8_t* packed, const double* scales, const uint
 
 /* ---- int8 activations, accuracy_level 4 [ACC4] --------------------------- */
 
-/* One row of A to int8: scale = max|a| / 127 and q[k] = round(clamp(a[k] / scale))
- * in the binary32 steps of the pages: the maximum skips NaN (as fmaxf does),
- * the reciprocal and the product are binary32 operations, the clamp keeps the
- * non-NaN bound (so a NaN activation becomes -127), and the rounding sends
- * halves away from zero.  A row whose maximum is 0 gets scale 0 and all-zero
- * codes. */
+/* The int8 activation codes of accuracy_level 4 (the quantize kernel of
+ * onnx-runtime-ep-cuda 0.1.0-dev.3, src/kernels/matmul_nbits.rs,
+ * matmul_nbits_quantize_accuracy4_block32), from the rule it implements:
+ * one binary32 scale per row, the largest magnitude over 127, and each code
+ * the binary32 value a * (1/scale) clamped to [-127, 127] and rounded to the
+ * nearest integer, halves away from zero.  The binary32 operations are
+ * evaluated exactly in binary64 and rounded once to binary32 (exact for a
+ * product of two binary32 values; for a quotient, rounding binary64 to
+ * binary32 is innocuous since 53 >= 2*24 + 2), so every step below is the
+ * correctly rounded binary32 result.  Readings: a NaN takes no part in the
+ * maximum, and the clamp sends it to -127; a row whose largest magnitude is 0
+ * has scale 0 and codes 0; an overflowing reciprocal is +inf and the codes
+ * follow from it (nonzero values +-127, zeros -127 since 0 * inf is NaN). */
+
+static float b32_quotient(float x, float y) { return (float)((double)x / (double)y); }
+static float b32_product(float x, float y) { return (float)((double)x * (double)y); }
+
+/* nearest integer, halves away from zero; |x| <= 127 here, so x + 0.5 is
+ * exact in binary64 */
+static int nearest_away(float x)
+{
+    const double m = floor(fabs((double)x) + 0.5);
+    return x < 0 ? -(int)m : (int)m;
+}
+
+static float largest_magnitude(const float* a, int64_t K)
+{
+    float best = 0.0f;
+    for (int64_t k = 0; k < K; ++k) {
+        const float v = a[k] < 0 ? -a[k] : a[k];
+        if (v == v && v > best) best = v;   /* NaN compares false */
+    }
+    return best;
+}
+
 void oracle_acc4_quantize_row(const float* a, int64_t K, int8_t* q, float* scale)
 {
-    float max_abs = 0.0f;
-    for (int64_t k = 0; k < K; ++k) max_abs = fmaxf(max_abs, fabsf(a[k]));
-    const float s = max_abs == 0.0f ? 0.0f : max_abs / 127.0f;
-    const float inv = s == 0.0f ? 0.0f : 1.0f / s;
+    const float top = largest_magnitude(a, K);
+    if (top == 0.0f) {
+        for (int64_t k = 0; k < K; ++k) q[k] = 0;
+        *scale = 0.0f;
+        return;
+    }
+    const float s = b32_quotient(top, 127.0f);
+    const float inv = b32_quotient(1.0f, s);
     for (int64_t k = 0; k < K; ++k) {
-        int v = 0;
-        if (s != 0.0f) {
-            const float x = a[k] * inv;
-            v = (int)roundf(fminf(127.0f, fmaxf(-127.0f, x)));
-        }
-        q[k] = (int8_t)v;
+        float x = b32_product(a[k], inv);
+        if (!(x >= -127.0f)) x = -127.0f;   /* below the range, or NaN */
+        if (x > 127.0f) x = 127.0f;
+        q[k] = (int8_t)nearest_away(x);
     }
     *scale = s;
 }

@@ -267,9 +267,11 @@ def bias_epilogue_f16(acc, bias, after_round: bool) -> np.ndarray:
 def bias_bound(Y: np.ndarray, Bnd: np.ndarray, bias64: np.ndarray) -> np.ndarray:
     """Tolerance of a biased fp16 output against Y + b (fp64), a reading: the
     matmul's own rule for the accumulator, then one binary32 addition and one
-    binary16 rounding of the sum (together at most 2^-10 of its magnitude)."""
+    binary16 rounding of the sum (together at most 2^-10 of its magnitude,
+    plus half the binary16 subnormal spacing, 2^-25, for sums below the
+    binary16 normal range)."""
     e = REL_TOL * np.asarray(Bnd, np.float64) + ABS_TOL
-    return e + 2.0 ** -10 * (np.abs(np.asarray(Y, np.float64) + bias64) + e)
+    return e + 2.0 ** -10 * (np.abs(np.asarray(Y, np.float64) + bias64) + e) + 2.0 ** -25
 
 
 # ---- int8 activations (accuracy_level 4) -----------------------------------

@@ -463,6 +463,73 @@ def test_custom_bound_rejects_values_against_an_infinite_expectation():
         G.assert_within(np.array([[1.6]]), np.array([[1.0]]), None, "fin", bound=np.array([[0.5]]))
 
 
+def _f16(x):
+    with np.errstate(over="ignore"):
+        return np.asarray(x, np.float32).astype(np.float16).astype(np.float32)
+
+
+def test_swiglu_bound_covers_the_pages_two_op_order():
+    """The fused output's bound (reading r7) admits the pages' two-operator
+    order (matmul_nbits.rs, the fp16 gate/up SwiGLU GEMV and its bit-exact
+    test against the two-op path: gate and up each rounded to fp16, silu and
+    the product in fp32, then fp16) as well as one fp16 rounding of the fp32
+    silu(g)*u, for accumulators anywhere inside the matmul bound of G and U:
+    the extremes of that bound and random points inside it, over gate values
+    from -60 to 60 and up values of every sign and size."""
+    rng = np.random.default_rng(41)
+    for scale in (1e-3, 0.1, 1.0, 8.0, 60.0):
+        n = 200000
+        G = rng.standard_normal(n) * scale
+        U = rng.standard_normal(n) * scale * rng.choice([1e-2, 1.0, 30.0], n)
+        BG = np.abs(G) * (1 + 20 * rng.random(n)) + rng.random(n) * scale
+        BU = np.abs(U) * (1 + 20 * rng.random(n)) + rng.random(n) * scale
+        # outputs (and projections) that binary16 represents
+        keep = (np.abs(G) < 3e4) & (np.abs(U) < 3e4) & (np.abs(o.swiglu(G, U)) < 3e4)
+        G, U, BG, BU = G[keep], U[keep], BG[keep], BU[keep]
+        n = G.size
+        S = o.swiglu(G, U)
+        tol = o.swiglu_bound(G, BG, U, BU)
+        Eg = o.REL_TOL * BG + o.ABS_TOL
+        Eu = o.REL_TOL * BU + o.ABS_TOL
+        for pick in (-1.0, 1.0, None):
+            dg = Eg * (rng.uniform(-1, 1, n) if pick is None else pick)
+            du = Eu * (rng.uniform(-1, 1, n) if pick is None else -pick)
+            g32 = (G + dg).astype(np.float32)
+            u32 = (U + du).astype(np.float32)
+            with np.errstate(over="ignore"):
+                # two-op order: g, u to fp16; silu and the product in fp32
+                gh, uh = _f16(g32), _f16(u32)
+                two_op = _f16(np.float32(gh / (np.float32(1) + np.exp(-gh))) * uh)
+                # one rounding: silu(g) * u in fp32, then fp16
+                fused = _f16(np.float32(g32 / (np.float32(1) + np.exp(-g32))) * u32)
+            for name, out in (("two-op", two_op), ("fused", fused)):
+                ok = o.within_bound(out.astype(np.float64), S, None, tol=tol)
+                assert ok.all(), (name, scale, pick, np.argwhere(~ok)[:3])
+
+
+def test_bias_bound_covers_the_fused_bias_order():
+    """The biased output's bound (reading r18) admits the pages' fused bias
+    epilogue (matmul_nbits.rs, fold_bias_f16: the fp32 accumulator plus the
+    fp16 bias in fp32, rounded once to fp16) for accumulators anywhere inside
+    the matmul bound, including sums that cancel to nearly zero."""
+    rng = np.random.default_rng(43)
+    n = 200000
+    for scale in (1e-4, 1e-2, 1.0, 30.0, 2000.0):
+        Y = np.clip(rng.standard_normal(n) * scale, -2e4, 2e4)
+        B = np.abs(Y) * (1 + 20 * rng.random(n)) + rng.random(n) * scale
+        b16 = _f16(rng.standard_normal(n) * scale)
+        b16[: n // 10] = _f16(-Y[: n // 10])           # sums that cancel
+        b64 = b16.astype(np.float64)
+        tol = o.bias_bound(Y, B, b64)
+        E = o.REL_TOL * B + o.ABS_TOL
+        for pick in (-1.0, 1.0, None):
+            d = E * (rng.uniform(-1, 1, n) if pick is None else pick)
+            acc = (Y + d).astype(np.float32)
+            out = _f16(np.float32(acc + b16))
+            ok = o.within_bound(out.astype(np.float64), Y + b64, None, tol=tol)
+            assert ok.all(), (scale, pick, np.argwhere(~ok)[:3])
+
+
 def test_acc4_bound_covers_the_pages_binary32_orders():
     """The int8-activation tolerance holds for both binary32 evaluation orders
     the pages' kernels use (matmul_nbits.rs, matmul_nbits_accuracy4): the sum
@@ -539,10 +606,11 @@ MUTANTS = {
     "act-order scale by block": ("* scales[n * kb + grp];", "* scales[n * kb + k / g];"),
     "act-order zero point by block": ("oracle_zero_point(zero_points, n, grp, kb);",
                                       "oracle_zero_point(zero_points, n, k / g, kb);"),
-    "int8 codes ties to even": ("v = (int)roundf(", "v = (int)rintf("),
-    "int8 codes truncated": ("v = (int)roundf(", "v = (int)truncf("),
-    "int8 scale max/128": ("max_abs / 127.0f", "max_abs / 128.0f"),
-    "int8 clamp at -128": ("fmaxf(-127.0f, x)", "fmaxf(-128.0f, x)"),
+    "int8 codes ties to even": ("floor(fabs((double)x) + 0.5)", "nearbyint(fabs((double)x))"),
+    "int8 codes truncated": ("floor(fabs((double)x) + 0.5)", "floor(fabs((double)x))"),
+    "int8 scale max/128": ("b32_quotient(top, 127.0f)", "b32_quotient(top, 128.0f)"),
+    "int8 clamp at -128": ("if (!(x >= -127.0f)) x = -127.0f;", "if (!(x >= -128.0f)) x = -128.0f;"),
+    "int8 NaN skipped by the clamp too": ("if (!(x >= -127.0f)) x = -127.0f;", "if (x < -127.0f) x = -127.0f;"),
     "int8 dot without zero point": ("(oracle_code(packed, n, k, K, g) - zp)", "oracle_code(packed, n, k, K, g)"),
     "int8 product without activation scale": ("const double y = sa != 0.0 ? sa * inner", "const double y = sa != 0.0 ? inner"),
     "int8 weight scale of block 0": ("const double term = scales[n * kb + blk]", "const double term = scales[n * kb]"),
