@@ -24,8 +24,10 @@
 // * Per-group scaling with a single accumulator per output: while group g
 //   accumulates, acc holds total / s_g; entering group g+1 it is multiplied
 //   by s_g / s_{g+1}, and after the last group the output is acc * s_last.
-//   The ratio is a correctly rounded division; each rescale adds two fp32
-//   roundings (the ratio and the product).  A group with
+//   For fp32 outputs (int8 activations) the ratio is a correctly rounded
+//   division and each rescale adds two fp32 roundings (the ratio and the
+//   product); for fp16 outputs it is the product with v_rcp_f32 (1 ulp), a
+//   relative error of at most 2^-22 per rescale.  A group with
 //   scale 0 gets all-zero B operands (it adds exactly nothing, NaN for
 //   infinite activations as (c - z) * 0 * a does) and keeps the units; the
 //   padding past K is such a group.  Half the registers of a separate group
@@ -84,6 +86,10 @@ struct GemmParams {
     float* y32;
     const float* row_scale;
     const float* bias32;
+    int64_t bias32_stride;  // fp32 bias element (m, n) at bias32[m * stride + n]
+    // fp32 activations split into row pairs (hi, lo): output row m is
+    // row_scale[m] * (acc[2m] + acc[2m + 1])
+    int pair_rows;
     int M, N, K, C;
     int T;                 // column tiles
     int num_m, num_n;      // workgroup grid
@@ -351,7 +357,14 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
             for (int g = 0; g < Q; ++g) {
                 const int sl = slot_of(i, g, Q);
                 const float sg = to_f32(srec[sl]);
-                rt[q][g] = sg != 0.f ? __fdiv_rn(unit[q], sg) : 1.f;
+                // the int8-activation (fp32 output) form, whose bound counts
+                // roundings, divides correctly rounded; the fp16 output's
+                // bound (1e-3 of the magnitude sum) leaves room for the
+                // reciprocal's 1-ulp error
+                if constexpr (F32OUT)
+                    rt[q][g] = sg != 0.f ? __fdiv_rn(unit[q], sg) : 1.f;
+                else
+                    rt[q][g] = sg != 0.f ? unit[q] * __builtin_amdgcn_rcpf(sg) : 1.f;
                 unit[q] = sg != 0.f ? sg : unit[q];
                 uint32_t zv = 8u;
                 if (HAS_ZP) {
@@ -623,6 +636,29 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
     // ---- epilogue: lane holds column (lane & 31) of each 32x32 block, rows
     // 8*(e/4) + 4*oct + e%4
     if constexpr (F32OUT) {
+        if (p.pair_rows) {
+            // fp32 activations as (hi, lo) row pairs: rows 2m and 2m + 1 of
+            // the block sit in the same lane (elements e and e + 1, e even,
+            // since m0 and the other row offsets are even); each output is
+            // stored on its own
+#pragma unroll
+            for (int q = 0; q < PAIRS; ++q) {
+                const int n = nb * BN + wave * 64 + q * 32 + (lane & 31);
+                if (n >= p.N) continue;
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                    for (int e = 0; e < 16; e += 2) {
+                        const int m = m0 + rb * 32 + 8 * (e >> 2) + 4 * oct + (e & 3);
+                        if (m >= p.M) continue;
+                        const int mo = m >> 1;
+                        float v = (acc[rb][q][e] + acc[rb][q][e + 1]) * p.row_scale[mo];
+                        if (p.bias32) v = v + p.bias32[(int64_t)mo * p.bias32_stride + n];
+                        p.y32[(int64_t)mo * p.N + n] = v;
+                    }
+            }
+            return;
+        }
         // fp32 outputs: the row's activation scale, then the bias; the
         // lane's row scales are loaded before any is used
         float rs[RB][16];
@@ -830,6 +866,8 @@ hipError_t launch_gemm_mfma(const Layout& L, const WeightView& w, const void* a,
     p.y32 = nullptr;
     p.row_scale = nullptr;
     p.bias32 = nullptr;
+    p.bias32_stride = 0;
+    p.pair_rows = 0;
     p.w = w.codes;   // the codes section starts the repacked buffer
     p.scales_off = L.scales_off;
     p.zp_off = L.zp_off;
@@ -856,7 +894,7 @@ hipError_t launch_gemm_mfma(const Layout& L, const WeightView& w, const void* a,
 
 hipError_t launch_gemm_mfma_f32(const Layout& L, const WeightView& w, const void* a16, int64_t m,
                                 const float* row_scale, const float* bias, float* y, hipStream_t stream,
-                                const char** variant)
+                                const char** variant, int pair_rows, int64_t bias_stride)
 {
     GemmParams p;
     p.w = w.codes;
@@ -871,6 +909,8 @@ hipError_t launch_gemm_mfma_f32(const Layout& L, const WeightView& w, const void
     p.y32 = y;
     p.row_scale = row_scale;
     p.bias32 = bias;
+    p.bias32_stride = bias_stride;
+    p.pair_rows = pair_rows;
     p.M = (int)m;
     p.N = (int)L.N;
     p.K = (int)L.K;
@@ -880,7 +920,7 @@ hipError_t launch_gemm_mfma_f32(const Layout& L, const WeightView& w, const void
     p.num_n = (int)((L.N + BN - 1) / BN);
     p.vec_store = (L.N % 4 == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0) ? 1 : 0;
     p.flags_off = L.flags_off;
-    if (variant) *variant = "gemm_mfma_32x32x16_accuracy4";
+    if (variant) *variant = pair_rows ? "gemm_mfma_32x32x16_f32act" : "gemm_mfma_32x32x16_accuracy4";
     if (L.ss == 2)
         return L.has_zp ? launch_q<__half, true>(L, p, stream) : launch_q<__half, false>(L, p, stream);
     return L.has_zp ? launch_q<float, true>(L, p, stream) : launch_q<float, false>(L, p, stream);

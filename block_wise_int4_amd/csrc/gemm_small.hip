@@ -42,6 +42,10 @@ struct SmallParams {
     float* y32;
     const float* row_scale;
     const float* bias32;
+    int64_t bias32_stride;  // fp32 bias element (m, n) at bias32[m * stride + n]
+    // fp32 activations split into row pairs (hi, lo): output row m is
+    // row_scale[m] * (acc[2m] + acc[2m + 1])
+    int pair_rows;
     int M, N, K, C;
     int64_t T;
 };
@@ -185,6 +189,22 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_small_kernel(SmallParams p)
         const int e = o & 255;
         const int row = e >> 4, col = e & 15;
         const int64_t n = (t0 + tt) * kTileN + col;
+        if (p.pair_rows) {
+            // rows 2r and 2r + 1 hold the hi and lo parts of output row r
+            if ((row & 1) == 0 && row < p.M && n < p.N) {
+                float v = 0.0f, v2 = 0.0f;
+#pragma unroll
+                for (int w = 0; w < kWaves; ++w) {
+                    v += red[w][tt][e];
+                    v2 += red[w][tt][e + 16];
+                }
+                const int mo = row >> 1;
+                float out = (v + v2) * p.row_scale[mo];
+                if (p.bias32) out = out + p.bias32[(int64_t)mo * p.bias32_stride + n];
+                p.y32[(int64_t)mo * p.N + n] = out;
+            }
+            continue;
+        }
         if (row < p.M && n < p.N) {
             float v = 0.0f;
 #pragma unroll
@@ -232,6 +252,8 @@ hipError_t launch_gemm_small(const Layout& L, const WeightView& w, const void* a
     p.y32 = nullptr;
     p.row_scale = nullptr;
     p.bias32 = nullptr;
+    p.bias32_stride = 0;
+    p.pair_rows = 0;
     p.codes = reinterpret_cast<const u4_t*>(w.codes);
     p.scales = w.scales;
     p.zp = w.zp;
@@ -253,7 +275,7 @@ hipError_t launch_gemm_small(const Layout& L, const WeightView& w, const void* a
 
 hipError_t launch_gemm_small_f32(const Layout& L, const WeightView& w, const void* a16, int64_t m,
                                  const float* row_scale, const float* bias, float* y, void*,
-                                 hipStream_t stream, const char** variant)
+                                 hipStream_t stream, const char** variant, int pair_rows, int64_t bias_stride)
 {
     SmallParams p;
     p.codes = reinterpret_cast<const u4_t*>(w.codes);
@@ -267,12 +289,14 @@ hipError_t launch_gemm_small_f32(const Layout& L, const WeightView& w, const voi
     p.y32 = y;
     p.row_scale = row_scale;
     p.bias32 = bias;
+    p.bias32_stride = bias_stride;
+    p.pair_rows = pair_rows;
     p.M = (int)m;
     p.N = (int)L.N;
     p.K = (int)L.K;
     p.C = (int)L.C;
     p.T = L.T;
-    if (variant) *variant = "gemm_small_m_accuracy4";
+    if (variant) *variant = pair_rows ? "gemm_small_m_f32act" : "gemm_small_m_accuracy4";
     if (L.ss == 2)
         return L.has_zp ? launch_q<__half, true>(L, p, stream) : launch_q<__half, false>(L, p, stream);
     return L.has_zp ? launch_q<float, true>(L, p, stream) : launch_q<float, false>(L, p, stream);

@@ -277,6 +277,15 @@ constexpr int kRedBytes = 2 * kMaxWaves * 16 * sizeof(float);
 // act order: index vectors (4 columns each) a thread requests up front
 constexpr int kPermPre = 4;
 
+// LDS bytes of the staged activation: a slot of kBatch chunks per wave
+// (WAVE_STAGE), or the whole activation padded to whole chunks.  The wave
+// partials follow it (kRedBytes), then, for act order, the gathered copy.
+template <typename AT, int kBatch, bool WAVE_STAGE>
+__host__ __device__ inline size_t stage_bytes(int waves, int C)
+{
+    return WAVE_STAGE ? (size_t)waves * kBatch * kChunkK * sizeof(AT) : (size_t)C * kChunkK * sizeof(AT);
+}
+
 // kBatch chunks per wave are in flight together.  LOOP = false: every chunk of
 // the tile fits in one batch per wave (waves * kBatch >= C), so the kernel is
 // straight-line code holding one register set; LOOP = true: batches alternate
@@ -286,6 +295,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr bool F16 = sizeof(AT) == 2;
+    constexpr bool WAVE_STAGE = !LOOP && !PERM;
     constexpr int NW = FUSED ? 2 : 1;
     typedef ChunkRegs<ST, Q, HAS_ZP> Regs;
 
@@ -319,13 +329,32 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
         }
     }
 
-    // 1. first activation vector of this thread (16 bytes)
+    // 1. the activation.  WAVE_STAGE: this wave's own slices of it (the 128
+    //    k of each of its chunks), requested first; else the thread's first
+    //    16-byte vector of the whole activation, staged for the workgroup.
     constexpr int kPerVec = 16 / sizeof(AT);
     const int nvec = (int)(kpad / kPerVec);
     const int nvec_valid = p.K / kPerVec;
     const u4_t* a_vec = static_cast<const u4_t*>(p.a);
     u4_t* s_vec = reinterpret_cast<u4_t*>(smem);
-    const u4_t first = a_vec[tid < nvec_valid ? tid : 0];   // zeroed at the store
+    constexpr int kVecPerChunk = kChunkK / kPerVec;                  // 16 (fp16) or 32 (fp32)
+    constexpr int kWaveVecs = (kBatch * kVecPerChunk + 63) / 64;      // per lane
+    u4_t own[WAVE_STAGE ? kWaveVecs : 1];
+    u4_t first = u4_t{0u, 0u, 0u, 0u};
+    if constexpr (WAVE_STAGE) {
+#pragma unroll
+        for (int i = 0; i < kWaveVecs; ++i) {
+            const int v = lane + 64 * i;
+            const int u = v / kVecPerChunk, e = v % kVecPerChunk;
+            const int c = wave + nw * u;
+            // K is a whole number of groups, so a vector is all inside or all
+            // outside the activation
+            const int kv = c * kVecPerChunk + e;
+            own[i] = (u < kBatch && c < C && kv < nvec_valid) ? a_vec[kv] : u4_t{0u, 0u, 0u, 0u};
+        }
+    } else {
+        first = a_vec[tid < nvec_valid ? tid : 0];   // zeroed at the store
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     float acc[NW];
@@ -357,16 +386,33 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
     Regs cur[NW][kBatch];
     load_batch(cur, wave);
 
-    // 3. stage the activation in LDS (zero beyond K) while the codes stream in
-    if (tid < nvec) s_vec[tid] = tid < nvec_valid ? first : u4_t{0u, 0u, 0u, 0u};
-    for (int v = tid + blockDim.x; v < nvec; v += blockDim.x)
-        s_vec[v] = v < nvec_valid ? a_vec[v] : u4_t{0u, 0u, 0u, 0u};
-    block_sync_lds();
+    // 3. stage the activation in LDS (zero beyond K) while the codes stream
+    //    in.  WAVE_STAGE: each wave writes its slices to a slot of its own and
+    //    reads only those, so no workgroup barrier stands between a wave and
+    //    its compute (a barrier here would hold every wave until the slowest
+    //    had issued its loads, which stalls under a full memory queue).
+    const unsigned char* act = smem;
+    if constexpr (WAVE_STAGE) {
+        u4_t* slot = s_vec + wave * (kBatch * kVecPerChunk);
+#pragma unroll
+        for (int i = 0; i < kWaveVecs; ++i) {
+            const int v = lane + 64 * i;
+            if (v < kBatch * kVecPerChunk) slot[v] = own[i];
+        }
+        // the wave's own LDS writes complete before its reads (in order);
+        // this keeps the compiler from moving the reads above them
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        act = reinterpret_cast<const unsigned char*>(slot);
+    } else {
+        if (tid < nvec) s_vec[tid] = tid < nvec_valid ? first : u4_t{0u, 0u, 0u, 0u};
+        for (int v = tid + blockDim.x; v < nvec; v += blockDim.x)
+            s_vec[v] = v < nvec_valid ? a_vec[v] : u4_t{0u, 0u, 0u, 0u};
+        block_sync_lds();
+    }
 
     // 3b. act order: gather the staged activation into the codes' column
     //     order, behind the reduction area (an index outside 0..K-1 reads
     //     column 0; columns past K stay zero)
-    const unsigned char* act = smem;
     if constexpr (PERM) {
         typedef typename std::conditional<F16, uint16_t, uint32_t>::type RT;
         typedef typename std::conditional<F16, u2_t, u4_t>::type VT;
@@ -399,15 +445,18 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
             const int c = cb + nw * u;
+            // the activation of chunk c: in the wave's slot (slot chunk u) or
+            // in the workgroup's copy (chunk c)
+            const int ca = WAVE_STAGE ? u : c;
             if (c < C) {
 #pragma unroll
                 for (int x = 0; x < NW; ++x) {
                     if (F16)
                         acc[x] = chunk_dot_f16<ST, Q, HAS_ZP>(
-                            r[x][u], reinterpret_cast<const _Float16*>(act), c, h, acc[x]);
+                            r[x][u], reinterpret_cast<const _Float16*>(act), ca, h, acc[x]);
                     else
                         acc[x] = chunk_dot_f32<ST, Q, HAS_ZP>(
-                            r[x][u], reinterpret_cast<const float*>(act), c, h, acc[x]);
+                            r[x][u], reinterpret_cast<const float*>(act), ca, h, acc[x]);
                 }
             }
         }
@@ -443,7 +492,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
             acc[x] += __shfl_xor(acc[x], 32);
         }
     }
-    float* red = reinterpret_cast<float*>(smem + kpad * sizeof(AT));
+    float* red = reinterpret_cast<float*>(smem + stage_bytes<AT, kBatch, WAVE_STAGE>(nw, C));
 #pragma unroll
     for (int x = 0; x < NW; ++x) red[(x * kMaxWaves + wave) * 16 + (lane & 15)] = acc[x];
     // the store's bias, requested before the barrier so that its latency
@@ -483,53 +532,61 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
 // the stream and the unpack work runs after it instead of beside it.
 constexpr int kMaxBatch = 4;
 
-template <typename AT, typename ST, int Q, bool HAS_ZP, bool FUSED, bool PERM>
-hipError_t launch_b(const GemvParams& p, int waves, size_t smem, int64_t tiles, hipStream_t s)
+template <typename AT, typename ST, int Q, bool HAS_ZP, bool FUSED, int B, bool PERM, bool LOOP>
+void launch_k(const GemvParams& p, int waves, int64_t tiles, hipStream_t s)
 {
-    const dim3 grid((unsigned)tiles), block(waves * 64);
+    constexpr bool WAVE_STAGE = !LOOP && !PERM;
+    const size_t stage = stage_bytes<AT, B, WAVE_STAGE>(waves, p.C);
+    const size_t smem = stage + kRedBytes + (PERM ? stage : 0);
+    gemv_kernel<AT, ST, Q, HAS_ZP, FUSED, B, PERM, LOOP><<<dim3((unsigned)tiles), dim3(waves * 64), smem, s>>>(p);
+}
+
+template <typename AT, typename ST, int Q, bool HAS_ZP, bool FUSED, bool PERM>
+hipError_t launch_b(const GemvParams& p, int waves, int64_t tiles, hipStream_t s)
+{
     const int per_wave = (p.C + waves - 1) / waves;
     if (per_wave <= 1)
-        gemv_kernel<AT, ST, Q, HAS_ZP, FUSED, 1, PERM, false><<<grid, block, smem, s>>>(p);
+        launch_k<AT, ST, Q, HAS_ZP, FUSED, 1, PERM, false>(p, waves, tiles, s);
     else if (per_wave <= 2)
-        gemv_kernel<AT, ST, Q, HAS_ZP, FUSED, 2, PERM, false><<<grid, block, smem, s>>>(p);
+        launch_k<AT, ST, Q, HAS_ZP, FUSED, 2, PERM, false>(p, waves, tiles, s);
     else if (per_wave <= kMaxBatch)
-        gemv_kernel<AT, ST, Q, HAS_ZP, FUSED, kMaxBatch, PERM, false><<<grid, block, smem, s>>>(p);
+        launch_k<AT, ST, Q, HAS_ZP, FUSED, kMaxBatch, PERM, false>(p, waves, tiles, s);
     else if (waves > kMaxWaves / 2)
-        gemv_kernel<AT, ST, Q, HAS_ZP, FUSED, 2, PERM, true><<<grid, block, smem, s>>>(p);
+        launch_k<AT, ST, Q, HAS_ZP, FUSED, 2, PERM, true>(p, waves, tiles, s);
     else
-        gemv_kernel<AT, ST, Q, HAS_ZP, FUSED, 4, PERM, true><<<grid, block, smem, s>>>(p);
+        launch_k<AT, ST, Q, HAS_ZP, FUSED, 4, PERM, true>(p, waves, tiles, s);
     return hipGetLastError();
 }
 
 template <typename AT, typename ST, int Q, bool HAS_ZP, bool FUSED>
-hipError_t launch_t(const GemvParams& p, int waves, size_t smem, int64_t tiles, hipStream_t s)
+hipError_t launch_t(const GemvParams& p, int waves, int64_t tiles, hipStream_t s)
 {
     // act order comes without the fused gate/up form
     if constexpr (!FUSED)
-        if (p.perm) return launch_b<AT, ST, Q, HAS_ZP, false, true>(p, waves, smem, tiles, s);
-    return launch_b<AT, ST, Q, HAS_ZP, FUSED, false>(p, waves, smem, tiles, s);
+        if (p.perm) return launch_b<AT, ST, Q, HAS_ZP, false, true>(p, waves, tiles, s);
+    return launch_b<AT, ST, Q, HAS_ZP, FUSED, false>(p, waves, tiles, s);
 }
 
 template <typename AT, typename ST, bool HAS_ZP, bool FUSED>
-hipError_t launch_q(const Layout& L, const GemvParams& p, int waves, size_t smem, hipStream_t s)
+hipError_t launch_q(const Layout& L, const GemvParams& p, int waves, hipStream_t s)
 {
     switch (L.Q) {
-    case 1: return launch_t<AT, ST, 1, HAS_ZP, FUSED>(p, waves, smem, L.T, s);
-    case 2: return launch_t<AT, ST, 2, HAS_ZP, FUSED>(p, waves, smem, L.T, s);
-    case 4: return launch_t<AT, ST, 4, HAS_ZP, FUSED>(p, waves, smem, L.T, s);
-    default: return launch_t<AT, ST, 8, HAS_ZP, FUSED>(p, waves, smem, L.T, s);
+    case 1: return launch_t<AT, ST, 1, HAS_ZP, FUSED>(p, waves, L.T, s);
+    case 2: return launch_t<AT, ST, 2, HAS_ZP, FUSED>(p, waves, L.T, s);
+    case 4: return launch_t<AT, ST, 4, HAS_ZP, FUSED>(p, waves, L.T, s);
+    default: return launch_t<AT, ST, 8, HAS_ZP, FUSED>(p, waves, L.T, s);
     }
 }
 
 template <typename AT, bool FUSED>
-hipError_t launch_a(const Layout& L, const GemvParams& p, int waves, size_t smem, hipStream_t s)
+hipError_t launch_a(const Layout& L, const GemvParams& p, int waves, hipStream_t s)
 {
     if (L.ss == 2) {
-        return L.has_zp ? launch_q<AT, __half, true, FUSED>(L, p, waves, smem, s)
-                        : launch_q<AT, __half, false, FUSED>(L, p, waves, smem, s);
+        return L.has_zp ? launch_q<AT, __half, true, FUSED>(L, p, waves, s)
+                        : launch_q<AT, __half, false, FUSED>(L, p, waves, s);
     }
-    return L.has_zp ? launch_q<AT, float, true, FUSED>(L, p, waves, smem, s)
-                    : launch_q<AT, float, false, FUSED>(L, p, waves, smem, s);
+    return L.has_zp ? launch_q<AT, float, true, FUSED>(L, p, waves, s)
+                    : launch_q<AT, float, false, FUSED>(L, p, waves, s);
 }
 
 GemvWeight gw(const WeightView& v)
@@ -562,18 +619,16 @@ hipError_t launch_gemv(const Layout& L, const WeightView& gate, const WeightView
     const int max_waves = L.T * kMaxWaves <= kResidentWaves ? kMaxWaves : kMaxWaves / 2;
     int waves = (int)(L.C < max_waves ? L.C : max_waves);
     if (waves < 1) waves = 1;
-    const size_t act_bytes = (size_t)L.C * kChunkK * (f16_act ? 2 : 4);
-    const size_t smem = act_bytes * (p.perm ? 2 : 1) + kRedBytes;
     const bool fused = up != nullptr;
     if (variant) *variant = fused ? (f16_act ? "gemv_gate_up_swiglu_f16" : "gemv_gate_up_swiglu_f32")
                           : p.perm ? (f16_act ? "gemv_act_order_f16" : "gemv_act_order_f32")
                                    : (f16_act ? "gemv_f16" : "gemv_f32");
     if (f16_act) {
-        return fused ? launch_a<__half, true>(L, p, waves, smem, stream)
-                     : launch_a<__half, false>(L, p, waves, smem, stream);
+        return fused ? launch_a<__half, true>(L, p, waves, stream)
+                     : launch_a<__half, false>(L, p, waves, stream);
     }
-    return fused ? launch_a<float, true>(L, p, waves, smem, stream)
-                 : launch_a<float, false>(L, p, waves, smem, stream);
+    return fused ? launch_a<float, true>(L, p, waves, stream)
+                 : launch_a<float, false>(L, p, waves, stream);
 }
 
 }  // namespace mnb

@@ -27,12 +27,22 @@ hipError_t launch_acc4_quantize(const float* a, int64_t M, int64_t K, _Float16* 
 
 // The fp16 GEMMs on such codes (exact integers, so every group dot is exact
 // in their fp32 accumulators) with an fp32 output: y[m, n] = row_scale[m] *
-// acc[m, n] (+ bias[n]); a16 [M, K] fp16.
+// acc[m, n] (+ bias[n]); a16 [M, K] fp16.  With pair_rows, a16 holds 2M rows
+// (m counts them), the (hi, lo) parts of fp32 activations from
+// launch_split_f32_rows, and y[r, n] = row_scale[r] * (acc[2r, n] + acc[2r +
+// 1, n]) (+ bias[r * bias_stride + n]).
 hipError_t launch_gemm_small_f32(const Layout& L, const WeightView& w, const void* a16, int64_t m,
                                  const float* row_scale, const float* bias, float* y, void* ws,
-                                 hipStream_t stream, const char** variant);
+                                 hipStream_t stream, const char** variant, int pair_rows = 0,
+                                 int64_t bias_stride = 0);
 hipError_t launch_gemm_mfma_f32(const Layout& L, const WeightView& w, const void* a16, int64_t m,
                                 const float* row_scale, const float* bias, float* y, hipStream_t stream,
-                                const char** variant);
+                                const char** variant, int pair_rows = 0, int64_t bias_stride = 0);
+
+// fp32 activations a [M, K] (K a multiple of 16, 16-byte aligned) as fp16 row
+// pairs hl [2M, K] (row 2m = hi, 2m + 1 = lo of row m, scaled by 2^-e_m) and
+// row_scale [M] = 2^e_m.
+hipError_t launch_split_f32_rows(const float* a, int64_t M, int64_t K, _Float16* hl, float* row_scale,
+                                 hipStream_t stream);
 
 }  // namespace mnb

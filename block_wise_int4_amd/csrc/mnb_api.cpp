@@ -268,16 +268,38 @@ static size_t workspace_for(const Layout& L, int64_t m)
     return 0;
 }
 
+// fp32 activations with M > 1: the row scales (fp32 [M]) at offset 0, then
+// at the next 256-byte boundary the (hi, lo) fp16 row pairs [2M, K], then the
+// workspace of the GEMM that runs on those 2M rows.
+static size_t f32_scale_bytes(int64_t m) { return (size_t)((4 * m + 255) / 256 * 256); }
+static size_t f32_rows_bytes(const Layout& L, int64_t m) { return (size_t)((4 * m * L.K + 255) / 256 * 256); }
+
+static size_t workspace_for(const Layout& L, int64_t m, int32_t a_dtype)
+{
+    if (a_dtype == MNB_F32 && m > 1) return f32_scale_bytes(m) + f32_rows_bytes(L, m) + workspace_for(L, 2 * m);
+    return workspace_for(L, m);
+}
+
 size_t mnb_gemm_workspace_bytes(const mnb_weight_desc* w, int64_t m)
+{
+    return mnb_gemm_workspace_bytes_for(w, m, MNB_F16);
+}
+
+size_t mnb_gemm_workspace_bytes_for(const mnb_weight_desc* w, int64_t m, int32_t a_dtype)
 {
     Layout L;
     if (check_desc(w, &L) != MNB_OK) return 0;
+    if (check_act_dtype(a_dtype) != MNB_OK) return 0;
     if (m < 0) {
         fail(MNB_ERR_INVALID_ARGUMENT, "M must be >= 0");
         return 0;
     }
+    if (m > INT64_MAX / 8 / L.K) {
+        fail(MNB_ERR_INVALID_ARGUMENT, "M*K overflows");
+        return 0;
+    }
     g_error.clear();
-    return workspace_for(L, m);
+    return workspace_for(L, m, a_dtype);
 }
 
 // M > 16 runs the prefill GEMM, whose buffer offsets are 32-bit.
@@ -287,6 +309,44 @@ static mnb_status check_gemm_k(const Layout& L, int64_t m)
         return fail(MNB_ERR_UNSUPPORTED, "K=%lld exceeds the prefill GEMM limit %lld (M > 16)", (long long)L.K,
                     (long long)mnb::gemm_mfma_max_k());
     return MNB_OK;
+}
+
+// fp32 activations, M > 1: each row split into a (hi, lo) pair of fp16 rows
+// scaled by a power of two, then the fp16 GEMM on the 2M rows with an epilogue
+// that adds each pair and scales it back.
+static mnb_status gemm_f32_rows(const mnb_weight_desc* w, const Layout& L, const void* repacked, const void* a,
+                                int64_t m, const mnb::Bias& bias, void* y, void* workspace,
+                                size_t workspace_bytes, void* stream)
+{
+    if (m > INT64_MAX / 8 / L.K) return fail(MNB_ERR_INVALID_ARGUMENT, "M*K overflows");
+    if (2 * m > INT32_MAX) return fail(MNB_ERR_INVALID_ARGUMENT, "2M must fit in 32 bits");
+    if (L.N == 0) return ok("noop");
+    MNB_TRY(check_gemm_k(L, 2 * m));
+    const size_t need = workspace_for(L, m, MNB_F32);
+    if (workspace_bytes < need)
+        return fail(MNB_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed (fp32 activations, "
+                    "mnb_gemm_workspace_bytes_for)", workspace_bytes, need);
+    MNB_TRY(check_ptr(workspace, 256, "workspace"));
+    MNB_TRY(check_ptr(repacked, 256, "repacked"));
+    MNB_TRY(check_ptr(a, 16, "a"));
+    MNB_TRY(check_ptr(y, 4, "y"));
+    if (bias.ptr) MNB_TRY(check_ptr(bias.ptr, 4, "bias"));
+    MNB_TRY(check_device());
+    const mnb::WeightView v = mnb::view_of(L, repacked);
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    float* rs = reinterpret_cast<float*>(ws);
+    _Float16* hl = reinterpret_cast<_Float16*>(ws + f32_scale_bytes(m));
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = mnb::launch_split_f32_rows(static_cast<const float*>(a), m, L.K, hl, rs, s);
+    if (e != hipSuccess) return launched(e, "f32_split");
+    const char* variant = "";
+    const float* b = static_cast<const float*>(bias.ptr);
+    if (2 * m <= 16)
+        e = mnb::launch_gemm_small_f32(L, v, hl, 2 * m, rs, b, static_cast<float*>(y),
+                                       ws + f32_scale_bytes(m) + f32_rows_bytes(L, m), s, &variant, 1, bias.row_stride);
+    else
+        e = mnb::launch_gemm_mfma_f32(L, v, hl, 2 * m, rs, b, static_cast<float*>(y), s, &variant, 1, bias.row_stride);
+    return launched(e, variant);
 }
 
 static mnb_status gemm_common(const mnb_weight_desc* w, const void* repacked, const void* a, int64_t m,
@@ -299,8 +359,7 @@ static mnb_status gemm_common(const mnb_weight_desc* w, const void* repacked, co
     if (m < 0) return fail(MNB_ERR_INVALID_ARGUMENT, "M must be >= 0 (got %lld)", (long long)m);
     if (m > INT32_MAX) return fail(MNB_ERR_INVALID_ARGUMENT, "M must fit in 32 bits");
     if (m == 1) return gemv_common(w, repacked, nullptr, a, a_dtype, bias, y, stream);
-    if (m > 1 && a_dtype != MNB_F16)
-        return fail(MNB_ERR_UNSUPPORTED, "M>1 GEMM takes fp16 activations only");
+    if (m > 1 && a_dtype == MNB_F32) return gemm_f32_rows(w, L, repacked, a, m, bias, y, workspace, workspace_bytes, stream);
     const size_t need = workspace_for(L, m);
     if (m == 0 || L.N == 0) return ok("noop");
     MNB_TRY(check_gemm_k(L, m));
@@ -360,12 +419,12 @@ size_t mnb_gemm_act_order_workspace_bytes(const mnb_weight_desc* w, int64_t m, i
     Layout L;
     if (check_desc(w, &L) != MNB_OK) return 0;
     if (m < 0 || check_act_dtype(a_dtype) != MNB_OK) return 0;
-    if (L.K > 0 && m > INT64_MAX / 4 / L.K) {
+    if (L.K > 0 && m > INT64_MAX / 16 / L.K) {
         fail(MNB_ERR_INVALID_ARGUMENT, "M*K overflows");
         return 0;
     }
     g_error.clear();
-    return act_order_a_bytes(L, m, a_dtype) + workspace_for(L, m);
+    return act_order_a_bytes(L, m, a_dtype) + workspace_for(L, m, a_dtype);
 }
 
 mnb_status mnb_gemm_act_order(const mnb_weight_desc* w, const void* repacked, const void* a, int64_t m,
@@ -378,12 +437,10 @@ mnb_status mnb_gemm_act_order(const mnb_weight_desc* w, const void* repacked, co
     if (m < 0) return fail(MNB_ERR_INVALID_ARGUMENT, "M must be >= 0 (got %lld)", (long long)m);
     if (m == 0 || L.N == 0) return ok("noop");
     if (m > INT32_MAX) return fail(MNB_ERR_INVALID_ARGUMENT, "M must fit in 32 bits");
-    if (L.K > 0 && m > INT64_MAX / 4 / L.K) return fail(MNB_ERR_INVALID_ARGUMENT, "M*K overflows");
-    if (m > 1 && a_dtype != MNB_F16)
-        return fail(MNB_ERR_UNSUPPORTED, "M>1 GEMM takes fp16 activations only");
-    MNB_TRY(check_gemm_k(L, m));
+    if (L.K > 0 && m > INT64_MAX / 16 / L.K) return fail(MNB_ERR_INVALID_ARGUMENT, "M*K overflows");
+    MNB_TRY(check_gemm_k(L, a_dtype == MNB_F32 ? 2 * m : m));
     const size_t a_bytes = act_order_a_bytes(L, m, a_dtype);
-    const size_t need = a_bytes + workspace_for(L, m);
+    const size_t need = a_bytes + workspace_for(L, m, a_dtype);
     if (workspace_bytes < need)
         return fail(MNB_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed",
                     workspace_bytes, need);

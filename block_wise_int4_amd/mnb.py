@@ -26,7 +26,8 @@ MNB_BIAS_FUSED = 0
 MNB_BIAS_AFTER_ROUND = 1
 
 EXPORTS = ("mnb_repacked_bytes", "mnb_repacked_layout", "mnb_repack", "mnb_gemv",
-           "mnb_gemv_gate_up_swiglu", "mnb_gemm_workspace_bytes", "mnb_gemm", "mnb_gemm_bias",
+           "mnb_gemv_gate_up_swiglu", "mnb_gemm_workspace_bytes", "mnb_gemm_workspace_bytes_for", "mnb_gemm",
+           "mnb_gemm_bias",
            "mnb_act_order_permutation", "mnb_repack_act_order", "mnb_gemm_act_order_workspace_bytes",
            "mnb_gemm_act_order", "mnb_gemm_accuracy4_workspace_bytes", "mnb_gemm_accuracy4",
            "mnb_gemm_accuracy4_noalloc",
@@ -84,6 +85,7 @@ def _load():
         "mnb_gemv": (ctypes.c_int, [D, P, P, i32, P, P]),
         "mnb_gemv_gate_up_swiglu": (ctypes.c_int, [D, P, P, P, i32, P, P]),
         "mnb_gemm_workspace_bytes": (sz, [D, i64]),
+        "mnb_gemm_workspace_bytes_for": (sz, [D, i64, i32]),
         "mnb_gemm": (ctypes.c_int, [D, P, P, i64, i32, P, P, sz, P]),
         "mnb_gemm_bias": (ctypes.c_int, [D, P, P, i64, i32, P, i64, i32, P, P, sz, P]),
         "mnb_act_order_permutation": (ctypes.c_int, [D, P, P]),
@@ -194,6 +196,10 @@ def mnb_gemv_gate_up_swiglu(w: mnb_weight_desc, gate_repacked: Ptr, up_repacked:
 
 def mnb_gemm_workspace_bytes(w: mnb_weight_desc, m: int) -> int:
     return int(lib.mnb_gemm_workspace_bytes(ctypes.byref(w), m))
+
+
+def mnb_gemm_workspace_bytes_for(w: mnb_weight_desc, m: int, a_dtype: int) -> int:
+    return int(lib.mnb_gemm_workspace_bytes_for(ctypes.byref(w), m, a_dtype))
 
 
 def mnb_gemm(w: mnb_weight_desc, repacked: Ptr, a, m: int, y, workspace: Ptr = None,

@@ -171,9 +171,14 @@ mnb_status mnb_gemv_gate_up_swiglu(const mnb_weight_desc* w, const void* gate_re
                                    const void* up_repacked, const void* a, int32_t a_dtype,
                                    void* y, void* stream);
 
-/* Workspace in bytes that mnb_gemm needs for (w, m); 0 when none.  Host
- * only.  Like splitk_partials_len of marlin_gemm.rs. */
+/* Workspace in bytes that mnb_gemm needs for (w, m) with fp16 activations;
+ * 0 when none.  Host only.  Like splitk_partials_len of marlin_gemm.rs. */
 size_t mnb_gemm_workspace_bytes(const mnb_weight_desc* w, int64_t m);
+
+/* The same for activations of a_dtype (MNB_F16 or MNB_F32): fp32
+ * activations with M > 1 need 4*M*K bytes plus the row scales (see
+ * mnb_gemm).  0 on an invalid argument (mnb_last_error() says why). */
+size_t mnb_gemm_workspace_bytes_for(const mnb_weight_desc* w, int64_t m, int32_t a_dtype);
 
 /* GEMM for any M >= 1 (marlin_gemm.rs, kernels matmul_nbits_marlin_gemm_f16
  * and its split-K form, re-designed for gfx950):
@@ -182,13 +187,21 @@ size_t mnb_gemm_workspace_bytes(const mnb_weight_desc* w, int64_t m);
  * GEMV (its K limit applies); 2 <= M <= 16 a weight-streaming MFMA kernel
  * whose workgroups split K among their waves and reduce in a fixed order;
  * larger M the MFMA prefill GEMM, for K <= 11184810 (its 32-bit buffer
- * offsets; else MNB_ERR_UNSUPPORTED).  The GEMM paths take fp16 A only
- * (MNB_ERR_UNSUPPORTED for fp32 A with M > 1).  Products are fp16 x fp16 on
- * the matrix cores with fp32 accumulation; each group's partial sum is
- * multiplied by its scale after that group's accumulation.  `workspace`
- * (device, 16-byte aligned) must hold mnb_gemm_workspace_bytes(w, m) bytes
- * (0 for every shape at present); it may be NULL when that is 0.  Results
- * are deterministic. */
+ * offsets; else MNB_ERR_UNSUPPORTED).  Products are fp16 x fp16 on the
+ * matrix cores with fp32 accumulation; each group's partial sum is
+ * multiplied by its scale after that group's accumulation.  fp32 A with
+ * M > 1 (the fp32 operator of matmul_nbits.rs, MatMulNBitsKernel::run, at
+ * any M): each row m is scaled by a power of two 2^-e_m that puts its largest
+ * finite magnitude in [2^14, 2^15) and written as two fp16 rows, hi =
+ * fp16(a 2^-e_m) and lo = fp16(a 2^-e_m - hi); the fp16 GEMM runs on the 2M
+ * rows (the small-M kernel for 2M <= 16, else the prefill kernel, whose K
+ * limit then applies) and y[m,n] = 2^e_m * (acc[2m,n] + acc[2m+1,n]) in fp32.
+ * The split errs by at most 2^-22 |a| + 2^-39 max|a| per element; NaN and
+ * infinities pass whole.  `workspace` (device) must hold
+ * mnb_gemm_workspace_bytes_for(w, m, a_dtype) bytes: none for fp16 (it may be
+ * NULL), and for fp32 with M > 1 the row scales (fp32 [M]) at offset 0 and the
+ * row pairs (fp16 [2M, K]) at the next 256-byte boundary (256-byte aligned).
+ * Results are deterministic. */
 mnb_status mnb_gemm(const mnb_weight_desc* w, const void* repacked, const void* a, int64_t m,
                     int32_t a_dtype, void* y, void* workspace, size_t workspace_bytes,
                     void* stream);
@@ -212,7 +225,7 @@ typedef enum {
  * a_dtype, element-aligned) holds (M-1)*bias_row_stride + N elements:
  * bias_row_stride = 0 adds one [N] vector to every row, N (or more) adds a
  * per-row residual [M, stride].  bias_mode is an mnb_bias_mode; for fp32
- * outputs (M = 1 with fp32 activations) both modes are acc + b in fp32.
+ * outputs (fp32 activations) both modes are acc + b in fp32.
  * bias = NULL is mnb_gemm.  Every other argument, the workspace and the
  * error behaviour are as for mnb_gemm; a negative stride or an unknown mode
  * is MNB_ERR_INVALID_ARGUMENT. */

@@ -186,6 +186,37 @@ def matmul(A64: np.ndarray, W64: np.ndarray, threads: int = 0):
     return Y, B
 
 
+def matmul_lib(A64: np.ndarray, W64: np.ndarray):
+    """Y = A . W^T and Bnd = |A| . |W|^T with a library matrix product
+    (numpy's fp64 matmul) as the step: the same sums as ``matmul`` in another
+    order, each within K * 2^-53 * Bnd of the exact value, for products too
+    large for the naive loops (a full prefill output)."""
+    A64 = np.ascontiguousarray(A64, np.float64)
+    W64 = np.ascontiguousarray(W64, np.float64)
+    assert A64.shape[1] == W64.shape[1]
+    Y = A64 @ W64.T
+    B = np.abs(A64) @ np.abs(W64).T
+    return Y, B
+
+
+def acc4_matmul_lib(A, packed, scales, zp, N: int, K: int, g: int, bias=None) -> tuple:
+    """acc4_matmul for every output with a library matrix product as the
+    step: the oracle's int8 rows q and scales s, the oracle's dequantized
+    weights w = (c - z) * scale in fp64, then s[m] * (q . w^T) + b in fp64.
+    The block sums of acc4_matmul are exact integers; here the same value is
+    summed in another order, within K * 2^-53 * Bnd of it.  Returns (Y, Bnd, q, s)."""
+    A = np.ascontiguousarray(A, np.float32).reshape(-1, K)
+    q, sc = acc4_quantize(A)
+    W64 = dequant(packed, scales, zp, N, K, g)
+    inner, mag = matmul_lib(q.astype(np.float64), W64)
+    s64 = sc.astype(np.float64)[:, None]
+    b = np.zeros(N) if bias is None else np.asarray(bias, np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        Y = np.where(s64 != 0, s64 * inner, 0.0) + b[None, :]
+        Bnd = np.where(s64 != 0, np.abs(s64) * mag, 0.0) + np.abs(b)[None, :]
+    return Y, Bnd, q, sc
+
+
 def matmul_nbits(A: np.ndarray, packed, scales, zp, N: int, K: int, g: int, threads: int = 0):
     """The whole method (dequantize on the fly) for every output: (Y, Bnd) [M,N]."""
     A64 = decode(np.ascontiguousarray(A)).reshape(-1, K)

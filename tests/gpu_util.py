@@ -29,11 +29,11 @@ def upload(w: synth.Weight):
 _WS = {}
 
 
-def workspace(q, M):
-    """A GEMM workspace for (q, M) (zero-filled), shared by every call that
-    fits in it."""
+def workspace(q, M, a_dtype=None):
+    """A GEMM workspace for (q, M) and the activation dtype (zero-filled),
+    shared by every call that fits in it."""
     from block_wise_int4_amd import mnb
-    n = mnb.mnb_gemm_workspace_bytes(q.desc, M)
+    n = mnb.mnb_gemm_workspace_bytes_for(q.desc, M, mnb.MNB_F16 if a_dtype is None else a_dtype)
     buf = _WS.get("buf")
     if buf is None or buf.numel() < n:
         buf = torch().zeros(max(n, 256), dtype=torch().uint8, device="cuda")
@@ -43,7 +43,7 @@ def workspace(q, M):
 
 def gemm(q, a, M, y, stream=None):
     from block_wise_int4_amd import mnb
-    ws, n = workspace(q, M)
+    ws, n = workspace(q, M, mnb._dtype_code(a))
     mnb.mnb_gemm(q.desc, q.repacked, a, M, y, ws, n, stream=stream)
 
 

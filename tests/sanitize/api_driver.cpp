@@ -34,9 +34,10 @@ hipError_t launch_acc4_gemv(const Layout&, const WeightView&, const float*, cons
                             float*, hipStream_t, const char**) { std::abort(); }
 hipError_t launch_acc4_quantize(const float*, int64_t, int64_t, _Float16*, float*, hipStream_t) { std::abort(); }
 hipError_t launch_gemm_small_f32(const Layout&, const WeightView&, const void*, int64_t, const float*,
-                                 const float*, float*, void*, hipStream_t, const char**) { std::abort(); }
+                                 const float*, float*, void*, hipStream_t, const char**, int, int64_t) { std::abort(); }
 hipError_t launch_gemm_mfma_f32(const Layout&, const WeightView&, const void*, int64_t, const float*,
-                                const float*, float*, hipStream_t, const char**) { std::abort(); }
+                                const float*, float*, hipStream_t, const char**, int, int64_t) { std::abort(); }
+hipError_t launch_split_f32_rows(const float*, int64_t, int64_t, _Float16*, float*, hipStream_t) { std::abort(); }
 hipError_t noalloc_scratch(int, void**) { std::abort(); }
 }  // namespace mnb
 
@@ -105,7 +106,14 @@ int main()
     expect(mnb_gemv_gate_up_swiglu(&d, fake, nullptr, fake, MNB_F16, fake, nullptr), INV, "gate/up NULL");
     expect(mnb_gemm(&d, fake, fake, -1, MNB_F16, fake, nullptr, 0, nullptr), INV, "negative M");
     expect(mnb_gemm(&d, fake, fake, 0, MNB_F16, fake, nullptr, 0, nullptr), OK, "M = 0");
-    expect(mnb_gemm(&d, fake, fake, 8, MNB_F32, fake, nullptr, 0, nullptr), UNS, "fp32 GEMM");
+    const size_t wsf = mnb_gemm_workspace_bytes_for(&d, 8, MNB_F32);
+    if (wsf != 256 + (4 * 8 * 512 + 255) / 256 * 256) {
+        std::printf("FAIL fp32 workspace size %zu\n", wsf);
+        ++failures;
+    }
+    expect(mnb_gemm(&d, fake, fake, 8, MNB_F32, fake, nullptr, 0, nullptr), INV, "fp32 GEMM without workspace");
+    expect(mnb_gemm(&d, fake, fake, 8, MNB_F32, fake, fake, wsf - 1, nullptr), INV, "fp32 GEMM workspace too small");
+    expect(mnb_gemm(&d, fake, fake, 8, MNB_F32, fake, fake, wsf, nullptr), DEV, "valid fp32 GEMM without a device");
     expect(mnb_gemm(&d, fake, fake, 64, MNB_F16, fake, nullptr, 0, nullptr), DEV, "valid GEMM without a device");
     expect(mnb_gemm_bias(&d, fake, fake, 4, MNB_F16, fake, -1, MNB_BIAS_FUSED, fake, nullptr, 0, nullptr), INV,
            "negative bias stride");

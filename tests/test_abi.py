@@ -150,9 +150,16 @@ def test_argument_validation():
     assert "zero_points" in _expect(E, lib.mnb_repack, D(d), FAKE, FAKE, None, FAKE, None)
     d0 = mnb.desc(64, 256, 32, False, mnb.MNB_F16)
     assert "has_zero_points" in _expect(E, lib.mnb_repack, D(d0), FAKE, FAKE, FAKE, FAKE, None)
-    # GEMM: fp32 activations only for M = 1; negative M; workspace size
-    assert "fp16" in _expect(mnb.MNB_ERR_UNSUPPORTED, lib.mnb_gemm, D(d), FAKE, FAKE, 8, mnb.MNB_F32,
-                             FAKE, None, 0, None)
+    # GEMM: fp32 activations with M > 1 need their workspace (row pairs and
+    # scales); negative M; workspace size
+    need32 = lib.mnb_gemm_workspace_bytes_for(D(d), 8, mnb.MNB_F32)
+    assert need32 == 256 + (4 * 8 * 256 + 255) // 256 * 256
+    assert lib.mnb_gemm_workspace_bytes_for(D(d), 8, mnb.MNB_F16) == lib.mnb_gemm_workspace_bytes(D(d), 8)
+    assert lib.mnb_gemm_workspace_bytes_for(D(d), 1, mnb.MNB_F32) == 0
+    assert lib.mnb_gemm_workspace_bytes_for(D(d), 8, 7) == 0
+    assert "workspace" in _expect(E, lib.mnb_gemm, D(d), FAKE, FAKE, 8, mnb.MNB_F32, FAKE, None, 0, None)
+    assert "workspace" in _expect(E, lib.mnb_gemm, D(d), FAKE, FAKE, 8, mnb.MNB_F32, FAKE, FAKE, need32 - 1,
+                                  None)
     _expect(E, lib.mnb_gemm, D(d), FAKE, FAKE, -1, 1, FAKE, None, 0, None)
     need = lib.mnb_gemm_workspace_bytes(D(mnb.desc(64, 4096, 64, True, 1)), 4)
     if need:
@@ -253,8 +260,10 @@ def test_act_order_argument_validation():
                                   FAKE, need - 1, None)
     assert "perm" in _expect(E, lib.mnb_gemm_act_order, D(d), FAKE, FAKE, 40, 1, None, FAKE,
                              FAKE, need, None)
-    assert "fp16" in _expect(mnb.MNB_ERR_UNSUPPORTED, lib.mnb_gemm_act_order, D(d), FAKE, FAKE, 8,
-                             mnb.MNB_F32, FAKE, FAKE, FAKE, 1 << 30, None)
+    need32 = lib.mnb_gemm_act_order_workspace_bytes(D(d), 8, mnb.MNB_F32)
+    assert need32 == 8 * 256 * 4 + 256 + 8 * 256 * 4
+    assert "workspace" in _expect(E, lib.mnb_gemm_act_order, D(d), FAKE, FAKE, 8, mnb.MNB_F32, FAKE, FAKE,
+                                  FAKE, need32 - 1, None)
     assert "perm" in _expect(E, lib.mnb_repack_act_order, D(d), FAKE, FAKE, FAKE, None, FAKE, None)
     assert lib.mnb_gemm_act_order(D(d), None, None, 0, 1, None, None, None, 0, None) == mnb.MNB_OK
     # K is a whole number of groups (the descriptor check every call makes)

@@ -172,3 +172,20 @@ def test_accuracy4_workload_sizes_sampled(mnb):
             G.assert_within(y[m:m + 1], Y, B, "accuracy4 M=%d row %d" % (M, m), bound=o.acc4_bound(B, K, g))
         del y
         t.cuda.empty_cache()
+
+
+def test_accuracy4_prefill_workload_every_output(mnb):
+    """The int8-activation prefill workload (M=2048, K=4096, N=14336, g=128,
+    fp32 scales, zero points, fp32 bias): all 2048 rows, every output, against
+    the oracle's int8 rows and dequantized weights through a library fp64
+    matrix product (oracle.acc4_matmul_lib, pinned against acc4_matmul)."""
+    t = G.torch()
+    M, K, N, g = 2048, 4096, 14336, 128
+    w = synth.weight(N, K, g, "f32", (0.002, 0.01), True, (320, M))
+    A = synth.activation(M, K, "f32", 1.0, (321, M))
+    bias = synth.activation(1, N, "f32", 1.0, (322, N)).reshape(N)
+    y, _, _, _ = _run(mnb, w, A, bias)
+    t.cuda.empty_cache()
+    Y, B, _, _ = o.acc4_matmul_lib(A, w.packed, w.scales, w.zero_points, N, K, g, bias)
+    G.assert_within(y, Y, B, "accuracy4 prefill, every output", bound=o.acc4_bound(B, K, g))
+

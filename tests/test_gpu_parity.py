@@ -353,6 +353,27 @@ def test_prefill_workload_sampled_parity(mnb):
     assert np.isfinite(yh).all()
 
 
+def test_prefill_workload_every_output(mnb):
+    """The full prefill workload (M=2048, K=4096, N=14336, g=128) in the
+    launch bench.py times: all 29,360,128 outputs against the oracle's
+    dequantized weights and a library fp64 matrix product (oracle.matmul_lib,
+    pinned against the naive loops)."""
+    t = G.torch()
+    wl = synth.PREFILL_GEMM
+    w = synth.workload_weights(wl)
+    A = synth.workload_activation(wl)
+    q = G.upload(w)
+    y = t.empty((wl.M, wl.N), dtype=t.float16, device="cuda")
+    G.gemm(q, G.to_dev(A), wl.M, y)
+    yh = G.host(y)
+    del y, q
+    t.cuda.empty_cache()
+    W64 = o.dequant(w.packed, w.scales, w.zero_points, wl.N, wl.K, wl.group)
+    Y, B = o.matmul_lib(o.decode(A), W64)
+    del W64
+    G.assert_within(yh, Y, B, "prefill workload, every output")
+
+
 def test_prefill_mid_size_sampled_parity(mnb):
     """Mid-size prefill shapes: between one and two rounds of output tiles
     (M=1000, N=14336: 11 x 56 tiles of 96 x 256) and fewer tiles than the
@@ -677,6 +698,86 @@ def test_zero_and_non_finite_scales(mnb):
             assert (yh[:, 3] == 0).all()
 
 
+F32_CASES = [
+    # M, N, K, g, scale dtype, zero points: the small-M kernel on 2M <= 16
+    # rows, the prefill kernel beyond, K tails, every group size
+    (2, 200, 512, 32, "f16", True), (5, 257, 896, 64, "f32", False), (8, 130, 384, 128, "f16", True),
+    (9, 96, 1024, 16, "f16", True), (16, 300, 512, 64, "f32", True), (40, 513, 1024, 32, "f16", True),
+    (200, 300, 384, 128, "f16", False), (33, 70, 400, 16, "f32", True), (3, 70, 352, 32, "f16", True)]
+
+
+def _f32_rows(M, K, seed):
+    """fp32 activations N(0,1) with special rows: huge, tiny, mixed
+    magnitudes, a NaN, an infinity, zeros, a subnormal-only row."""
+    A = synth.activation(M, K, "f32", 1.0, (230, M, K, seed))
+    rng = np.random.default_rng(M + K)
+    specials = [lambda r: r * np.float32(1e30), lambda r: r * np.float32(1e-30),
+                lambda r: np.where(rng.random(K) < 0.5, r * 1e6, r * 1e-6).astype(np.float32),
+                lambda r: np.where(np.arange(K) == 3, np.float32(np.nan), r),
+                lambda r: np.where(np.arange(K) == 7, np.float32(np.inf), r),
+                lambda r: np.zeros_like(r), lambda r: (r * np.float32(1e-40)).astype(np.float32)]
+    for j, f in enumerate(specials):
+        if j < M:
+            A[(j * 7) % M] = f(A[(j * 7) % M])
+    return A
+
+
+@pytest.mark.parametrize("M,N,K,g,sdt,zp", F32_CASES)
+def test_f32_activations_gemm_parity(mnb, M, N, K, g, sdt, zp):
+    """fp32 activations with M > 1: rows split into fp16 (hi, lo) pairs under
+    a power-of-two row scale, the fp16 GEMM on the 2M rows, the pairs summed
+    and scaled back in fp32.  Against the oracle on the fp32 values (exact in
+    fp64), with huge, tiny, subnormal, NaN and infinite rows, and with an fp32
+    bias vector and a per-row bias."""
+    t = G.torch()
+    w = _weight(N, K, g, sdt, zp, seed=M + 21)
+    q = G.upload(w)
+    A = _f32_rows(M, K, 1)
+    a = G.to_dev(A)
+    y = t.empty((M, N), dtype=t.float32, device="cuda")
+    G.gemm(q, a, M, y)
+    expect = "gemm_small_m_f32act" if 2 * M <= 16 else "gemm_mfma_32x32x16_f32act"
+    assert mnb.mnb_last_variant() == expect
+    Y, B, W64 = G.oracle_dense(A, w)
+    G.assert_within(G.host(y), Y, B, "fp32 activations M=%d N=%d K=%d g=%d" % (M, N, K, g))
+    # bias: a vector, then a per-row residual [M, N + 3]; the fp32 add is
+    # covered by the rule applied to sum |a w| + |b|
+    ws, n = G.workspace(q, M, mnb.MNB_F32)
+    rows_ok = np.isfinite(A).all(axis=1)
+    for stride in (0, N + 3):
+        rows = 1 if stride == 0 else M
+        b = synth.activation(rows, max(stride, N), "f32", 2.0, (231, M, stride))
+        mnb.mnb_gemm_bias(q.desc, q.repacked, a, M, G.to_dev(b), stride, mnb.MNB_BIAS_FUSED, y, ws, n)
+        b64 = (b[0, :N][None, :] if stride == 0 else b[:, :N]).astype(np.float64)
+        yh = G.host(y)
+        G.assert_within(yh[rows_ok], (Y + b64)[rows_ok], (B + np.abs(b64))[rows_ok],
+                        "fp32 activations + bias stride %d" % stride)
+
+
+def test_f32_activations_act_order(mnb):
+    """Act-order weights with fp32 activations and M > 1: the columns of A
+    permuted in fp32, then the row-pair GEMM."""
+    t = G.torch()
+    for (M, N, K, g) in ((4, 96, 512, 32), (40, 130, 1024, 128)):
+        w = _weight(N, K, g, "f16", True, seed=M + 9)
+        rng = np.random.default_rng(M * 7 + K)
+        g_idx = np.empty(K, np.int32)
+        g_idx[rng.permutation(K)] = np.arange(K) // g
+        A = _act(M, K, "f32", seed=M + 11)
+        d = mnb.desc(N, K, g, True, mnb.MNB_F16)
+        perm = G.to_dev(mnb.mnb_act_order_permutation(d, g_idx))
+        rep = t.empty(mnb.mnb_repacked_bytes(d), dtype=t.uint8, device="cuda")
+        mnb.mnb_repack_act_order(d, G.to_dev(w.packed.reshape(-1)), G.to_dev(w.scales.reshape(-1)),
+                                 G.to_dev(w.zero_points.reshape(-1)), perm, rep)
+        n_ws = mnb.mnb_gemm_act_order_workspace_bytes(d, M, mnb.MNB_F32)
+        ws = t.zeros(n_ws, dtype=t.uint8, device="cuda")
+        y = t.empty((M, N), dtype=t.float32, device="cuda")
+        mnb.mnb_gemm_act_order(d, rep, G.to_dev(A), M, perm, y, ws, n_ws)
+        W = o.dequant_gidx(w.packed, w.scales, w.zero_points, g_idx, N, K, g)
+        Y, B = o.matmul(o.decode(A), W)
+        G.assert_within(G.host(y), Y, B, "act order fp32 M=%d N=%d K=%d g=%d" % (M, N, K, g))
+
+
 def _extreme_scales(N, kb, base, big=False):
     """fp32 scales [N, kb] from `base` with columns whose groups span extreme
     ranges: a tiny scale beside ordinary ones (ratio about 2^90), a
@@ -751,6 +852,7 @@ def test_empty_and_unsupported_requests(mnb):
     mnb.mnb_gemm(q.desc, q.repacked, G.to_dev(_act(1, 256)), 0, y)
     assert (G.host(y) == 3.0).all()
     with pytest.raises(mnb.MnbError) as e:
+        # fp32 activations with M > 1 need their workspace
         mnb.mnb_gemm(q.desc, q.repacked, G.to_dev(_act(4, 256, "f32")), 4,
                      t.empty((4, 64), dtype=t.float32, device="cuda"))
-    assert e.value.status == mnb.MNB_ERR_UNSUPPORTED
+    assert e.value.status == mnb.MNB_ERR_INVALID_ARGUMENT

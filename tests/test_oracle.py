@@ -17,6 +17,7 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
+from block_wise_int4_amd import synth
 from oracle import oracle as o
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
@@ -80,7 +81,8 @@ def pin_worked_examples():
             Y2, B2 = o.matmul_nbits(A, packed, scales, zp, N, K, g)
             Y3, B3 = o.matmul_nbits_at(A, packed, scales, zp, N, K, g,
                                        np.zeros(N, np.int64), np.arange(N))
-            for Y, B in ((Y1[0], B1[0]), (Y2[0], B2[0]), (Y3, B3)):
+            Y4, B4 = o.matmul_lib(o.decode(A), w)
+            for Y, B in ((Y1[0], B1[0]), (Y2[0], B2[0]), (Y3, B3), (Y4[0], B4[0])):
                 assert (Y == np.array(case["Y"])).all(), (ex["name"], case["A"], Y)
                 assert (B == np.array(case["B"])).all(), (ex["name"], case["A"], B)
 
@@ -410,11 +412,44 @@ def pin_acc4_matmul():
             assert (Y[m] != Yp[m]).any()
 
 
+def pin_library_products():
+    """The library-product steps agree with the naive loops and with exact
+    rationals: matmul_lib against matmul (same sums, other order) within
+    K * 2^-52 * Bnd, and against Fraction on a small case; acc4_matmul_lib
+    against acc4_matmul (exact block integers) within K * 2^-52 * Bnd, with
+    the same codes and scales (the worked examples run it too, exactly)."""
+    rng = np.random.default_rng(17)
+    for (M, N, K, g) in ((3, 40, 256, 32), (5, 33, 384, 128), (2, 17, 64, 16)):
+        w = synth.weight(N, K, g, "f16", (0.005, 0.02), True, (71, N, K))
+        A = synth.activation(M, K, "f16", 1.0, (72, M, K))
+        W64 = o.dequant(w.packed, w.scales, w.zero_points, N, K, g)
+        Y1, B1 = o.matmul(o.decode(A), W64)
+        Y2, B2 = o.matmul_lib(o.decode(A), W64)
+        assert (np.abs(Y1 - Y2) <= K * 2.0 ** -52 * B1).all()
+        assert (np.abs(B1 - B2) <= K * 2.0 ** -52 * B1).all()
+        Af = (rng.standard_normal((M, K)) * 3).astype(np.float32)
+        b = rng.standard_normal(N).astype(np.float32)
+        Y3, B3, q3, s3 = o.acc4_matmul(Af, w.packed, w.scales, w.zero_points, N, K, g, b)
+        Y4, B4, q4, s4 = o.acc4_matmul_lib(Af, w.packed, w.scales, w.zero_points, N, K, g, b)
+        assert (q3 == q4).all() and (s3 == s4).all()
+        assert (np.abs(Y3 - Y4) <= K * 2.0 ** -52 * B3 + 1e-300).all()
+    # exact rationals on a small case
+    w = synth.weight(7, 48, 16, "f32", (0.005, 0.02), True, (73,))
+    A = synth.activation(2, 48, "f32", 1.0, (74,))
+    W64 = o.dequant(w.packed, w.scales, w.zero_points, 7, 48, 16)
+    Y, _ = o.matmul_lib(o.decode(A), W64)
+    for m in range(2):
+        for n in range(7):
+            exact = sum(Fraction(float(A[m, k])) * Fraction(float(W64[n, k])) for k in range(48))
+            assert abs(Fraction(float(Y[m, n])) - exact) <= Fraction(48) * Fraction(2) ** -52 * \
+                sum(abs(Fraction(float(A[m, k])) * Fraction(float(W64[n, k]))) for k in range(48))
+
+
 PINS = [pin_worked_examples, pin_exhaustive_nibbles, pin_pack_unpack_identity,
         pin_code_equals_zero_point_gives_zero, pin_bruteforce_exact,
         pin_integer_special_case, pin_linear_and_one_hot, pin_fp16_decode_all_patterns,
         pin_swiglu, pin_round_f16_against_numpy, pin_bias_epilogue, pin_group_indices,
-        pin_acc4_quantize, pin_acc4_matmul]
+        pin_acc4_quantize, pin_acc4_matmul, pin_library_products]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
