@@ -287,7 +287,7 @@ def finish(w):
 # Source files each variant's kernel is compiled from (its own file plus the
 # shared headers): a profile summary applies only while these are unchanged.
 CSRC = os.path.join(ROOT, "block_wise_int4_amd", "csrc")
-SHARED_HEADERS = ["mnb_device.hpp", "mnb_layout.hpp", "mnb_internal.hpp"]
+SHARED_HEADERS = ["mnb_device.hpp", "mnb_layout.hpp", "mnb_internal.hpp", "mnb_acc4.hpp"]
 VARIANT_SOURCE = {"gemv_accuracy4": "acc4.hip", "gemv": "gemv.hip", "gemm_small": "gemm_small.hip",
                   "gemm_mfma": "gemm_mfma.hip"}
 
