@@ -65,7 +65,8 @@ def parse():
     p.add_argument("--only", default="",
                    help="comma list of: prefill,small_m,down,gate_up,gemv,tiny,bias,act_order,accuracy4 "
                         "(default all); copy adds a plain 256 MiB device copy, the reference kernel "
-                        "for scaling the HBM byte counters")
+                        "for scaling the HBM byte counters; gidx adds the general group-index route at "
+                        "M = 1, 16 and 256 (never part of the default step)")
     return p.parse_args()
 
 
@@ -148,7 +149,7 @@ class Workload:
     of the CPU baseline leg)."""
 
     def __init__(self, name, config, M, weights, K, N, g, act="f16", sigma=1.0, seed=(0,), bias=None,
-                 act_order=False, accuracy4=False, copies=None):
+                 act_order=False, accuracy4=False, copies=None, group_indices=False):
         import numpy as np
         import torch
         from block_wise_int4_amd import mnb, synth
@@ -158,6 +159,7 @@ class Workload:
         qs = []
         self.perm = None
         self.g_idx = None
+        self.g_idx_dev = None
         for w in weights:
             args = (torch.from_numpy(w.packed.reshape(-1)).to(dev), torch.from_numpy(w.scales.reshape(-1)).to(dev),
                     None if w.zero_points is None else torch.from_numpy(w.zero_points.reshape(-1)).to(dev))
@@ -174,6 +176,12 @@ class Workload:
                 q = mnb.QuantWeight(d, out)
             else:
                 q = mnb.repack(*args, N, K, g)
+                if group_indices:
+                    # a seeded g_idx whose groups have random sizes (the
+                    # general route's input)
+                    rng = np.random.default_rng(seed + (9,))
+                    self.g_idx = rng.integers(0, K // g, K).astype(np.int32)
+                    self.g_idx_dev = torch.from_numpy(self.g_idx).to(dev)
             qs.append(q)
         self.A_host = synth.activation(M, K, act, sigma, seed)
         A = torch.from_numpy(self.A_host).to(dev)
@@ -190,7 +198,7 @@ class Workload:
             self.bias_stride = N if bias[0] == "rows" else 0
             self.bias_mode = bias[1]
             self.bytes += bias_rows * N * 2
-        if act_order:
+        if act_order or group_indices:
             self.bytes += K * 4                       # the group indices
         self.accuracy4 = accuracy4
         if accuracy4:
@@ -237,6 +245,8 @@ class Workload:
             elif self.accuracy4:
                 mnb.mnb_gemm_accuracy4(self.desc, ws[0], a, self.M, b, y,
                                        self.workspaces[r] if self.ws_bytes else None, self.ws_bytes)
+            elif self.g_idx_dev is not None:
+                mnb.mnb_gemm_group_indices(self.desc, ws[0], a, self.M, self.g_idx_dev, y)
             elif self.perm is not None:
                 mnb.mnb_gemm_act_order(self.desc, ws[0], a, self.M, self.perm, y, self.workspaces[r],
                                        self.ws_bytes)
@@ -289,7 +299,7 @@ def finish(w):
 CSRC = os.path.join(ROOT, "block_wise_int4_amd", "csrc")
 SHARED_HEADERS = ["mnb_device.hpp", "mnb_layout.hpp", "mnb_internal.hpp", "mnb_acc4.hpp"]
 VARIANT_SOURCE = {"gemv_accuracy4": "acc4.hip", "gemv": "gemv.hip", "gemm_small": "gemm_small.hip",
-                  "gemm_mfma": "gemm_mfma.hip"}
+                  "gemm_mfma": "gemm_mfma.hip", "gemm_gidx": "gidx.hip"}
 
 
 def kernel_source_sha(variant):
@@ -393,6 +403,13 @@ def build_workloads(only):
     if "gemv" in sel:
         c = S.DECODE_GEMV
         wl.append(Workload(c.name, "c2", 1, [S.workload_weights(c)], c.K, c.N, c.group, seed=c.seed + (1,)))
+    # the general group-index route, only on request (not part of a step)
+    if "gidx" in sel:
+        c = S.DECODE_GEMV
+        for M in (1, 16, 256):
+            wl.append(Workload(c.name.replace("decode GEMV M=1", "group-index route M=%d" % M) + ", g_idx of random group sizes", "N3", M,
+                               [S.workload_weights(c)], c.K, c.N, c.group, seed=c.seed + (M,),
+                               group_indices=True))
     return wl
 
 

@@ -16,7 +16,7 @@ LIB_DIR = os.path.join(HERE, "lib")
 LIB = os.path.join(LIB_DIR, "libmnb.so")
 
 SOURCES = ["mnb_api.cpp", "repack.hip", "act_order.hip", "gemv.hip", "gemm_small.hip", "gemm_mfma.hip",
-           "noalloc.hip", "f32_split.hip",
+           "noalloc.hip", "f32_split.hip", "gidx.hip",
            "acc4.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -17,6 +17,7 @@
 #include "../../include/mnb.h"
 #include "mnb_acc4.hpp"
 #include "mnb_internal.hpp"
+#include "mnb_gidx.hpp"
 
 using mnb::Layout;
 
@@ -460,6 +461,45 @@ mnb_status mnb_gemm_act_order(const mnb_weight_desc* w, const void* repacked, co
     if (e != hipSuccess) return launched(e, "act_order_permute");
     return gemm_common(w, repacked, workspace, m, a_dtype, mnb::Bias(), y,
                        static_cast<unsigned char*>(workspace) + a_bytes, workspace_bytes - a_bytes, stream);
+}
+
+mnb_status mnb_gemm_group_indices(const mnb_weight_desc* w, const void* repacked, const void* a, int64_t m,
+                                  int32_t a_dtype, const int32_t* g_idx, const void* bias,
+                                  int64_t bias_row_stride, int32_t bias_mode, void* y, void* stream)
+{
+    Layout L;
+    MNB_TRY(check_desc(w, &L));
+    MNB_TRY(check_act_dtype(a_dtype));
+    if (bias_mode != MNB_BIAS_FUSED && bias_mode != MNB_BIAS_AFTER_ROUND)
+        return fail(MNB_ERR_INVALID_ARGUMENT, "bias_mode must be MNB_BIAS_FUSED or MNB_BIAS_AFTER_ROUND (got %d)",
+                    (int)bias_mode);
+    if (bias_row_stride < 0)
+        return fail(MNB_ERR_INVALID_ARGUMENT, "bias_row_stride must be >= 0 (got %lld)",
+                    (long long)bias_row_stride);
+    if (m < 0) return fail(MNB_ERR_INVALID_ARGUMENT, "M must be >= 0 (got %lld)", (long long)m);
+    if (m > mnb::gidx_max_m())
+        return fail(MNB_ERR_UNSUPPORTED, "M must be at most %lld (got %lld)", (long long)mnb::gidx_max_m(),
+                    (long long)m);
+    if (bias && m > 1 && bias_row_stride > (INT64_MAX / 4 - L.N) / (m - 1))
+        return fail(MNB_ERR_INVALID_ARGUMENT, "bias extent (M-1)*%lld + N overflows", (long long)bias_row_stride);
+    if (L.K > INT32_MAX - mnb::kChunkK) return fail(MNB_ERR_UNSUPPORTED, "K too large for the group-index kernel");
+    if (m == 0 || L.N == 0) return ok("noop");
+    if (L.K > 0 && !g_idx) return fail(MNB_ERR_INVALID_ARGUMENT, "g_idx is NULL");
+    MNB_TRY(check_ptr(repacked, 256, "repacked"));
+    const uintptr_t elem = a_dtype == MNB_F32 ? 4 : 2;
+    MNB_TRY(check_ptr(a, 16, "a"));
+    MNB_TRY(check_ptr(y, elem, "y"));
+    if (g_idx) MNB_TRY(check_ptr(g_idx, 16, "g_idx"));
+    if (bias) MNB_TRY(check_ptr(bias, elem, "bias"));
+    MNB_TRY(check_device());
+    mnb::Bias b;
+    b.ptr = bias;
+    b.row_stride = bias_row_stride;
+    b.after_round = bias_mode == MNB_BIAS_AFTER_ROUND ? 1 : 0;
+    const char* variant = "";
+    const hipError_t e = mnb::launch_gemm_gidx(L, mnb::view_of(L, repacked), a, m, a_dtype == MNB_F16, g_idx, b, y,
+                                               static_cast<hipStream_t>(stream), &variant);
+    return launched(e, variant);
 }
 
 // int8 activations (accuracy_level 4): the workspace holds the activation

@@ -29,7 +29,7 @@ EXPORTS = ("mnb_repacked_bytes", "mnb_repacked_layout", "mnb_repack", "mnb_gemv"
            "mnb_gemv_gate_up_swiglu", "mnb_gemm_workspace_bytes", "mnb_gemm_workspace_bytes_for", "mnb_gemm",
            "mnb_gemm_bias",
            "mnb_act_order_permutation", "mnb_repack_act_order", "mnb_gemm_act_order_workspace_bytes",
-           "mnb_gemm_act_order", "mnb_gemm_accuracy4_workspace_bytes", "mnb_gemm_accuracy4",
+           "mnb_gemm_act_order", "mnb_gemm_group_indices", "mnb_gemm_accuracy4_workspace_bytes", "mnb_gemm_accuracy4",
            "mnb_gemm_accuracy4_noalloc",
            "mnb_unpack_debug", "mnb_status_string", "mnb_last_error", "mnb_last_variant")
 
@@ -92,6 +92,7 @@ def _load():
         "mnb_repack_act_order": (ctypes.c_int, [D, P, P, P, P, P, P]),
         "mnb_gemm_act_order_workspace_bytes": (sz, [D, i64, i32]),
         "mnb_gemm_act_order": (ctypes.c_int, [D, P, P, i64, i32, P, P, P, sz, P]),
+        "mnb_gemm_group_indices": (ctypes.c_int, [D, P, P, i64, i32, P, P, i64, i32, P, P]),
         "mnb_gemm_accuracy4_workspace_bytes": (sz, [D, i64]),
         "mnb_gemm_accuracy4": (ctypes.c_int, [D, P, P, i64, P, P, P, sz, P]),
         "mnb_gemm_accuracy4_noalloc": (ctypes.c_int, [D, P, P, i64, P, P, P]),
@@ -254,6 +255,14 @@ def mnb_gemm_act_order(w: mnb_weight_desc, repacked: Ptr, a, m: int, perm: Ptr, 
             workspace.numel() * workspace.element_size()
     _check(lib.mnb_gemm_act_order(ctypes.byref(w), _ptr(repacked), _ptr(a), m, dt, _ptr(perm), _ptr(y),
                                   _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def mnb_gemm_group_indices(w: mnb_weight_desc, repacked: Ptr, a, m: int, g_idx: Ptr, y, bias=None,
+                           bias_row_stride: int = 0, bias_mode: int = MNB_BIAS_FUSED,
+                           a_dtype: Optional[int] = None, stream=None) -> None:
+    dt = _dtype_code(a) if a_dtype is None else a_dtype
+    _check(lib.mnb_gemm_group_indices(ctypes.byref(w), _ptr(repacked), _ptr(a), m, dt, _ptr(g_idx), _ptr(bias),
+                                      bias_row_stride, bias_mode, _ptr(y), _stream(stream)))
 
 
 def mnb_gemm_accuracy4_workspace_bytes(w: mnb_weight_desc, m: int) -> int:

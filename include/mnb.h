@@ -242,13 +242,14 @@ mnb_status mnb_gemm_bias(const mnb_weight_desc* w, const void* repacked, const v
  *   dequant(B)[n,k] = (code[n,k] - zp[n, g_idx[k]]) * scale[n, g_idx[k]].
  * The repack sorts k by group, so every group becomes contiguous, and the
  * GEMM takes A's columns in the same order; the product is the same sum over
- * k in another order.  Three steps:
+ * k in another order.  Three steps, and a fourth for any g_idx:
  *
  * 1. mnb_act_order_permutation (host only, host pointers, no HIP call):
  *    checks g_idx (every value in 0..k_blocks-1, else
  *    MNB_ERR_INVALID_ARGUMENT; every group with exactly group_size members,
- *    else MNB_ERR_UNSUPPORTED) and writes perm [K]: the positions of group 0
- *    in increasing k, then those of group 1, and so on. */
+ *    else MNB_ERR_UNSUPPORTED, and step 4 below serves that g_idx) and
+ *    writes perm [K]: the positions of group 0 in increasing k, then those
+ *    of group 1, and so on; perm is written only on MNB_OK. */
 mnb_status mnb_act_order_permutation(const mnb_weight_desc* w, const int32_t* g_idx, int32_t* perm);
 
 /* 2. mnb_repack_act_order: mnb_repack of the same ONNX operands with the
@@ -274,6 +275,30 @@ size_t mnb_gemm_act_order_workspace_bytes(const mnb_weight_desc* w, int64_t m, i
 mnb_status mnb_gemm_act_order(const mnb_weight_desc* w, const void* repacked, const void* a, int64_t m,
                               int32_t a_dtype, const int32_t* perm, void* y, void* workspace,
                               size_t workspace_bytes, void* stream);
+
+/* 4. Any g_idx, groups of any size: the general route of the fp32
+ *    operator (matmul_nbits.rs, MatMulNBitsKernel::run with group_indices:
+ *    the dequant kernel with group_indices, then the dense GEMM with its
+ *    bias), for a g_idx that mnb_act_order_permutation answers with
+ *    MNB_ERR_UNSUPPORTED, or any other:
+ *      Y[m,n] = epilogue(sum_k A[m,k] * (code[n,k] - zp[n,G]) * scale[n,G]),
+ *    G = g_idx[k], the sum in fp32 over k in increasing order, each weight
+ *    (code - zp) * scale formed in fp32 (exact for fp16 scales).  repacked:
+ *    the plain mnb_repack buffer (codes at their ONNX positions).  g_idx:
+ *    device int32 [K], 16-byte aligned; a value outside 0..k_blocks-1 gives
+ *    the weight 0 at that k, as the dequant kernel does (the operator
+ *    rejects such a g_idx on the host beforehand;
+ *    mnb_act_order_permutation makes that check, MNB_ERR_INVALID_ARGUMENT).
+ *    A (device, [M,K], 16-byte aligned) and Y (device, [M,N], element-
+ *    aligned) of a_dtype; bias, bias_row_stride and bias_mode as for
+ *    mnb_gemm_bias (bias NULL for none).  Any M >= 1 up to 65535*64 (else
+ *    MNB_ERR_UNSUPPORTED), no workspace, K below 2^31 - 128.  M <= 16
+ *    streams the weight (fp32 vector products); larger M stages the
+ *    dequantized 64-column block and 64 rows of A in LDS for fp32 matrix-core
+ *    products (v_mfma_f32_16x16x4_f32).  Deterministic. */
+mnb_status mnb_gemm_group_indices(const mnb_weight_desc* w, const void* repacked, const void* a, int64_t m,
+                                  int32_t a_dtype, const int32_t* g_idx, const void* bias,
+                                  int64_t bias_row_stride, int32_t bias_mode, void* y, void* stream);
 
 /* int8 activations: accuracy_level = 4 of the fp32 operator
  * (onnx-runtime-ep-cuda 0.1.0-dev.3, src/kernels/matmul_nbits.rs, kernels

@@ -13,6 +13,7 @@
 #include "mnb.h"
 #include "mnb_acc4.hpp"
 #include "mnb_internal.hpp"
+#include "mnb_gidx.hpp"
 
 namespace mnb {
 int64_t gemv_max_k(bool, bool) { return int64_t(1) << 30; }
@@ -39,6 +40,9 @@ hipError_t launch_gemm_mfma_f32(const Layout&, const WeightView&, const void*, i
                                 const float*, float*, hipStream_t, const char**, int, int64_t) { std::abort(); }
 hipError_t launch_split_f32_rows(const float*, int64_t, int64_t, _Float16*, float*, hipStream_t) { std::abort(); }
 hipError_t noalloc_scratch(int, void**) { std::abort(); }
+int64_t gidx_max_m() { return int64_t(65535) * 64; }
+hipError_t launch_gemm_gidx(const Layout&, const WeightView&, const void*, int64_t, bool, const int32_t*,
+                            const Bias&, void*, hipStream_t, const char**) { std::abort(); }
 }  // namespace mnb
 
 static int failures = 0;
@@ -139,6 +143,26 @@ int main()
     expect(mnb_gemm_act_order(&d, fake, fake, 40, MNB_F16, nullptr, fake, fake, wsa, nullptr), INV, "perm NULL");
     expect(mnb_gemm_act_order(&d, fake, fake, 40, MNB_F16, static_cast<const int32_t*>(fake), fake, fake, wsa - 1,
                               nullptr), INV, "act-order workspace too small");
+    // any g_idx: validation, then the device
+    const int32_t* fg = static_cast<const int32_t*>(fake);
+    expect(mnb_gemm_group_indices(&d, fake, fake, 40, MNB_F16, nullptr, nullptr, 0, MNB_BIAS_FUSED, fake, nullptr),
+           INV, "group indices NULL");
+    expect(mnb_gemm_group_indices(&d, fake, fake, 40, MNB_F16, fg, nullptr, -1, MNB_BIAS_FUSED, fake, nullptr), INV,
+           "group indices negative bias stride");
+    expect(mnb_gemm_group_indices(&d, fake, fake, 40, MNB_F16, fg, nullptr, 0, 7, fake, nullptr), INV,
+           "group indices bias mode");
+    expect(mnb_gemm_group_indices(&d, fake, fake, 40, MNB_F32, fg, nullptr, 0, MNB_BIAS_FUSED, fakec + 2, nullptr),
+           INV, "group indices misaligned fp32 output");
+    expect(mnb_gemm_group_indices(&d, fake, fake, 40, MNB_F16, reinterpret_cast<const int32_t*>(fakec + 4), nullptr,
+                                  0, MNB_BIAS_FUSED, fake, nullptr), INV, "group indices misaligned g_idx");
+    expect(mnb_gemm_group_indices(&d, fake, fakec + 8, 40, MNB_F16, fg, nullptr, 0, MNB_BIAS_FUSED, fake, nullptr),
+           INV, "group indices misaligned activation");
+    expect(mnb_gemm_group_indices(&d, fake, fake, int64_t(65535) * 64 + 1, MNB_F16, fg, nullptr, 0, MNB_BIAS_FUSED,
+                                  fake, nullptr), UNS, "group indices M beyond the grid");
+    expect(mnb_gemm_group_indices(&d, fake, fake, 0, MNB_F16, nullptr, nullptr, 0, MNB_BIAS_FUSED, fake, nullptr),
+           MNB_OK, "group indices M = 0");
+    expect(mnb_gemm_group_indices(&d, fake, fake, 40, MNB_F32, fg, fake, 512, MNB_BIAS_FUSED, fake, nullptr), DEV,
+           "valid group-indices call without a device");
     expect(mnb_unpack_debug(&d, fakec + 16, nullptr, nullptr, nullptr), INV, "unpack misaligned");
     for (int s = -1; s < 6; ++s)
         if (std::strlen(mnb_status_string(s)) == 0) {

@@ -47,6 +47,8 @@ def _setup(mnb):
     rep_ao = t.empty(mnb.mnb_repacked_bytes(q.desc), dtype=t.uint8, device="cuda")
     mnb.mnb_repack_act_order(q.desc, G.to_dev(w.packed.reshape(-1)), G.to_dev(w.scales.reshape(-1)),
                              G.to_dev(w.zero_points.reshape(-1)), perm, rep_ao)
+    # a g_idx of uneven groups for the general route
+    gi_any = G.to_dev(rng.integers(0, K // 32, K).astype(np.int32))
     n_ao = mnb.mnb_gemm_act_order_workspace_bytes(q.desc, 40, mnb.MNB_F16)
     n_a4 = mnb.mnb_gemm_accuracy4_workspace_bytes(q32.desc, 40)
     n_g = max(mnb.mnb_gemm_workspace_bytes(q.desc, 8), 16)
@@ -59,6 +61,8 @@ def _setup(mnb):
         "act_order": t.empty((40, N), dtype=t.float16, device="cuda"),
         "acc4_decode": t.empty((1, N), dtype=t.float32, device="cuda"),
         "acc4_prefill": t.empty((40, N), dtype=t.float32, device="cuda"),
+        "gidx_stream": t.empty((8, N), dtype=t.float16, device="cuda"),
+        "gidx_mfma": t.empty((40, N), dtype=t.float32, device="cuda"),
     }
     t.cuda.synchronize()
 
@@ -73,6 +77,9 @@ def _setup(mnb):
         mnb.mnb_gemm_accuracy4(q32.desc, q32.repacked, f1, 1, bias32, outs["acc4_decode"], stream=stream)
         mnb.mnb_gemm_accuracy4(q32.desc, q32.repacked, f40, 40, bias32, outs["acc4_prefill"], ws["a4"], n_a4,
                                stream=stream)
+        mnb.mnb_gemm_group_indices(q.desc, q.repacked, a8, 8, gi_any, outs["gidx_stream"], stream=stream)
+        mnb.mnb_gemm_group_indices(q.desc, q.repacked, f40, 40, gi_any, outs["gidx_mfma"], bias32, 0,
+                                   stream=stream)
 
     return issue, outs
 

@@ -606,6 +606,105 @@ def test_act_order_parity(mnb, M, N, K, g, adt, zp):
         assert t.equal(y, y2)
 
 
+GIDX_CASES = [
+    # M, N, K, g, activation dtype, scale dtype, zp, how g_idx is drawn
+    (1, 300, 512, 32, "f32", "f32", True, "random"),    # the fp32 operator's decode
+    (1, 257, 400, 16, "f16", "f16", True, "random"),    # K not a multiple of the 128-k chunk
+    (5, 1000, 1024, 64, "f32", "f16", False, "random"),
+    (40, 70, 384, 128, "f16", "f32", True, "skewed"),   # sizes far from g, some groups empty
+    (130, 60, 896, 32, "f32", "f32", False, "one"),     # every k in one group
+    (17, 48, 512, 32, "f16", "f16", True, "whole"),     # whole groups: the sorted route's input
+    (3, 40, 640, 64, "f32", "f16", True, "range"),      # values outside 0..k_blocks-1 weigh 0
+    (16, 33, 512, 32, "f16", "f16", True, "random"),    # the largest M of the streaming kernel
+    (17, 200, 1024, 16, "f32", "f32", True, "random"),  # the smallest of the matrix-core kernel
+    (300, 130, 768, 128, "f16", "f16", False, "range"),
+    # metadata too large for LDS (2048 groups of fp32 scales and zero points;
+    # 512 groups for the four tiles of the matrix-core kernel): read from L2
+    (2, 40, 32768, 16, "f16", "f32", True, "random"),
+    (70, 48, 8192, 16, "f32", "f32", True, "random"),
+]
+
+
+def _g_idx(kind, K, kb, rng):
+    if kind == "random":
+        return rng.integers(0, kb, K).astype(np.int32)
+    if kind == "skewed":
+        # group b drawn with weight 2^-b: a few large groups, many empty
+        p = 0.5 ** np.arange(kb)
+        return rng.choice(kb, K, p=p / p.sum()).astype(np.int32)
+    if kind == "one":
+        return np.full(K, kb // 2, np.int32)
+    if kind == "whole":
+        g = np.empty(K, np.int32)
+        g[rng.permutation(K)] = np.arange(K) // (K // kb)
+        return g
+    g = rng.integers(0, kb, K).astype(np.int32)
+    g[rng.choice(K, K // 8, replace=False)] = rng.choice(np.array([-1, kb, -(1 << 30), 1 << 30], np.int32), K // 8)
+    return g
+
+
+@pytest.mark.parametrize("M,N,K,g,adt,sdt,zp,kind", GIDX_CASES)
+def test_group_indices_parity(mnb, M, N, K, g, adt, sdt, zp, kind):
+    """Any g_idx through the general route (plain repack, scale and zero
+    point of group g_idx[k] looked up per k): against the oracle's act-order
+    dequant and fp64 matmul, without a bias, with a bias vector and with a
+    per-row bias (fused mode under its bound, after-round mode bit for bit
+    against the oracle's epilogue on the unbiased output); two calls agree
+    bit for bit; the host check's answer for this g_idx."""
+    t = G.torch()
+    kb = K // g
+    w = _weight(N, K, g, sdt, zp, seed=M + 11)
+    rng = np.random.default_rng(M * 131 + K + kb)
+    g_idx = _g_idx(kind, K, kb, rng)
+    A = _act(M, K, adt, seed=M + 12)
+    q = G.upload(w)
+    gi = G.to_dev(g_idx)
+    a = G.to_dev(A)
+    odt = t.float16 if adt == "f16" else t.float32
+    ndt = np.float16 if adt == "f16" else np.float32
+    y = t.empty((M, N), dtype=odt, device="cuda")
+    mnb.mnb_gemm_group_indices(q.desc, q.repacked, a, M, gi, y)
+    assert mnb.mnb_last_variant() == "gemm_gidx_%s_%s" % ("stream" if M <= 16 else "mfma", adt)
+    y2 = t.empty_like(y)
+    mnb.mnb_gemm_group_indices(q.desc, q.repacked, a, M, gi, y2)
+    W = o.dequant_gidx(w.packed, w.scales, w.zero_points, g_idx, N, K, g)
+    Y, B = o.matmul(o.decode(A.reshape(-1, K)), W)
+    what = "group indices %s M=%d N=%d K=%d g=%d %s/%s" % (kind, M, N, K, g, adt, sdt)
+    G.assert_within(G.host(y), Y, B, what)
+    assert t.equal(y, y2), what + " (two calls)"
+    y0h = y.cpu().numpy()
+    for stride in (0, N):
+        rows = M if stride else 1
+        bias = (rng.standard_normal((rows, N)) * 2.0).astype(ndt)
+        bias_dev = G.to_dev(bias.reshape(-1))
+        b64 = np.broadcast_to(bias.astype(np.float64), (M, N))
+        outs = {}
+        for mode in (mnb.MNB_BIAS_FUSED, mnb.MNB_BIAS_AFTER_ROUND):
+            yb = t.empty((M, N), dtype=odt, device="cuda")
+            mnb.mnb_gemm_group_indices(q.desc, q.repacked, a, M, gi, yb, bias_dev, stride, mode)
+            outs[mode] = yb.cpu().numpy()
+        yf, ya = outs[mnb.MNB_BIAS_FUSED], outs[mnb.MNB_BIAS_AFTER_ROUND]
+        b_mn = np.broadcast_to(bias, (M, N))
+        if adt == "f16":
+            want = o.bias_epilogue_f16(y0h.astype(np.float32), b_mn, True)
+            assert (ya.view(np.uint16) == want.view(np.uint16)).all(), what + " (after-round)"
+            tol = o.bias_bound(Y, B, b64)
+        else:
+            assert (yf.view(np.uint32) == ya.view(np.uint32)).all(), what
+            assert (yf == (y0h + b_mn)).all(), what
+            tol = o.REL_TOL * B + o.ABS_TOL + 2.0 ** -23 * np.abs(Y + b64)
+        G.assert_within(yf.astype(np.float64), Y + b64, B, what + " bias stride %d" % stride, bound=tol)
+    # the host check: whole groups are the sorted route's, others this one's
+    d = mnb.desc(N, K, g, zp, mnb.MNB_F16 if sdt == "f16" else mnb.MNB_F32)
+    if kind == "whole":
+        mnb.mnb_act_order_permutation(d, g_idx)
+    else:
+        with pytest.raises(mnb.MnbError) as e:
+            mnb.mnb_act_order_permutation(d, g_idx)
+        want = mnb.MNB_ERR_INVALID_ARGUMENT if kind == "range" else mnb.MNB_ERR_UNSUPPORTED
+        assert e.value.status == want
+
+
 # ------------------------------------------------------------ properties ----
 
 def test_results_are_deterministic(mnb):
