@@ -66,7 +66,8 @@ def parse():
                    help="comma list of: prefill,small_m,down,gate_up,gemv,tiny,bias,act_order,accuracy4 "
                         "(default all); copy adds a plain 256 MiB device copy, the reference kernel "
                         "for scaling the HBM byte counters; gidx adds the general group-index route at "
-                        "M = 1, 16 and 256 (never part of the default step)")
+                        "M = 1, 16 and 256, prefill_groups the prefill GEMM at g = 64, 32 and 16 (neither "
+                        "is part of the default step)")
     return p.parse_args()
 
 
@@ -403,6 +404,14 @@ def build_workloads(only):
     if "gemv" in sel:
         c = S.DECODE_GEMV
         wl.append(Workload(c.name, "c2", 1, [S.workload_weights(c)], c.K, c.N, c.group, seed=c.seed + (1,)))
+    # the prefill at the other group sizes, only on request (not part of a step)
+    if "prefill_groups" in sel:
+        import dataclasses
+        c0 = S.PREFILL_GEMM
+        for g in (64, 32, 16):
+            c = dataclasses.replace(c0, name=c0.name.replace("g=128", "g=%d" % g), group=g, seed=c0.seed + (g,))
+            wl.append(Workload(c.name, "c5-g%d" % g, c.M, [S.workload_weights(c)], c.K, c.N, c.group,
+                               sigma=c.sigma, seed=c.seed + (c.M,)))
     # the general group-index route, only on request (not part of a step)
     if "gidx" in sel:
         c = S.DECODE_GEMV

@@ -10,7 +10,11 @@
 // * v_mfma_f32_32x32x16_f16 (32x32 output, 16 k).
 // * Workgroup tile 96 (M) x 256 (N), 4 waves; wave w owns columns
 //   [64w, +64) of all 96 rows: 3 row blocks x 2 column pairs of 32x32 tiles.
-//   Two workgroups share a CU (two waves per SIMD).
+//   Two workgroups share a CU (two waves per SIMD).  Groups of 32 or 16 k
+//   (and fp32 scales with zero points at 64 k) use 64-row tiles (2 row
+//   blocks): their per-chunk rescale factors and zero points would push a
+//   96-row wave past 256 registers or its stages past half the LDS, one
+//   wave per SIMD, which measured twice as slow.
 // * A rows reach LDS by buffer_load ... lds (no VGPR round trip) into a ring
 //   of as many stages as the workgroup's share of LDS holds (three for the
 //   common record sizes); the DMAs of chunk c + stages - 1 are spread over the
@@ -54,10 +58,8 @@ namespace mnb {
 
 namespace {
 
-constexpr int BM = 96;             // rows per workgroup
 constexpr int BN = 256;            // columns per workgroup (16 tiles of 16)
 constexpr int WAVES = 4;           // one per SIMD; wave w owns columns [64w, 64w+64)
-constexpr int RB = BM / 32;        // 32-row blocks per wave
 constexpr int PAIRS = 2;           // 32-column pairs of tiles per wave
 constexpr int TPW = 2 * PAIRS;     // 16-column tiles per wave
 constexpr int SEGS = kChunkK / 8;  // 16-byte segments per A row per chunk
@@ -66,9 +68,8 @@ constexpr int kWgPerCu = 8 / WAVES;          // two waves per SIMD
 constexpr int kLdsCu = 160 * 1024;
 constexpr int kLdsBudget = kLdsCu / kWgPerCu;   // this workgroup's share
 constexpr int kMaxStages = 6;
-constexpr int ROWS_PER_WAVE = BM / WAVES;   // A rows each wave copies per chunk
-constexpr int A_DMA = ROWS_PER_WAVE / 4;    // 1 KiB (4-row) DMAs per wave per chunk
-static_assert(ROWS_PER_WAVE % 4 == 0, "A is copied in 4-row pieces");
+constexpr int kMaxBM = 96;
+
 
 typedef float f16v_t __attribute__((ext_vector_type(16)));
 
@@ -97,7 +98,11 @@ struct GemmParams {
     int64_t flags_off;     // the per-tile scale range classes
 };
 
-// LDS geometry of one pipeline stage for (Q, scale bytes, zero points).
+// Tile height and LDS geometry of one pipeline stage for (Q, scale bytes,
+// zero points).  Rows per workgroup: 96 when a 96-row stage leaves room for
+// three stages in the workgroup's half of the LDS and groups span 64 k or
+// more; else 64 (groups of 32 or 16 k, whose per-chunk rescale factors and
+// zero points would also push a 96-row wave past 256 registers).
 template <int Q, int SS, bool HAS_ZP> struct StageGeom {
     static constexpr int kScaleDw = kTileN * Q * SS / 4;               // dwords per tile record
     static constexpr int kZpDw = HAS_ZP ? kTileN * Q / 8 : 0;          // 8Q bytes per tile record
@@ -108,9 +113,15 @@ template <int Q, int SS, bool HAS_ZP> struct StageGeom {
     static constexpr int kMetaInstr = kScaleInstr + kZpInstr;
     static constexpr int kZpOffDw = kScaleInstr * 64;                  // zero points in the record
     static constexpr int kMetaDwPad = kMetaInstr * 64;
+    static constexpr int kMeta = WAVES * kMetaDwPad * 4;
+    static constexpr bool kTall = Q < 4 && kLdsBudget / (kMaxBM * SEGS * 16 + kMeta) >= 3;
+    static constexpr int BM = kTall ? kMaxBM : 64;
+    static constexpr int RB = BM / 32;                  // 32-row blocks per wave
+    static constexpr int ROWS_PER_WAVE = BM / WAVES;    // A rows each wave copies per chunk
+    static constexpr int A_DMA = ROWS_PER_WAVE / 4;     // 1 KiB (4-row) DMAs per wave per chunk
+    static_assert(ROWS_PER_WAVE % 4 == 0, "A is copied in 4-row pieces");
     static constexpr int kA = BM * SEGS * 16;                          // bytes
     static constexpr int kB = 0;                                       // codes go to VGPRs
-    static constexpr int kMeta = WAVES * kMetaDwPad * 4;
     static constexpr int kBytes = kA + kB + kMeta;
     // as many pipeline stages as the workgroup's share of LDS holds (up to
     // kMaxStages); when that is fewer than three (large scale records), three
@@ -204,6 +215,7 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
 {
     typedef StageGeom<Q, (int)sizeof(ST), HAS_ZP> G;
     constexpr int NST = G::kStages;
+    constexpr int BM = G::BM, RB = G::RB, ROWS_PER_WAVE = G::ROWS_PER_WAVE, A_DMA = G::A_DMA;
     __shared__ __align__(16) unsigned char lds[KernelLds<ST, Q, HAS_ZP>::kBytes];
 
     const int tid = threadIdx.x;
@@ -693,14 +705,14 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
             const int n = nb * BN + wave * 64 + (lane & 15) * 4;
 #pragma unroll
             for (int hp = 0; hp < 2; ++hp) {
-                // 8-row block rb*4 + e/4 of the wave's 96 rows is in pass (rb*4 + e/4) / 6
+                // 8-row block rb*4 + e/4 of the wave's BM rows is in pass (rb*4 + e/4) / (HALF/8)
 #pragma unroll
                 for (int q = 0; q < PAIRS; ++q)
 #pragma unroll
                     for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                         for (int e = 0; e < 16; ++e) {
-                            if ((rb * 4 + (e >> 2)) / 6 != hp) continue;
+                            if ((rb * 4 + (e >> 2)) / (HALF / 8) != hp) continue;
                             const int row = rb * 32 + 8 * (e >> 2) + 4 * oct + (e & 3) - hp * HALF;
                             *reinterpret_cast<float*>(ob + row * RS + (q * 32 + (lane & 31)) * 4) = value(rb, q, e);
                         }
@@ -826,8 +838,11 @@ void launch_k(const GemmParams& p, hipStream_t s)
 }
 
 template <typename ST, int Q, bool HAS_ZP>
-hipError_t launch_t(const GemmParams& p, hipStream_t s)
+hipError_t launch_t(const GemmParams& p0, hipStream_t s)
 {
+    GemmParams p = p0;
+    constexpr int BM = StageGeom<Q, (int)sizeof(ST), HAS_ZP>::BM;
+    p.num_m = (p.M + BM - 1) / BM;
     if (p.row_scale)
         launch_k<ST, Q, HAS_ZP, true>(p, s);
     else
@@ -849,12 +864,12 @@ hipError_t launch_q(const Layout& L, const GemmParams& p, hipStream_t s)
 }  // namespace
 
 // Largest K the kernel's 32-bit buffer ranges and offsets cover: a
-// workgroup's BM rows of A (BM * K * 2 bytes) and the code bytes of its
+// workgroup's rows of A (at most 96 * K * 2 bytes) and the code bytes of its
 // BN / 16 tiles (BN / 16 * C * 1024) each stay below 2^31.
 int64_t gemm_mfma_max_k()
 {
     const int64_t lim = (int64_t(1) << 31) - 1;
-    const int64_t by_a = lim / (2 * BM);
+    const int64_t by_a = lim / (2 * kMaxBM);
     const int64_t by_codes = lim / ((BN / 16) * 1024) * kChunkK;
     return by_a < by_codes ? by_a : by_codes;
 }
@@ -882,7 +897,7 @@ hipError_t launch_gemm_mfma(const Layout& L, const WeightView& w, const void* a,
     p.K = (int)L.K;
     p.C = (int)L.C;
     p.T = (int)L.T;
-    p.num_m = (int)((m + BM - 1) / BM);
+    p.num_m = 0;   // set per tile height in launch_t
     p.num_n = (int)((L.N + BN - 1) / BN);
     p.vec_store = (L.N % 8 == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0) ? 1 : 0;
     p.flags_off = L.flags_off;
@@ -916,7 +931,7 @@ hipError_t launch_gemm_mfma_f32(const Layout& L, const WeightView& w, const void
     p.K = (int)L.K;
     p.C = (int)L.C;
     p.T = (int)L.T;
-    p.num_m = (int)((m + BM - 1) / BM);
+    p.num_m = 0;   // set per tile height in launch_t
     p.num_n = (int)((L.N + BN - 1) / BN);
     p.vec_store = (L.N % 4 == 0 && reinterpret_cast<uintptr_t>(y) % 16 == 0) ? 1 : 0;
     p.flags_off = L.flags_off;

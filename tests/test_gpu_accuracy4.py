@@ -68,6 +68,10 @@ ACC4_CASES = [
     (16, 100, 1024, 16, "f32", True, True),
     (40, 300, 512, 64, "f32", True, True), (130, 70, 384, 128, "f16", False, False),
     (200, 513, 1024, 32, "f32", True, True),
+    # the prefill's 64-row tiles (groups of 32 or 16 k, fp32 scales with zero
+    # points at 64 k) with 16-byte fp32 row stores (N % 4 == 0), ragged M
+    (150, 256, 1024, 32, "f32", True, True), (97, 260, 512, 16, "f16", False, False),
+    (70, 128, 768, 64, "f32", True, True),
     # K not a multiple of the 128-k chunk: the last chunk's padding
     (1, 70, 400, 16, "f32", True, True), (3, 70, 352, 32, "f16", True, False),
     (33, 70, 400, 16, "f32", True, True), (1, 90, 1088, 64, "f16", False, True),

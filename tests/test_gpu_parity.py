@@ -310,7 +310,11 @@ def test_small_m_ragged_parity(mnb, M, N, K, g, zp):
 
 PREFILL_CASES = [(17, 70, 384, 128, True, "f16"), (130, 300, 512, 64, True, "f16"),
                  (64, 257, 256, 32, False, "f32"), (33, 40, 160, 16, True, "f16"),
-                 (300, 512, 1024, 128, False, "f16"), (129, 16, 4096, 128, True, "f16")]
+                 (300, 512, 1024, 128, False, "f16"), (129, 16, 4096, 128, True, "f16"),
+                 # 64-row tiles: groups of 32 or 16 k, and fp32 scales with
+                 # zero points at 64 k; several row blocks and a ragged one
+                 (200, 300, 1024, 32, True, "f16"), (65, 64, 256, 32, False, "f16"),
+                 (150, 130, 640, 64, True, "f32"), (130, 96, 512, 16, True, "f32")]
 
 
 @pytest.mark.parametrize("M,N,K,g,zp,sdt", PREFILL_CASES)
@@ -802,7 +806,8 @@ F32_CASES = [
     # rows, the prefill kernel beyond, K tails, every group size
     (2, 200, 512, 32, "f16", True), (5, 257, 896, 64, "f32", False), (8, 130, 384, 128, "f16", True),
     (9, 96, 1024, 16, "f16", True), (16, 300, 512, 64, "f32", True), (40, 513, 1024, 32, "f16", True),
-    (200, 300, 384, 128, "f16", False), (33, 70, 400, 16, "f32", True), (3, 70, 352, 32, "f16", True)]
+    (200, 300, 384, 128, "f16", False), (33, 70, 400, 16, "f32", True), (3, 70, 352, 32, "f16", True),
+    (70, 256, 512, 32, "f16", True)]
 
 
 def _f32_rows(M, K, seed):
