@@ -14,17 +14,16 @@
 // one rounding for fp32 ones), and the products are summed in fp32, as the
 // dequant-then-GEMM route does; nothing goes through a dense weight in memory.
 //
-// gfx950 design, two kernels:
-//  * M <= 16 (weight streaming): a workgroup of 16 waves owns one 16-column
-//    tile; each wave takes every 16th 128-k chunk, one lane per 16-byte lane
-//    record (one column, 32 k), dequantizes its 32 weights in registers and
-//    multiplies them into up to 16 rows of A read straight from L2.  No
-//    barrier inside the loop; the 4 lanes of a column and then the 16 waves
-//    are summed in a fixed order at the end.
-//  * M > 16 (a dense contraction): a workgroup of 4 waves owns 64 rows x 64
-//    columns (4 tiles); per chunk it stages A (fp32, row-major) and the
-//    dequantized weights (fp32, k-major) in LDS and runs
-//    v_mfma_f32_16x16x4_f32, each wave 16 rows x 64 columns.
+// gfx950 design, one weight-streaming kernel: a workgroup of 16 waves owns
+// one 16-column tile and a block of rows (up to 16 rows when M <= 16, else
+// 64), and first writes a table of the tile's (zero point, scale) pairs per
+// group to LDS (read from L2 instead when the table is too large).  Each wave
+// takes every 16th 128-k chunk, one lane per 16-byte lane record (one column,
+// 32 k), and dequantizes its 32 weights in registers, one table read each.
+// It multiplies them into the rows of A, read straight from L2: one row by
+// fp32 fma, more on v_mfma_f32_16x16x4_f32, each word's weights reused for
+// every block of 16 rows.  No barrier inside the loop; the lanes of a column
+// and then the 16 waves are summed in a fixed order at the end.
 #include <type_traits>
 
 #include "mnb_device.hpp"
@@ -36,17 +35,14 @@ namespace {
 
 typedef float fx4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kSmallM = 16;     // largest M of the weight-streaming kernel
+constexpr int kSmallM = 16;     // rows per workgroup when M <= 16
+constexpr int kBigRows = 64;    // rows per workgroup beyond
 constexpr int kSmallWaves = 16;
-constexpr int kBigRows = 64;    // rows of A per workgroup of the MFMA kernel
-constexpr int kBigTiles = 4;    // 16-column tiles per workgroup of the MFMA kernel
-constexpr int kAPad = 4;        // a_s row stride 132 floats: the A-fragment reads hit 64 banks
-constexpr int kWPad = 16;       // w_s row stride 80 floats: the B-fragment reads hit 64 banks
-// LDS for the tiles' scales and zero points (else they are read from L2):
-// the streaming kernel's 1024 threads keep one workgroup per CU anyway; the
-// matrix-core kernel's 74 KiB of staging leave this much of the 160 KiB.
+// LDS for the table of (zero point, scale) pairs, 128 bytes per group (else
+// the pairs are read from L2): 1024 threads keep one workgroup per CU
+// anyway; beside the 64 KiB reduction array of 64 rows, less.
 constexpr int64_t kSmallMetaLds = 96 * 1024;
-constexpr int64_t kBigMetaLds = 80 * 1024;
+constexpr int64_t kBigTableLds = 80 * 1024;
 
 struct GidxParams {
     const uint4* codes;      // repacked codes section, one 16-byte lane record per element
@@ -78,36 +74,6 @@ __device__ __forceinline__ TileMeta<ST> global_meta(const GidxParams& p, int64_t
                         p.zp ? p.zp + rec * (kTileN / 2) * p.Q : nullptr};
 }
 
-// Bytes of one tile's metadata in LDS: its scales, then its zero points at the
-// next 16-byte boundary.
-__host__ __device__ inline int64_t meta_scale_bytes(int64_t C, int Q, int ss) { return C * kTileN * Q * ss; }
-__host__ __device__ inline int64_t meta_bytes(int64_t C, int Q, int ss, bool has_zp)
-{
-    return (meta_scale_bytes(C, Q, ss) + 15) / 16 * 16 + (has_zp ? (C * (kTileN / 2) * Q + 15) / 16 * 16 : 0);
-}
-
-// Copy tile t's metadata into LDS at dst (16-byte aligned) with the
-// workgroup's threads (the caller synchronizes after): the scales in 16-byte
-// pieces (each chunk record is a multiple of 32 bytes and the tile's first is
-// 32-byte aligned), the zero points in 4-byte pieces (records of 8Q bytes).
-template <typename ST, bool HAS_ZP>
-__device__ __forceinline__ TileMeta<ST> stage_meta(const GidxParams& p, int64_t t, unsigned char* dst,
-                                                   int tid, int nthreads)
-{
-    const TileMeta<ST> g = global_meta<ST>(p, t);
-    const int64_t sb = meta_scale_bytes(p.C, p.Q, (int)sizeof(ST));
-    const uint4* ss = reinterpret_cast<const uint4*>(g.scales);
-    uint4* sd = reinterpret_cast<uint4*>(dst);
-    for (int64_t v = tid; v < sb / 16; v += nthreads) sd[v] = ss[v];
-    unsigned char* zd = dst + (sb + 15) / 16 * 16;
-    if (HAS_ZP) {
-        const int64_t zb = (int64_t)p.C * (kTileN / 2) * p.Q;
-        const uint32_t* zs = reinterpret_cast<const uint32_t*>(g.zp);
-        for (int64_t v = tid; v < zb / 4; v += nthreads) reinterpret_cast<uint32_t*>(zd)[v] = zs[v];
-    }
-    return TileMeta<ST>{reinterpret_cast<const ST*>(dst), HAS_ZP ? zd : nullptr};
-}
-
 // The weights of one 32-bit word of a lane record of tile t (metadata mt):
 // column i = lane % 16, k = k0 + e for e = 0..7.  Each is (code - zp) * scale
 // of group g_idx[k], or 0 where that group is out of range.  k0 < K, and K is
@@ -132,6 +98,46 @@ __device__ __forceinline__ void dequant_word(const GidxParams& p, const TileMeta
             v = ((float)code_at(d, e) - (float)z) * sc;
         }
         w[e] = v;
+    }
+}
+
+// The streaming kernel's per-tile table in LDS: entry G * 16 + i holds the
+// zero point and the scale of group G and column i as fp32 (x, y); entry
+// kb * 16 + i is (0, 0), the weight of a group out of range.
+__host__ __device__ inline int64_t table_bytes(int64_t kb) { return (kb + 1) * kTileN * 8; }
+
+template <typename ST, bool HAS_ZP>
+__device__ __forceinline__ void stage_table(const GidxParams& p, int64_t t, float2* tab, int tid, int nthreads)
+{
+    const TileMeta<ST> g = global_meta<ST>(p, t);
+    const int n = (p.kb + 1) * kTileN;
+    for (int v = tid; v < n; v += nthreads) {
+        const int G = v >> 4, i = v & 15;
+        float2 e = make_float2(0.0f, 0.0f);
+        if (G < p.kb) {
+            const int cg = G >> p.qshift, q = G & (p.Q - 1);
+            const int s = slot_of(i, q, p.Q);
+            uint32_t z = 8u;
+            if (HAS_ZP) z = (g.zp[cg * (kTileN / 2) * p.Q + (s >> 1)] >> (4 * (s & 1))) & 15u;
+            e = make_float2((float)z, to_f32(g.scales[cg * kTileN * p.Q + s]));
+        }
+        tab[v] = e;
+    }
+}
+
+// dequant_word through the table: the same weights, (code - zp) * scale,
+// and 0 for a group out of range ((code - 0) * 0).
+__device__ __forceinline__ void dequant_word_tab(const GidxParams& p, const float2* tab, int i, uint32_t d, int k0,
+                                                 float w[8])
+{
+    const int4 g0 = *reinterpret_cast<const int4*>(p.g_idx + k0);
+    const int4 g1 = *reinterpret_cast<const int4*>(p.g_idx + k0 + 4);
+    const int gs[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int G = (unsigned)gs[e] < (unsigned)p.kb ? gs[e] : p.kb;
+        const float2 zs = tab[G * kTileN + i];
+        w[e] = ((float)code_at(d, e) - zs.x) * zs.y;
     }
 }
 
@@ -173,33 +179,72 @@ __device__ __forceinline__ void store_out(const GidxParams& p, int m, int64_t n,
     }
 }
 
-template <typename AT, typename ST, bool HAS_ZP, bool LDS_META>
+// MF (2 <= M <= 16): the products on v_mfma_f32_16x16x4_f32, one per k
+// offset e of a word: lane (i, h) gives A row i at k = k0(h) + e and B
+// column i at the same k, so D[row][col] sums over the word's four k-octets.
+// The tail past K enters as zeros, so every lane issues the same MFMAs.
+template <typename AT, typename ST, bool HAS_ZP, bool TABLE, bool MF, int RB>
 __global__ __launch_bounds__(kSmallWaves * 64) void gidx_small_kernel(GidxParams p)
 {
-    __shared__ float red[kSmallWaves][kSmallM][kTileN];
+    static_assert(MF || RB == 1, "the fp32 fma form serves one block of rows");
+    __shared__ float red[kSmallWaves][16 * RB][kTileN];
     extern __shared__ __attribute__((aligned(16))) unsigned char meta_s[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int i = lane & 15, h = lane >> 4;
     const int64_t t = blockIdx.x;
-    TileMeta<ST> mt;
-    if constexpr (LDS_META) {
-        mt = stage_meta<ST, HAS_ZP>(p, t, meta_s, threadIdx.x, kSmallWaves * 64);
+    const int m0 = blockIdx.y * 16 * RB;   // first row of the workgroup
+    const float2* tab = reinterpret_cast<const float2*>(meta_s);
+    const TileMeta<ST> mt = global_meta<ST>(p, t);
+    if constexpr (TABLE) {
+        stage_table<ST, HAS_ZP>(p, t, reinterpret_cast<float2*>(meta_s), threadIdx.x, kSmallWaves * 64);
         __syncthreads();
-    } else {
-        mt = global_meta<ST>(p, t);
     }
     float acc[kSmallM];
 #pragma unroll
     for (int m = 0; m < kSmallM; ++m) acc[m] = 0.0f;
+    fx4_t dacc[RB];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) dacc[rb] = fx4_t{0.0f, 0.0f, 0.0f, 0.0f};
     for (int c = wave; c < p.C; c += kSmallWaves) {
         const uint4 d4 = p.codes[(t * p.C + c) * 64 + lane];
         const uint32_t ds[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int k0 = c * kChunkK + 32 * j + 8 * h;
+            if constexpr (MF) {
+                float w[8];
+                if (k0 < p.K) {
+                    if constexpr (TABLE)
+                        dequant_word_tab(p, tab, i, ds[j], k0, w);
+                    else
+                        dequant_word<ST, HAS_ZP>(p, mt, i, ds[j], k0, w);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) w[e] = 0.0f;
+                }
+                // the word's weights, reused for every block of 16 rows
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    const int row = m0 + 16 * rb + i;
+                    float x[8];
+                    if (k0 < p.K && row < p.M) {
+                        load_a8<AT>(p, row, k0, x);
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+                    }
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        dacc[rb] = __builtin_amdgcn_mfma_f32_16x16x4f32(x[e], w[e], dacc[rb], 0, 0, 0);
+                }
+                continue;
+            }
             if (k0 < p.K) {   // the chunk's tail beyond K holds no weights
                 float w[8];
-                dequant_word<ST, HAS_ZP>(p, mt, i, ds[j], k0, w);
+                if constexpr (TABLE)
+                    dequant_word_tab(p, tab, i, ds[j], k0, w);
+                else
+                    dequant_word<ST, HAS_ZP>(p, mt, i, ds[j], k0, w);
 #pragma unroll
                 for (int m = 0; m < kSmallM; ++m) {
                     if (m < p.M) {
@@ -212,116 +257,32 @@ __global__ __launch_bounds__(kSmallWaves * 64) void gidx_small_kernel(GidxParams
             }
         }
     }
-    // the 4 lanes of column i (h = 0..3), then the waves in order
+    if constexpr (MF) {
+        // D lane layout: rows 4h + r of each block, column i
 #pragma unroll
-    for (int m = 0; m < kSmallM; ++m) {
-        float v = acc[m];
-        v += __shfl_xor(v, 16);
-        v += __shfl_xor(v, 32);
-        if (h == 0) red[wave][m][i] = v;
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wave][16 * rb + 4 * h + r][i] = dacc[rb][r];
+    } else {
+        // the 4 lanes of column i (h = 0..3), then the waves in order
+#pragma unroll
+        for (int m = 0; m < kSmallM; ++m) {
+            float v = acc[m];
+            v += __shfl_xor(v, 16);
+            v += __shfl_xor(v, 32);
+            if (h == 0) red[wave][m][i] = v;
+        }
     }
     __syncthreads();
-    const int tid = threadIdx.x;
-    if (tid < kSmallM * kTileN) {
-        const int m = tid >> 4, col = tid & 15;
+    for (int o = threadIdx.x; o < 16 * RB * kTileN; o += kSmallWaves * 64) {
+        const int r = o >> 4, col = o & 15;
+        const int m = m0 + r;
         const int64_t n = t * kTileN + col;
         if (m < p.M && n < p.N) {
             float s = 0.0f;
 #pragma unroll
-            for (int w = 0; w < kSmallWaves; ++w) s += red[w][m][col];
+            for (int w = 0; w < kSmallWaves; ++w) s += red[w][r][col];
             store_out<AT>(p, m, n, s);
-        }
-    }
-}
-
-template <typename AT, typename ST, bool HAS_ZP, bool LDS_META>
-__global__ __launch_bounds__(256) void gidx_mfma_kernel(GidxParams p)
-{
-    extern __shared__ __attribute__((aligned(16))) unsigned char meta_s[];
-    __shared__ __attribute__((aligned(16))) float a_s[kBigRows][kChunkK + kAPad];    // A of the chunk, row-major
-    __shared__ __attribute__((aligned(16))) float w_s[kChunkK][kBigTiles * kTileN + kWPad];  // weights, k-major
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int i = lane & 15, h = lane >> 4;
-    const int64_t t0 = (int64_t)blockIdx.x * kBigTiles;
-    const int m0 = blockIdx.y * kBigRows;
-    // wave tt dequantizes tile t0 + tt; its metadata, in LDS when it fits
-    const int64_t tw = t0 + wave;
-    TileMeta<ST> mt;
-    if constexpr (LDS_META) {
-        const int64_t mb = meta_bytes(p.C, p.Q, (int)sizeof(ST), HAS_ZP);
-        for (int tt = 0; tt < kBigTiles; ++tt) {
-            if (t0 + tt < p.T) {
-                const TileMeta<ST> m = stage_meta<ST, HAS_ZP>(p, t0 + tt, meta_s + tt * mb, tid, 256);
-                if (tt == wave) mt = m;
-            }
-        }
-        __syncthreads();
-    } else {
-        mt = global_meta<ST>(p, tw < p.T ? tw : 0);
-    }
-    fx4_t acc[kBigTiles];
-#pragma unroll
-    for (int tt = 0; tt < kBigTiles; ++tt) acc[tt] = fx4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int c = 0; c < p.C; ++c) {
-        // A: 64 rows x 128 k, 8 consecutive k per load (zero beyond M and K)
-#pragma unroll
-        for (int v = tid; v < kBigRows * (kChunkK / 8); v += 256) {
-            const int r = v >> 4, k8 = (v & 15) * 8;
-            const int m = m0 + r, k0 = c * kChunkK + k8;
-            float x[8];
-            if (m < p.M && k0 < p.K) {
-                load_a8<AT>(p, m, k0, x);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = 0.0f;
-            }
-            *reinterpret_cast<fx4_t*>(&a_s[r][k8]) = fx4_t{x[0], x[1], x[2], x[3]};
-            *reinterpret_cast<fx4_t*>(&a_s[r][k8 + 4]) = fx4_t{x[4], x[5], x[6], x[7]};
-        }
-        // weights: wave tt dequantizes the lane records of tile t0 + tt
-        {
-            const int tt = wave;
-            const int64_t t = tw;
-            uint4 d4 = make_uint4(0u, 0u, 0u, 0u);
-            if (t < p.T) d4 = p.codes[(t * p.C + c) * 64 + lane];
-            const uint32_t ds[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int kin = 32 * j + 8 * h;
-                const int k0 = c * kChunkK + kin;
-                float w[8];
-                if (t < p.T && k0 < p.K) {
-                    dequant_word<ST, HAS_ZP>(p, mt, i, ds[j], k0, w);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) w[e] = 0.0f;
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) w_s[kin + e][tt * kTileN + i] = w[e];
-            }
-        }
-        __syncthreads();
-        // v_mfma_f32_16x16x4_f32: A lane (row i, k h), B lane (k h, column i)
-        const int r = wave * 16 + i;
-#pragma unroll 4
-        for (int kk = 0; kk < kChunkK; kk += 4) {
-            const float av = a_s[r][kk + h];
-#pragma unroll
-            for (int tt = 0; tt < kBigTiles; ++tt)
-                acc[tt] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, w_s[kk + h][tt * kTileN + i], acc[tt], 0, 0, 0);
-        }
-        __syncthreads();
-    }
-    // D lane layout: row 4h + e, column i
-#pragma unroll
-    for (int tt = 0; tt < kBigTiles; ++tt) {
-        const int64_t n = (t0 + tt) * kTileN + i;
-        if (n >= p.N) continue;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int m = m0 + wave * 16 + 4 * h + e;
-            if (m < p.M) store_out<AT>(p, m, n, acc[tt][e]);
         }
     }
 }
@@ -329,19 +290,26 @@ __global__ __launch_bounds__(256) void gidx_mfma_kernel(GidxParams p)
 template <typename AT, typename ST, bool HAS_ZP>
 hipError_t launch_z(const Layout& L, const GidxParams& p, hipStream_t s)
 {
-    const int64_t mb = meta_bytes(L.C, L.Q, L.ss, HAS_ZP);
     if (p.M <= kSmallM) {
         const dim3 grid((unsigned)L.T), block(kSmallWaves * 64);
-        if (mb <= kSmallMetaLds)
-            gidx_small_kernel<AT, ST, HAS_ZP, true><<<grid, block, (size_t)mb, s>>>(p);
+        const int64_t tb = table_bytes(L.kb);
+        const bool table = tb <= kSmallMetaLds, mf = p.M > 1;
+        if (table && mf)
+            gidx_small_kernel<AT, ST, HAS_ZP, true, true, 1><<<grid, block, (size_t)tb, s>>>(p);
+        else if (table)
+            gidx_small_kernel<AT, ST, HAS_ZP, true, false, 1><<<grid, block, (size_t)tb, s>>>(p);
+        else if (mf)
+            gidx_small_kernel<AT, ST, HAS_ZP, false, true, 1><<<grid, block, 0, s>>>(p);
         else
-            gidx_small_kernel<AT, ST, HAS_ZP, false><<<grid, block, 0, s>>>(p);
+            gidx_small_kernel<AT, ST, HAS_ZP, false, false, 1><<<grid, block, 0, s>>>(p);
     } else {
-        const dim3 grid((unsigned)((L.T + kBigTiles - 1) / kBigTiles), (unsigned)((p.M + kBigRows - 1) / kBigRows));
-        if (kBigTiles * mb <= kBigMetaLds)
-            gidx_mfma_kernel<AT, ST, HAS_ZP, true><<<grid, dim3(256), (size_t)(kBigTiles * mb), s>>>(p);
+        // 64 rows per workgroup, the weights dequantized once for all of them
+        const dim3 grid((unsigned)L.T, (unsigned)((p.M + kBigRows - 1) / kBigRows)), block(kSmallWaves * 64);
+        const int64_t tb = table_bytes(L.kb);
+        if (tb <= kBigTableLds)
+            gidx_small_kernel<AT, ST, HAS_ZP, true, true, kBigRows / 16><<<grid, block, (size_t)tb, s>>>(p);
         else
-            gidx_mfma_kernel<AT, ST, HAS_ZP, false><<<grid, dim3(256), 0, s>>>(p);
+            gidx_small_kernel<AT, ST, HAS_ZP, false, true, kBigRows / 16><<<grid, block, 0, s>>>(p);
     }
     return hipGetLastError();
 }
@@ -378,9 +346,7 @@ hipError_t launch_gemm_gidx(const Layout& L, const WeightView& w, const void* a,
     p.qshift = __builtin_ctz((unsigned)L.Q);
     p.kb = (int)L.kb;
     p.T = L.T;
-    if (variant)
-        *variant = m <= kSmallM ? (f16_act ? "gemm_gidx_stream_f16" : "gemm_gidx_stream_f32")
-                                : (f16_act ? "gemm_gidx_mfma_f16" : "gemm_gidx_mfma_f32");
+    if (variant) *variant = f16_act ? "gemm_gidx_stream_f16" : "gemm_gidx_stream_f32";
     if (f16_act)
         return L.ss == 2 ? launch_s<__half, __half>(L, p, stream) : launch_s<__half, float>(L, p, stream);
     return L.ss == 2 ? launch_s<float, __half>(L, p, stream) : launch_s<float, float>(L, p, stream);

@@ -292,10 +292,11 @@ mnb_status mnb_gemm_act_order(const mnb_weight_desc* w, const void* repacked, co
  *    A (device, [M,K], 16-byte aligned) and Y (device, [M,N], element-
  *    aligned) of a_dtype; bias, bias_row_stride and bias_mode as for
  *    mnb_gemm_bias (bias NULL for none).  Any M >= 1 up to 65535*64 (else
- *    MNB_ERR_UNSUPPORTED), no workspace, K below 2^31 - 128.  M <= 16
- *    streams the weight (fp32 vector products); larger M stages the
- *    dequantized 64-column block and 64 rows of A in LDS for fp32 matrix-core
- *    products (v_mfma_f32_16x16x4_f32).  Deterministic. */
+ *    MNB_ERR_UNSUPPORTED), no workspace, K below 2^31 - 128.  The weight is
+ *    streamed once per block of up to 16 rows (M <= 16) or 64 rows, each
+ *    weight dequantized in registers from a per-tile table of (zero point,
+ *    scale) pairs; products by fp32 fma at M = 1, else on the fp32 matrix
+ *    cores (v_mfma_f32_16x16x4_f32).  Deterministic. */
 mnb_status mnb_gemm_group_indices(const mnb_weight_desc* w, const void* repacked, const void* a, int64_t m,
                                   int32_t a_dtype, const int32_t* g_idx, const void* bias,
                                   int64_t bias_row_stride, int32_t bias_mode, void* y, void* stream);

@@ -620,12 +620,16 @@ GIDX_CASES = [
     (17, 48, 512, 32, "f16", "f16", True, "whole"),     # whole groups: the sorted route's input
     (3, 40, 640, 64, "f32", "f16", True, "range"),      # values outside 0..k_blocks-1 weigh 0
     (16, 33, 512, 32, "f16", "f16", True, "random"),    # the largest M of the streaming kernel
+    (6, 60, 400, 16, "f16", "f16", True, "skewed"),     # its matrix-core products over a K tail
     (17, 200, 1024, 16, "f32", "f32", True, "random"),  # the smallest of the matrix-core kernel
     (300, 130, 768, 128, "f16", "f16", False, "range"),
-    # metadata too large for LDS (2048 groups of fp32 scales and zero points;
-    # 512 groups for the four tiles of the matrix-core kernel): read from L2
+    # a table of 688 groups (88 KiB of LDS); metadata too large for LDS (2048
+    # groups; 512 groups of fp32 scales and zero points for the four tiles of
+    # the matrix-core kernel): read from L2
+    (1, 40, 11008, 16, "f16", "f32", True, "random"),
     (2, 40, 32768, 16, "f16", "f32", True, "random"),
     (70, 48, 8192, 16, "f32", "f32", True, "random"),
+    (20, 40, 11008, 16, "f32", "f16", True, "random"),   # 64-row blocks, table too large (88 KiB)
 ]
 
 
@@ -668,7 +672,7 @@ def test_group_indices_parity(mnb, M, N, K, g, adt, sdt, zp, kind):
     ndt = np.float16 if adt == "f16" else np.float32
     y = t.empty((M, N), dtype=odt, device="cuda")
     mnb.mnb_gemm_group_indices(q.desc, q.repacked, a, M, gi, y)
-    assert mnb.mnb_last_variant() == "gemm_gidx_%s_%s" % ("stream" if M <= 16 else "mfma", adt)
+    assert mnb.mnb_last_variant() == "gemm_gidx_stream_" + adt
     y2 = t.empty_like(y)
     mnb.mnb_gemm_group_indices(q.desc, q.repacked, a, M, gi, y2)
     W = o.dequant_gidx(w.packed, w.scales, w.zero_points, g_idx, N, K, g)
