@@ -41,7 +41,7 @@ constexpr int kSmallWaves = 16;
 // LDS for the table of (zero point, scale) pairs, 128 bytes per group (else
 // the pairs are read from L2): 1024 threads keep one workgroup per CU
 // anyway; beside the 64 KiB reduction array of 64 rows, less.
-constexpr int64_t kSmallMetaLds = 96 * 1024;
+constexpr int64_t kSmallTableLds = 96 * 1024;
 constexpr int64_t kBigTableLds = 80 * 1024;
 
 struct GidxParams {
@@ -179,12 +179,13 @@ __device__ __forceinline__ void store_out(const GidxParams& p, int m, int64_t n,
     }
 }
 
-// MF (2 <= M <= 16): the products on v_mfma_f32_16x16x4_f32, one per k
-// offset e of a word: lane (i, h) gives A row i at k = k0(h) + e and B
-// column i at the same k, so D[row][col] sums over the word's four k-octets.
-// The tail past K enters as zeros, so every lane issues the same MFMAs.
+// RB blocks of 16 rows from row blockIdx.y * 16 * RB.  MF (M >= 2): the
+// products on v_mfma_f32_16x16x4_f32, one per k offset e of a word: lane
+// (i, h) gives A row i at k = k0(h) + e and B column i at the same k, so
+// D[row][col] sums over the word's four k-octets.  The tail past K enters as
+// zeros, so every lane issues the same MFMAs.  Otherwise (M = 1) fp32 fma.
 template <typename AT, typename ST, bool HAS_ZP, bool TABLE, bool MF, int RB>
-__global__ __launch_bounds__(kSmallWaves * 64) void gidx_small_kernel(GidxParams p)
+__global__ __launch_bounds__(kSmallWaves * 64) void gidx_stream_kernel(GidxParams p)
 {
     static_assert(MF || RB == 1, "the fp32 fma form serves one block of rows");
     __shared__ float red[kSmallWaves][16 * RB][kTileN];
@@ -293,23 +294,23 @@ hipError_t launch_z(const Layout& L, const GidxParams& p, hipStream_t s)
     if (p.M <= kSmallM) {
         const dim3 grid((unsigned)L.T), block(kSmallWaves * 64);
         const int64_t tb = table_bytes(L.kb);
-        const bool table = tb <= kSmallMetaLds, mf = p.M > 1;
+        const bool table = tb <= kSmallTableLds, mf = p.M > 1;
         if (table && mf)
-            gidx_small_kernel<AT, ST, HAS_ZP, true, true, 1><<<grid, block, (size_t)tb, s>>>(p);
+            gidx_stream_kernel<AT, ST, HAS_ZP, true, true, 1><<<grid, block, (size_t)tb, s>>>(p);
         else if (table)
-            gidx_small_kernel<AT, ST, HAS_ZP, true, false, 1><<<grid, block, (size_t)tb, s>>>(p);
+            gidx_stream_kernel<AT, ST, HAS_ZP, true, false, 1><<<grid, block, (size_t)tb, s>>>(p);
         else if (mf)
-            gidx_small_kernel<AT, ST, HAS_ZP, false, true, 1><<<grid, block, 0, s>>>(p);
+            gidx_stream_kernel<AT, ST, HAS_ZP, false, true, 1><<<grid, block, 0, s>>>(p);
         else
-            gidx_small_kernel<AT, ST, HAS_ZP, false, false, 1><<<grid, block, 0, s>>>(p);
+            gidx_stream_kernel<AT, ST, HAS_ZP, false, false, 1><<<grid, block, 0, s>>>(p);
     } else {
         // 64 rows per workgroup, the weights dequantized once for all of them
         const dim3 grid((unsigned)L.T, (unsigned)((p.M + kBigRows - 1) / kBigRows)), block(kSmallWaves * 64);
         const int64_t tb = table_bytes(L.kb);
         if (tb <= kBigTableLds)
-            gidx_small_kernel<AT, ST, HAS_ZP, true, true, kBigRows / 16><<<grid, block, (size_t)tb, s>>>(p);
+            gidx_stream_kernel<AT, ST, HAS_ZP, true, true, kBigRows / 16><<<grid, block, (size_t)tb, s>>>(p);
         else
-            gidx_small_kernel<AT, ST, HAS_ZP, false, true, kBigRows / 16><<<grid, block, 0, s>>>(p);
+            gidx_stream_kernel<AT, ST, HAS_ZP, false, true, kBigRows / 16><<<grid, block, 0, s>>>(p);
     }
     return hipGetLastError();
 }
