@@ -73,105 +73,222 @@ __device__ __forceinline__ h8_t zero_h8()
     return z;
 }
 
-// TPW tiles per workgroup; Q groups per chunk.
-template <typename ST, int Q, bool HAS_ZP, int TPW>
+// A lane's scales of one tile and chunk as one integer (NS consecutive
+// scales), so the load stays a single instruction.
+template <typename ST, int NS> struct RawScales;
+template <> struct RawScales<__half, 1> { typedef uint16_t type; };
+template <> struct RawScales<__half, 2> { typedef uint32_t type; };
+template <> struct RawScales<__half, 4> { typedef uint64_t type; };
+template <> struct RawScales<float, 1> { typedef uint32_t type; };
+template <> struct RawScales<float, 2> { typedef uint64_t type; };
+template <> struct RawScales<float, 4> { typedef u4_t type; };
+
+template <typename T> __device__ __forceinline__ T buf_load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff);
+template <> __device__ __forceinline__ uint16_t buf_load<uint16_t>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+template <> __device__ __forceinline__ uint32_t buf_load<uint32_t>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+template <> __device__ __forceinline__ uint64_t buf_load<uint64_t>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
+template <> __device__ __forceinline__ u4_t buf_load<u4_t>(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+template <typename ST, int NS>
+__device__ __forceinline__ float raw_scale(const typename RawScales<ST, NS>::type& r, int s)
+{
+    if constexpr (sizeof(ST) == 2) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(r >> (16 * s)));
+    } else if constexpr (NS == 4) {
+        const uint32_t e = r[s];
+        return __builtin_bit_cast(float, e);
+    } else {
+        return __builtin_bit_cast(float, (uint32_t)(r >> (32 * s)));
+    }
+}
+
+// Both constants of zero point z for unpack_zr in one register: the low half
+// is -(1024 + z), the high half -(64 + z) (fp16 64 + z has z in mantissa bits
+// 4..7).  z <= 15, so the halves form without carries.
+__device__ __forceinline__ uint32_t zp_pair(uint32_t z) { return __umul24(z, 0x100001u) + 0xD400E400u; }
+
+// unpack8 with both constants of the zero point in one register: each
+// packed add or fma takes its constant from one half of zr for both lanes.
+__device__ __forceinline__ void unpack_zr(uint32_t d, uint32_t zr, h2_t out[4])
+{
+    const uint32_t lo = 0x000F000Fu, hi = 0x00F000F0u, magic = 0x64006400u;
+    const h2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const h2_t r = as_h2(zr);
+    const h2_t c_lo = {r[0], r[0]}, c_hi = {r[1], r[1]};
+    const uint32_t d8 = d >> 8;
+    out[0] = as_h2(__builtin_amdgcn_bitop3_b32(d, lo, magic, 0xEA)) + c_lo;
+    out[1] = as_h2(__builtin_amdgcn_bitop3_b32(d, hi, magic, 0xEA)) * sixteenth + c_hi;
+    out[2] = as_h2(__builtin_amdgcn_bitop3_b32(d8, lo, magic, 0xEA)) + c_lo;
+    out[3] = as_h2(__builtin_amdgcn_bitop3_b32(d8, hi, magic, 0xEA)) * sixteenth + c_hi;
+}
+
+// Chunks per wave requested together: every load of a batch is in flight
+// before the first compute, so a wave pays one memory round trip per batch,
+// not one per chunk.  Two where the batch's registers fit the 128 a 16-wave
+// workgroup allows (fp16 scales, groups of 32 k or more), else one.
+template <typename ST, int Q> constexpr int batch_of() { return sizeof(ST) == 2 && Q <= 4 ? 2 : 1; }
+
+// TPW tiles per workgroup; Q groups per chunk.  KTAIL: K is not a multiple
+// of 128, so the activation loads of the last chunk are masked per k.
+//
+// Every load is a buffer load: the workgroup's tiles and the activation are
+// buffer ranges, a lane's part of each offset is fixed, and the chunk's part
+// is wave-uniform (a scalar offset), so addressing costs no vector
+// instructions.  Activation rows >= M read zero through the range check.
+template <typename ST, int Q, bool HAS_ZP, int TPW, bool KTAIL>
 __global__ __launch_bounds__(kWaves * 64) void gemm_small_kernel(SmallParams p)
 {
     __shared__ float red[kWaves][TPW][256];
+    constexpr int kBatch = batch_of<ST, Q>();
+    constexpr int NS = Q <= 4 ? Q : 4;           // scales per load (two loads for groups of 16)
+    constexpr int NL = Q <= 4 ? 1 : 2;
+    constexpr int SREC = kTileN * Q * (int)sizeof(ST), ZREC = kTileN / 2 * Q;
+    constexpr uint32_t kFar = 0x80000000u;       // past every range: reads zero
+    typedef typename RawScales<ST, NS>::type RawS;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = uniform(tid >> 6);
     const int i = lane & 15;      // column in tile (B and D), row of A
     const int h = lane >> 4;      // k-octet (A and B), row quad of D
     const int64_t t0 = (int64_t)blockIdx.x * TPW;
     const int C = p.C;
     const int K = p.K;
+    const int tiles_here = (int)((p.T - t0) < TPW ? (p.T - t0) : TPW);
+
+    const __amdgpu_buffer_rsrc_t c_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(p.codes + t0 * C * 64), (short)0, tiles_here * C * kChunkBytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(static_cast<const uint8_t*>(p.scales) + t0 * C * SREC), (short)0, tiles_here * C * SREC, 0x00020000);
+    const __amdgpu_buffer_rsrc_t z_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(HAS_ZP ? p.zp + t0 * C * ZREC : reinterpret_cast<const uint8_t*>(p.codes)), (short)0,
+        HAS_ZP ? tiles_here * C * ZREC : 0, 0x00020000);
+    const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)p.a, (short)0, p.M * K * 2, 0x00020000);
+
+    // lane parts of the offsets
+    const uint32_t a_voff = i < p.M ? ((uint32_t)i * (uint32_t)K + 8u * (uint32_t)h) * 2u : kFar;
+    const uint32_t s_voff = (uint32_t)(Q <= 4 ? i * Q : i * 4) * (uint32_t)sizeof(ST);
+    const uint32_t z_voff = Q == 1 ? (uint32_t)(i >> 1) : (Q == 2 ? (uint32_t)i : (Q == 4 ? 2u * i : 2u * ((h >> 1) * 16 + i)));
 
     f4_t total[TPW];
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) total[tt] = f4_t{0.f, 0.f, 0.f, 0.f};
 
-    const bool row_ok = i < p.M;
-    const _Float16* arow = p.a + (int64_t)(row_ok ? i : 0) * K;
-
-    for (int c = wave; c < C; c += kWaves) {
-        // loads: code words of every tile, A fragments of the 4 k-steps,
-        // scales and zero points
-        u4_t d[TPW];
-        uint32_t zw[TPW];
-        float s[TPW][Q <= 4 ? Q : 8];
+    for (int cb = wave; cb < C; cb += kWaves * kBatch) {
+        // Issue order: the A fragments of the batch, then its scales and
+        // zero points, then its code words.  Waits count completions in
+        // issue order, so the small loads never wait behind the code stream.
+        // A chunk past K loads the last chunk's weights again and is not
+        // computed.
+        h8_t afr[kBatch][4];
 #pragma unroll
-        for (int tt = 0; tt < TPW; ++tt) {
-            const int64_t t = t0 + tt;
-            const int64_t chunk = (t < p.T ? t : p.T - 1) * C + c;
-            d[tt] = __builtin_nontemporal_load(p.codes + chunk * 64 + lane);
-            const ST* sp = static_cast<const ST*>(p.scales) + chunk * kTileN * Q;
-            if (Q <= 4) {
-#pragma unroll
-                for (int q = 0; q < Q; ++q) s[tt][q] = to_f32(sp[i * Q + q]);
-            } else {
-#pragma unroll
-                for (int q = 0; q < 8; ++q) s[tt][q] = to_f32(sp[slot_of(i, q, 8)]);
-            }
-            zw[tt] = 0;
-            if (HAS_ZP) {
-                const uint8_t* zp = p.zp + chunk * (kTileN / 2) * Q;
-                if (Q == 1) {
-                    zw[tt] = (zp[i >> 1] >> (4 * (i & 1))) & 15u;
-                } else if (Q == 2) {
-                    zw[tt] = zp[i];
-                } else {
-                    const int sb = Q == 4 ? i * 4 : ((h >> 1) * 16 + i) * 4;
-                    zw[tt] = *reinterpret_cast<const uint16_t*>(zp + sb / 2);
-                }
-            }
-        }
-        h8_t afr[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int k = c * kChunkK + 32 * j + 8 * h;
-            if (row_ok && k < K)
-                afr[j] = *reinterpret_cast<const h8_t*>(arow + k);
-            else
-                afr[j] = zero_h8();
-        }
-
-#pragma unroll
-        for (int tt = 0; tt < TPW; ++tt) {
-            const uint32_t dw[4] = {d[tt].x, d[tt].y, d[tt].z, d[tt].w};
-            f4_t grp = f4_t{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < kBatch; ++u)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                // zero point of this lane's k-octet
-                const int zs = Q == 1 ? 0 : (Q == 2 ? (j >> 1) : j);
-                const uint32_t z = HAS_ZP ? (zw[tt] >> (4 * zs)) & 15u : 8u;
-                h2_t q[4];
-                unpack8(dw[j], zp_const(z), q);
-                const h8_t b = make_b(q);
-                if (Q <= 4) {
-                    grp = mfma16(afr[j], b, grp);
-                    // last k-step of a group: scale and fold into the total
-                    constexpr int steps = 4 / (Q <= 4 ? Q : 1);
-                    if ((j + 1) % steps == 0) {
-                        const float sc = s[tt][Q == 1 ? 0 : (Q == 2 ? (j >> 1) : j)];
+                const int k0 = (cb + kWaves * u) * kChunkK + 32 * j;   // wave-uniform
+                uint32_t vo = a_voff;
+                if (KTAIL && k0 + 8 * h >= K) vo = kFar;
+                afr[u][j] = __builtin_bit_cast(h8_t, buf_load<u4_t>(a_rsrc, vo, (uint32_t)k0 * 2u));
+            }
+        __builtin_amdgcn_sched_barrier(0);
+        RawS sr[kBatch][TPW][NL];
+        uint32_t zw[kBatch][TPW];
+        uint32_t rec[kBatch][TPW];
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) total[tt][r] = __builtin_fmaf(grp[r], sc, total[tt][r]);
-                        grp = f4_t{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt) {
+                const int c = cb + kWaves * u;
+                // a tile past N reads zero (outside the range); its outputs are not stored
+                rec[u][tt] = (uint32_t)(tt * C + (c < C ? c : C - 1));
+                sr[u][tt][0] = buf_load<RawS>(s_rsrc, s_voff, rec[u][tt] * SREC);
+                // groups of 16: the even groups of the 16 columns, then the odd ones
+                if (NL > 1) sr[u][tt][NL - 1] = buf_load<RawS>(s_rsrc, s_voff + 16 * sizeof(RawS), rec[u][tt] * SREC);
+                zw[u][tt] = 0;
+                if (HAS_ZP) {
+                    if (Q <= 2)
+                        zw[u][tt] = __builtin_amdgcn_raw_buffer_load_b8(z_rsrc, z_voff, rec[u][tt] * ZREC, 0);
+                    else
+                        zw[u][tt] = buf_load<uint16_t>(z_rsrc, z_voff, rec[u][tt] * ZREC);
+                }
+            }
+        __builtin_amdgcn_sched_barrier(0);
+        u4_t d[kBatch][TPW];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt)
+                d[u][tt] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                    c_rsrc, (uint32_t)lane * 16u, rec[u][tt] * kChunkBytes, 2));
+        __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            if (cb + kWaves * u >= C) continue;   // wave-uniform
+#pragma unroll
+            for (int tt = 0; tt < TPW; ++tt) {
+                const uint32_t dw[4] = {d[u][tt].x, d[u][tt].y, d[u][tt].z, d[u][tt].w};
+                // zero point of group q of the lane's column (or of its octet
+                // half's group q for groups of 16)
+                auto zr_of = [&](int q) {
+                    uint32_t z = 8u;
+                    if (HAS_ZP) z = Q == 1 ? (zw[u][tt] >> (4 * (i & 1))) & 15u : (zw[u][tt] >> (4 * q)) & 15u;
+                    return zp_pair(z);
+                };
+                if constexpr (Q <= 4) {
+                    // one independent chain per group, then the scales in
+                    // group order
+                    constexpr int steps = 4 / Q;   // k-steps per group
+                    f4_t grp[Q];
+                    uint32_t zr[Q];
+#pragma unroll
+                    for (int gq = 0; gq < Q; ++gq) zr[gq] = zr_of(gq);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        h2_t q[4];
+                        unpack_zr(dw[j], zr[j / steps], q);
+                        grp[j / steps] = mfma16(afr[u][j], make_b(q),
+                                                (j % steps == 0) ? f4_t{0.f, 0.f, 0.f, 0.f} : grp[j / steps]);
+                    }
+#pragma unroll
+                    for (int gq = 0; gq < Q; ++gq) {
+                        const float sc = raw_scale<ST, NS>(sr[u][tt][0], gq);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) total[tt][r] = __builtin_fmaf(grp[gq][r], sc, total[tt][r]);
                     }
                 } else {
-                    // group 16: a 32-k step spans groups 2j (octets 0,1) and
-                    // 2j+1 (octets 2,3); one MFMA per group with the other
-                    // group's octets zeroed
-                    const h8_t zero = zero_h8();
-                    const h8_t be = (h < 2) ? b : zero;
-                    const h8_t bo = (h < 2) ? zero : b;
-                    const f4_t ge = mfma16(afr[j], be, f4_t{0.f, 0.f, 0.f, 0.f});
-                    const f4_t go = mfma16(afr[j], bo, f4_t{0.f, 0.f, 0.f, 0.f});
-                    const float se = s[tt][2 * j], so = s[tt][2 * j + 1];
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        total[tt][r] = __builtin_fmaf(ge[r], se, total[tt][r]);
-                        total[tt][r] = __builtin_fmaf(go[r], so, total[tt][r]);
+                    for (int j = 0; j < 4; ++j) {
+                        h2_t q[4];
+                        unpack_zr(dw[j], zr_of(j), q);
+                        const h8_t b = make_b(q);
+                        // group 16: a 32-k step spans groups 2j (octets 0,1) and
+                        // 2j+1 (octets 2,3); one MFMA per group with the other
+                        // group's octets zeroed
+                        const h8_t zero = zero_h8();
+                        const h8_t be = (h < 2) ? b : zero;
+                        const h8_t bo = (h < 2) ? zero : b;
+                        const f4_t ge = mfma16(afr[u][j], be, f4_t{0.f, 0.f, 0.f, 0.f});
+                        const f4_t go = mfma16(afr[u][j], bo, f4_t{0.f, 0.f, 0.f, 0.f});
+                        const float se = raw_scale<ST, NS>(sr[u][tt][0], j);
+                        const float so = raw_scale<ST, NS>(sr[u][tt][NL - 1], j);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            total[tt][r] = __builtin_fmaf(ge[r], se, total[tt][r]);
+                            total[tt][r] = __builtin_fmaf(go[r], so, total[tt][r]);
+                        }
                     }
                 }
             }
@@ -226,7 +343,10 @@ template <typename ST, int Q, bool HAS_ZP, int TPW>
 hipError_t launch_t(const SmallParams& p, hipStream_t s)
 {
     const int64_t blocks = (p.T + TPW - 1) / TPW;
-    gemm_small_kernel<ST, Q, HAS_ZP, TPW><<<dim3((unsigned)blocks), dim3(kWaves * 64), 0, s>>>(p);
+    if (p.K % kChunkK != 0)
+        gemm_small_kernel<ST, Q, HAS_ZP, TPW, true><<<dim3((unsigned)blocks), dim3(kWaves * 64), 0, s>>>(p);
+    else
+        gemm_small_kernel<ST, Q, HAS_ZP, TPW, false><<<dim3((unsigned)blocks), dim3(kWaves * 64), 0, s>>>(p);
     return hipGetLastError();
 }
 
@@ -242,6 +362,11 @@ hipError_t launch_q(const Layout& L, const SmallParams& p, hipStream_t s)
 }
 
 }  // namespace
+
+// Largest K the kernel's 32-bit buffer ranges cover: the code bytes of a
+// workgroup's 4 tiles (4 * K / 128 * 1024 = 32 K) and 16 rows of fp16
+// activations (32 K) stay below 2^31 for K <= 2^25.
+int64_t gemm_small_max_k() { return int64_t(1) << 25; }
 
 size_t gemm_small_workspace(const Layout&, int64_t) { return 0; }
 

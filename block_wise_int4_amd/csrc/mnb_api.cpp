@@ -306,6 +306,9 @@ size_t mnb_gemm_workspace_bytes_for(const mnb_weight_desc* w, int64_t m, int32_t
 // M > 16 runs the prefill GEMM, whose buffer offsets are 32-bit.
 static mnb_status check_gemm_k(const Layout& L, int64_t m)
 {
+    if (m >= 2 && m <= 16 && L.K > mnb::gemm_small_max_k())
+        return fail(MNB_ERR_UNSUPPORTED, "K=%lld exceeds the small-M GEMM limit %lld (2 <= M <= 16)",
+                    (long long)L.K, (long long)mnb::gemm_small_max_k());
     if (m > 16 && L.K > mnb::gemm_mfma_max_k())
         return fail(MNB_ERR_UNSUPPORTED, "K=%lld exceeds the prefill GEMM limit %lld (M > 16)", (long long)L.K,
                     (long long)mnb::gemm_mfma_max_k());

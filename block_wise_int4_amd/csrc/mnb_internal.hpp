@@ -52,7 +52,8 @@ hipError_t launch_gemv(const Layout& L, const WeightView& gate, const WeightView
                        const void* a, const int32_t* perm, bool f16_act, const Bias& bias, void* y,
                        hipStream_t stream, const char** variant);
 
-// 2 <= M <= 16, fp16 activations.
+// 2 <= M <= 16, fp16 activations, K up to gemm_small_max_k().
+int64_t gemm_small_max_k();
 size_t gemm_small_workspace(const Layout& L, int64_t m);
 hipError_t launch_gemm_small(const Layout& L, const WeightView& w, const void* a, int64_t m,
                              const Bias& bias, void* y, void* ws, hipStream_t stream, const char** variant);

@@ -174,8 +174,7 @@ def test_prefill_k_limit():
     """M > 16 runs the prefill GEMM, whose buffer offsets are 32-bit: K up to
     11184810 (96 rows of A below 2^31 bytes) is accepted (without a device
     the call then stops at the device check), one group more is refused
-    before anything is enqueued, by every entry point that reaches it; the
-    small-M kernel has no such limit."""
+    before anything is enqueued, by every entry point that reaches it."""
     lib = mnb.lib
     U, DEV = mnb.MNB_ERR_UNSUPPORTED, mnb.MNB_ERR_DEVICE
     k_ok = 11184810 // 128 * 128
@@ -189,6 +188,25 @@ def test_prefill_k_limit():
                                            FAKE, 1 << 40, None)
     over32 = mnb.desc(16, k_ok + 128, 128, False, mnb.MNB_F32)
     assert "prefill GEMM limit" in _expect(U, lib.mnb_gemm_accuracy4, D(over32), FAKE, FAKE, 17, None, FAKE,
+                                           FAKE, 1 << 40, None)
+
+
+def test_small_m_k_limit():
+    """2 <= M <= 16 runs the small-M kernel, whose buffer ranges are 32-bit:
+    K up to 2^25 is accepted (without a device the call then stops at the
+    device check), one group more is refused before anything is enqueued, also
+    for fp32 activations (2M fp16 rows) and int8 activations."""
+    lib = mnb.lib
+    U, DEV = mnb.MNB_ERR_UNSUPPORTED, mnb.MNB_ERR_DEVICE
+    k_ok = 1 << 25
+    ok, over = mnb.desc(16, k_ok, 128, False, mnb.MNB_F16), mnb.desc(16, k_ok + 128, 128, False, mnb.MNB_F16)
+    for m in (2, 16):
+        assert lib.mnb_gemm(D(ok), FAKE, FAKE, m, 1, FAKE, None, 0, None) == DEV
+        assert "small-M GEMM limit" in _expect(U, lib.mnb_gemm, D(over), FAKE, FAKE, m, 1, FAKE, None, 0, None)
+    assert "small-M GEMM limit" in _expect(U, lib.mnb_gemm, D(over), FAKE, FAKE, 8, mnb.MNB_F32, FAKE, FAKE,
+                                           1 << 40, None)
+    over32 = mnb.desc(16, k_ok + 128, 128, False, mnb.MNB_F32)
+    assert "small-M GEMM limit" in _expect(U, lib.mnb_gemm_accuracy4, D(over32), FAKE, FAKE, 4, None, FAKE,
                                            FAKE, 1 << 40, None)
 
 

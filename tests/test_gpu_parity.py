@@ -487,6 +487,37 @@ def test_prefill_at_maximum_k(mnb):
     G.assert_within(yh[np.array(rows)[ms], ns], Y, B, "prefill at K=%d" % K)
 
 
+def test_small_m_at_maximum_k(mnb):
+    """The small-M kernel at its largest K (2^25 = 262144 chunks): 16 rows of
+    fp16 A are 2^30 bytes, so the activation offsets reach 2^30.  One
+    workgroup (N = 16) runs every chunk.  Rows are sparse (_sparse_row); rows
+    0, 1, 7 and 15 are checked against the oracle on every column."""
+    t = G.torch()
+    M, N, g = 16, 16, 128
+    K = 1 << 25
+    w = _weight(N, K, g, "f16", True, seed=22, lo=0.002, hi=0.01)
+    q = G.upload(w)
+    a = t.empty((M, K), dtype=t.float16, device="cuda")
+    rows = [0, 1, 7, 15]
+    kept = {}
+    for m in range(M):
+        r = _sparse_row(K, (220, m))
+        a[m].copy_(t.from_numpy(r))
+        if m in rows:
+            kept[m] = r
+    y = t.empty((M, N), dtype=t.float16, device="cuda")
+    G.gemm(q, a, M, y)
+    assert mnb.mnb_last_variant() == "gemm_small_m"
+    yh = G.host(y)
+    del a
+    t.cuda.empty_cache()
+    A = np.stack([kept[m] for m in rows])
+    ms = np.repeat(np.arange(len(rows)), N)
+    ns = np.tile(np.arange(N), len(rows))
+    Y, B = o.matmul_nbits_at(A, w.packed, w.scales, w.zero_points, N, K, g, ms, ns)
+    G.assert_within(yh[np.array(rows)[ms], ns], Y, B, "small M at K=%d" % K)
+
+
 BIAS_CASES = [
     # M, N, K, g, activation dtype, zp: every path (GEMV fp16/fp32, small M, prefill)
     (1, 300, 512, 32, "f16", True), (1, 200, 640, 64, "f32", False),
