@@ -303,7 +303,7 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
             // A rows [ROWS_PER_WAVE*wave + 4*idx, +4); a chunk reaching past K
             // (K not a multiple of 128) sends its lanes past K out of range
             uint32_t voff = a_voff[idx];
-            if (KTAIL && (c + 1) * kChunkK > K) {
+            if (KTAIL) {
                 const int r = ROWS_PER_WAVE * wave + 4 * idx + (lane >> 4);
                 if (c * kChunkK + 8 * ((lane & 15) ^ (r & 15)) >= K) voff = kFar;
             }
@@ -359,7 +359,7 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
     // points of the lane's columns, for the current and the next chunk
     float ratioA[PAIRS][Q], ratioB[PAIRS][Q];
     uint32_t zcA[PAIRS][Q], zcB[PAIRS][Q];
-    auto read_meta = [&](int st, float (&rt)[PAIRS][Q], uint32_t (&z)[PAIRS][Q]) {
+    auto read_meta = [&](int st, float (&rt)[PAIRS][Q], uint32_t (&z)[PAIRS][Q], bool live) {
         const unsigned char* Ms = stage_m(st);
 #pragma unroll
         for (int q = 0; q < PAIRS; ++q) {
@@ -377,7 +377,7 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
                     rt[q][g] = sg != 0.f ? __fdiv_rn(unit[q], sg) : 1.f;
                 else
                     rt[q][g] = sg != 0.f ? unit[q] * __builtin_amdgcn_rcpf(sg) : 1.f;
-                unit[q] = sg != 0.f ? sg : unit[q];
+                unit[q] = (live && sg != 0.f) ? sg : unit[q];
                 uint32_t zv = 8u;
                 if (HAS_ZP) {
                     const unsigned char* zrec = Ms + (G::kZpOffDw + tt * G::kZpDw) * 4;
@@ -511,17 +511,19 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
     };
 
     // ---- prologue: chunks 0 .. NST-2 in flight, chunk 0 read in ----
-    const int npre = C < NST - 1 ? C : NST - 1;
+    // Every chunk's loads and DMAs are issued whether or not the chunk
+    // exists: one past the operand reads bytes that are never used (inside
+    // the buffer range) or zeros (outside it), into a stage no wave still
+    // reads.  So the pipeline has no branches and the same number of loads
+    // in flight everywhere.
 #pragma unroll
     for (int j = 0; j < NST - 1; ++j) {
-        if (j < npre) {
 #pragma unroll
-            for (int k = 0; k < NP; ++k) issue_piece(j, j, k);
-        }
+        for (int k = 0; k < NP; ++k) issue_piece(j, j, k);
     }
     load_b(0, bqA);
     // chunk 0's DMAs landed for this wave (later issues may stay in flight)
-    wait_landed(npre - 1);
+    wait_landed(NST - 2);
     block_sync_lds();
 
     // every wave of the workgroup reads the same bytes: a uniform decision
@@ -537,7 +539,7 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
         wait_vm<0>();
         fallback_tile();
     } else {
-    read_meta(0, ratioA, zcA);
+    read_meta(0, ratioA, zcA, true);
     load_afr(0, afr[0], 0);
     {
         uint32_t w[PAIRS];
@@ -557,7 +559,6 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
         const int nst = st == NST - 1 ? 0 : st + 1;
         const int dst = st == 0 ? NST - 1 : st - 1;   // stage of chunk c + NST - 1
         const bool more = c + 1 < C;        // wave-uniform
-        const bool dma = c + NST - 1 < C;
         // one 16-k step; hs is a compile-time constant (the interleave
         // pattern needs constant counts)
         auto step = [&](auto hs_c) {
@@ -565,21 +566,22 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
             constexpr int gq = hs / HS_PER_GROUP;   // group within the chunk
             constexpr int t_in = hs % HS_PER_GROUP; // step within the group
             // the next chunk's code words, a chunk ahead
-            if (hs == 0 && more) load_b(c + 1, bq_n);
+            if (hs == 0) load_b(c + 1, bq_n);
             // LDS reads one step ahead (step 7 reads the next chunk's first)
             if (hs + 1 < 8) {
                 load_afr(st, afr[(hs + 1) & 1], hs + 1);
-            } else if (more) {
-                read_meta(nst, ratio_n, zc_n);
+            } else {
+                read_meta(nst, ratio_n, zc_n, more);
                 load_afr(nst, afr[0], 0);
             }
             // this chunk's share of the DMAs of chunk c + NST - 1
-            if (hs < 6 && dma) {
+            if (hs < 6) {
 #pragma unroll
                 for (int k = hs * NP_STEP; k < (hs + 1) * NP_STEP && k < NP; ++k) issue_piece(c + NST - 1, dst, k);
             }
-            // the matrix work, each group entered with its rescale
-            const bool rescale = t_in == 0 && !(c == 0 && hs == 0);
+            // the matrix work, each group entered with its rescale (the
+            // first group's factor is 0 or 1 and acc is still zero)
+            constexpr bool rescale = t_in == 0;
 #pragma unroll
             for (int q = 0; q < PAIRS; ++q) {
                 const float r = ratio[q][gq];
@@ -597,7 +599,7 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
             if (hs + 1 < 8) {
                 load_bw(bq, w, hs + 1);
                 unpack_b(w, zc, hs + 1, bop[(hs + 1) & 1]);
-            } else if (more) {
+            } else {
                 load_bw(bq_n, w, 0);
                 unpack_b(w, zc_n, 0, bop[0]);
             }
@@ -621,13 +623,11 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
         step(std::integral_constant<int, 4>());
         step(std::integral_constant<int, 5>());
         step(std::integral_constant<int, 6>());
-        if (more) {
-            // chunk c+1's DMAs landed for this wave (later issues: chunk
-            // c+1's code words and the DMAs of chunks c+2 .. c+NST-1, may
-            // stay in flight) ...
-            wait_landed(C - c - 2 < NST - 2 ? C - c - 2 : NST - 2);
-            block_sync_lds();   // ... and for every wave
-        }
+        // chunk c+1's DMAs landed for this wave (later issues: chunk c+1's
+        // code words and the DMAs of chunks c+2 .. c+NST-1, may stay in
+        // flight) ...
+        wait_landed(NST - 2);
+        block_sync_lds();   // ... and for every wave
         step(std::integral_constant<int, 7>());
         st = nst;
     };
@@ -636,6 +636,9 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
         if (c + 1 < C) chunk(c + 1, bqB, bqA, ratioB, ratioA, zcB, zcA);
     }
 
+    // the DMAs of the chunks past the last are not waited for in the loop;
+    // they land before the epilogue reuses the LDS
+    wait_vm<0>();
     // back from units of the last group's scale
 #pragma unroll
     for (int q = 0; q < PAIRS; ++q)
