@@ -73,6 +73,9 @@ __device__ __forceinline__ h8_t zero_h8()
     return z;
 }
 
+// LDS destination pointer of buffer_load ... lds
+typedef void __attribute__((address_space(3))) * lds_ptr_t;
+
 // A lane's scales of one tile and chunk as one integer (NS consecutive
 // scales), so the load stays a single instruction.
 template <typename ST, int NS> struct RawScales;
@@ -155,6 +158,15 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_small_kernel(SmallParams p)
     constexpr int NS = Q <= 4 ? Q : 4;           // scales per load (two loads for groups of 16)
     constexpr int NL = Q <= 4 ? 1 : 2;
     constexpr int SREC = kTileN * Q * (int)sizeof(ST), ZREC = kTileN / 2 * Q;
+    // For groups of 32 k or more the scales and zero points of a batch come
+    // through LDS: a few dword DMAs per wave (buffer_load ... lds, 64 dwords
+    // each) instead of one small load per record, then LDS reads.  A wave's
+    // region holds a full 64-lane slot per DMA, scales first, then zero points.
+    constexpr bool META_LDS = Q <= 4;
+    constexpr int R = kBatch * TPW;                                  // records per batch
+    constexpr int kSInstr = (R * SREC / 4 + 63) / 64;
+    constexpr int kMetaBytes = kSInstr * 256 + 256;
+    __shared__ __align__(16) unsigned char meta_lds[META_LDS ? kWaves : 1][META_LDS ? kMetaBytes : 16];
     constexpr uint32_t kFar = 0x80000000u;       // past every range: reads zero
     typedef typename RawScales<ST, NS>::type RawS;
     const int tid = threadIdx.x;
@@ -186,6 +198,24 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_small_kernel(SmallParams p)
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) total[tt] = f4_t{0.f, 0.f, 0.f, 0.f};
 
+    // DMA offsets (fixed per lane): scale dword p = lane + 64 m of record
+    // r = p / (SREC / 4); zero-point dword d = lane of record d / (ZREC / 4).
+    // Record r = u * TPW + tt is chunk cb + kWaves * u of tile tt.
+    uint32_t ms_voff[kSInstr];
+#pragma unroll
+    for (int m = 0; m < kSInstr; ++m) {
+        const int pc = lane + 64 * m;
+        const int r = pc / (SREC / 4), w = pc % (SREC / 4);
+        ms_voff[m] = pc < R * SREC / 4
+            ? (uint32_t)(((r % TPW) * C + kWaves * (r / TPW)) * SREC + w * 4) : kFar;
+    }
+    uint32_t mz_voff;
+    {
+        constexpr int ZD = ZREC / 4 > 0 ? ZREC / 4 : 1;
+        const int r = lane / ZD, w = lane % ZD;
+        mz_voff = (HAS_ZP && lane < R * ZD) ? (uint32_t)(((r % TPW) * C + kWaves * (r / TPW)) * ZREC + w * 4) : kFar;
+    }
+
     for (int cb = wave; cb < C; cb += kWaves * kBatch) {
         // Issue order: the A fragments of the batch, then its scales and
         // zero points, then its code words.  Waits count completions in
@@ -206,6 +236,16 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_small_kernel(SmallParams p)
         RawS sr[kBatch][TPW][NL];
         uint32_t zw[kBatch][TPW];
         uint32_t rec[kBatch][TPW];
+        if constexpr (META_LDS) {
+            unsigned char* mb = meta_lds[wave];
+#pragma unroll
+            for (int m = 0; m < kSInstr; ++m)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(s_rsrc, (lds_ptr_t)(mb + m * 256), 4, ms_voff[m],
+                                                         (uint32_t)cb * SREC, 0, 0);
+            if (HAS_ZP)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(z_rsrc, (lds_ptr_t)(mb + kSInstr * 256), 4, mz_voff,
+                                                         (uint32_t)cb * ZREC, 0, 0);
+        }
 #pragma unroll
         for (int u = 0; u < kBatch; ++u)
 #pragma unroll
@@ -213,6 +253,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_small_kernel(SmallParams p)
                 const int c = cb + kWaves * u;
                 // a tile past N reads zero (outside the range); its outputs are not stored
                 rec[u][tt] = (uint32_t)(tt * C + (c < C ? c : C - 1));
+                if (META_LDS) continue;
                 sr[u][tt][0] = buf_load<RawS>(s_rsrc, s_voff, rec[u][tt] * SREC);
                 // groups of 16: the even groups of the 16 columns, then the odd ones
                 if (NL > 1) sr[u][tt][NL - 1] = buf_load<RawS>(s_rsrc, s_voff + 16 * sizeof(RawS), rec[u][tt] * SREC);
@@ -233,6 +274,30 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_small_kernel(SmallParams p)
                 d[u][tt] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(
                     c_rsrc, (uint32_t)lane * 16u, rec[u][tt] * kChunkBytes, 2));
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (META_LDS) {
+            // wait until the DMAs (and the activation loads before them)
+            // have landed, the batch's code words may stay in flight (gfx9
+            // s_waitcnt: vmcnt = R < 16, expcnt and lgkmcnt left open); the
+            // LDS reads below stay after it
+            static_assert(R < 16, "vmcnt field");
+            __builtin_amdgcn_s_waitcnt(R | (7 << 4) | (15 << 8));
+            asm volatile("" ::: "memory");
+            const unsigned char* mb = meta_lds[wave];
+#pragma unroll
+            for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+                for (int tt = 0; tt < TPW; ++tt) {
+                    const int r = u * TPW + tt;
+                    sr[u][tt][0] = *reinterpret_cast<const RawS*>(mb + r * SREC + i * Q * (int)sizeof(ST));
+                    zw[u][tt] = 0;
+                    if (HAS_ZP) {
+                        const unsigned char* zr = mb + kSInstr * 256 + r * ZREC;
+                        if (Q == 1) zw[u][tt] = zr[i >> 1];
+                        else if (Q == 2) zw[u][tt] = zr[i];
+                        else zw[u][tt] = *reinterpret_cast<const uint16_t*>(zr + 2 * i);
+                    }
+                }
+        }
 
 #pragma unroll
         for (int u = 0; u < kBatch; ++u) {
