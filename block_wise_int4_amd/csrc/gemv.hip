@@ -201,7 +201,7 @@ __device__ __forceinline__ float chunk_dot_f16(const ChunkRegs<ST, Q, HAS_ZP>& r
             const int sj = LaneGroups<Q>::sidx(j);
             const uint32_t z = HAS_ZP ? (r.zw >> (4 * sj)) & 15u : 8u;
             h2_t q[4];
-            unpack8(dw[j], zp_const(z), q);
+            unpack_zr(dw[j], zp_pair(z), q);
             b[j] = as_h8(q);
             a[j] = *reinterpret_cast<const h8_t*>(as + c * kChunkK + 32 * j + 8 * h);
         }
@@ -218,7 +218,7 @@ __device__ __forceinline__ float chunk_dot_f16(const ChunkRegs<ST, Q, HAS_ZP>& r
         const int sj = LaneGroups<Q>::sidx(j);
         const uint32_t z = HAS_ZP ? (r.zw >> (4 * sj)) & 15u : 8u;
         h2_t q[4];
-        unpack8(dw[j], zp_const(z), q);
+        unpack_zr(dw[j], zp_pair(z), q);
         const h8_t b = as_h8(q);
         const h8_t a = *reinterpret_cast<const h8_t*>(as + c * kChunkK + 32 * j + 8 * h);
         {

@@ -53,6 +53,28 @@ __device__ __forceinline__ void unpack8(uint32_t d, ZpConst zc, h2_t out[4])
     out[3] = as_h2(__builtin_amdgcn_bitop3_b32(d8, hi, magic, 0xEA)) * sixteenth + as_h2(zc.neg64z);
 }
 
+// Both constants of zero point z for unpack_zr in one register: the low half
+// is -(1024 + z), the high half -(64 + z) (fp16 64 + z carries z in mantissa
+// bits 4..7).  z <= 15, so the halves form without carries: one 24-bit mad.
+__device__ __forceinline__ uint32_t zp_pair(uint32_t z) { return __umul24(z, 0x100001u) + 0xD400E400u; }
+
+// unpack8 with both constants of the zero point in one register (zp_pair):
+// each packed add or fma takes its constant from one half of zr for both of
+// its lanes (an op_sel broadcast), so a group costs one instruction for its
+// constants instead of two.
+__device__ __forceinline__ void unpack_zr(uint32_t d, uint32_t zr, h2_t out[4])
+{
+    const uint32_t lo = 0x000F000Fu, hi = 0x00F000F0u, magic = 0x64006400u;
+    const h2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    const h2_t r = as_h2(zr);
+    const h2_t c_lo = {r[0], r[0]}, c_hi = {r[1], r[1]};
+    const uint32_t d8 = d >> 8;
+    out[0] = as_h2(__builtin_amdgcn_bitop3_b32(d, lo, magic, 0xEA)) + c_lo;
+    out[1] = as_h2(__builtin_amdgcn_bitop3_b32(d, hi, magic, 0xEA)) * sixteenth + c_hi;
+    out[2] = as_h2(__builtin_amdgcn_bitop3_b32(d8, lo, magic, 0xEA)) + c_lo;
+    out[3] = as_h2(__builtin_amdgcn_bitop3_b32(d8, hi, magic, 0xEA)) * sixteenth + c_hi;
+}
+
 // The code of k-offset i (0..7) of a repacked word.
 __device__ __forceinline__ uint32_t code_at(uint32_t d, int i)
 {
