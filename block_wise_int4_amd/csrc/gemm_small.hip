@@ -76,6 +76,25 @@ __device__ __forceinline__ h8_t zero_h8()
 // LDS destination pointer of buffer_load ... lds
 typedef void __attribute__((address_space(3))) * lds_ptr_t;
 
+// One 16-byte LDS DMA per lane (lane L's bytes land at dst + 16 L).  The
+// builtin is compiled in the device pass only: the host pass compiles this
+// kernel just for its launch stub, and with the 16-byte form in it that pass
+// dropped the stub.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, lds_ptr_t dst, uint32_t voff, uint32_t soff)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
+#endif
+}
+
+// Wait until at most N vector-memory operations of this wave are
+// outstanding (gfx9 s_waitcnt encoding; expcnt and lgkmcnt left open).
+template <int N> __device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // A lane's scales of one tile and chunk as one integer (NS consecutive
 // scales), so the load stays a single instruction.
 template <typename ST, int NS> struct RawScales;
@@ -133,8 +152,15 @@ template <typename ST, int Q> constexpr int batch_of() { return sizeof(ST) == 2 
 template <typename ST, int Q, bool HAS_ZP, int TPW, bool KTAIL>
 __global__ __launch_bounds__(kWaves * 64) void gemm_small_kernel(SmallParams p)
 {
-    __shared__ float red[kWaves][TPW][256];
     constexpr int kBatch = batch_of<ST, Q>();
+    // Each wave's slices of A (its chunks' 128 k of all 16 rows, 4 KiB per
+    // chunk) reach a slot of its own by 16-byte LDS DMAs; the 16-byte
+    // segments of a row are XOR-swizzled by the row so fragment reads are
+    // conflict free.  After the wave's last chunk its slot holds its partial
+    // sums for the cross-wave reduction.
+    constexpr int kASlot = kBatch * 16 * kChunkK * 2;
+    static_assert(TPW * 256 * 4 <= kASlot, "the wave partials fit the wave's slot");
+    __shared__ __align__(16) unsigned char a_lds[kWaves][kASlot];
     constexpr int NS = Q <= 4 ? Q : 4;           // scales per load (two loads for groups of 16)
     constexpr int NL = Q <= 4 ? 1 : 2;
     constexpr int SREC = kTileN * Q * (int)sizeof(ST), ZREC = kTileN / 2 * Q;
@@ -170,7 +196,16 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_small_kernel(SmallParams p)
         (void*)p.a, (short)0, p.M * K * 2, 0x00020000);
 
     // lane parts of the offsets
-    const uint32_t a_voff = i < p.M ? ((uint32_t)i * (uint32_t)K + 8u * (uint32_t)h) * 2u : kFar;
+    // A DMA of row quad qd: lane L fetches row 4 qd + L / 16, logical
+    // segment (L % 16) ^ row (8 k each); rows >= M lie past the range (zeros)
+    uint32_t a_dvoff[4];
+    int a_dseg[4];
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd) {
+        const int r = 4 * qd + (lane >> 4);
+        a_dseg[qd] = ((lane & 15) ^ r) * 8;
+        a_dvoff[qd] = ((uint32_t)r * (uint32_t)K + (uint32_t)a_dseg[qd]) * 2u;
+    }
     const uint32_t s_voff = (uint32_t)(Q <= 4 ? i * Q : i * 4) * (uint32_t)sizeof(ST);
     const uint32_t z_voff = Q == 1 ? (uint32_t)(i >> 1) : (Q == 2 ? (uint32_t)i : (Q == 4 ? 2u * i : 2u * ((h >> 1) * 16 + i)));
 
@@ -202,15 +237,19 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_small_kernel(SmallParams p)
         // issue order, so the small loads never wait behind the code stream.
         // A chunk past K loads the last chunk's weights again and is not
         // computed.
-        h8_t afr[kBatch][4];
+        // row quads wholly past M are not fetched: those rows of the slot
+        // hold stale values, and MFMA output rows depend on their own A row
+        // only, so they reach no stored output
 #pragma unroll
         for (int u = 0; u < kBatch; ++u)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int k0 = (cb + kWaves * u) * kChunkK + 32 * j;   // wave-uniform
-                uint32_t vo = a_voff;
-                if (KTAIL && k0 + 8 * h >= K) vo = kFar;
-                afr[u][j] = __builtin_bit_cast(h8_t, buf_load<u4_t>(a_rsrc, vo, (uint32_t)k0 * 2u));
+            for (int qd = 0; qd < 4; ++qd) {
+                const int cu = cb + kWaves * u;               // wave-uniform
+                if (4 * qd < p.M) {
+                    uint32_t vo = a_dvoff[qd];
+                    if (KTAIL && cu * kChunkK + a_dseg[qd] >= K) vo = kFar;
+                    lds_dma16(a_rsrc, (lds_ptr_t)(a_lds[wave] + u * 4096 + qd * 1024), vo, (uint32_t)cu * (kChunkK * 2));
+                }
             }
         __builtin_amdgcn_sched_barrier(0);
         RawS sr[kBatch][TPW][NL];
@@ -254,14 +293,20 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_small_kernel(SmallParams p)
                 d[u][tt] = __builtin_bit_cast(u4_t, __builtin_amdgcn_raw_buffer_load_b128(
                     c_rsrc, (uint32_t)lane * 16u, rec[u][tt] * kChunkBytes, 2));
         __builtin_amdgcn_sched_barrier(0);
+        // wait until the DMAs (activation, and scales and zero points through
+        // LDS) have landed; the batch's code words (and for groups of 16 its
+        // scale and zero-point loads) may stay in flight.  The LDS reads
+        // below stay after it.
+        if constexpr (META_LDS) wait_vm<R>();
+        else wait_vm<R + R * (NL + (HAS_ZP ? 1 : 0))>();
+        asm volatile("" ::: "memory");
+        h8_t afr[kBatch][4];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                afr[u][j] = *reinterpret_cast<const h8_t*>(a_lds[wave] + u * 4096 + i * 256 + (((4 * j + h) ^ i) * 16));
         if constexpr (META_LDS) {
-            // wait until the DMAs (and the activation loads before them)
-            // have landed, the batch's code words may stay in flight (gfx9
-            // s_waitcnt: vmcnt = R < 16, expcnt and lgkmcnt left open); the
-            // LDS reads below stay after it
-            static_assert(R < 16, "vmcnt field");
-            __builtin_amdgcn_s_waitcnt(R | (7 << 4) | (15 << 8));
-            asm volatile("" ::: "memory");
             const unsigned char* mb = meta_lds[wave];
 #pragma unroll
             for (int u = 0; u < kBatch; ++u)
@@ -340,11 +385,13 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_small_kernel(SmallParams p)
         }
     }
 
-    // fixed-order reduction over the waves; D lane layout: row 4h + r, col i
+    // fixed-order reduction over the waves; D lane layout: row 4h + r, col i.
+    // A wave's partials go to its own slot, whose A reads are all done.
+    auto red_of = [&](int w) { return reinterpret_cast<float*>(a_lds[w]); };
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[wave][tt][(4 * h + r) * 16 + i] = total[tt][r];
+        for (int r = 0; r < 4; ++r) red_of(wave)[tt * 256 + (4 * h + r) * 16 + i] = total[tt][r];
     __syncthreads();
     for (int o = tid; o < TPW * 256; o += kWaves * 64) {
         const int tt = o >> 8;
@@ -357,8 +404,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_small_kernel(SmallParams p)
                 float v = 0.0f, v2 = 0.0f;
 #pragma unroll
                 for (int w = 0; w < kWaves; ++w) {
-                    v += red[w][tt][e];
-                    v2 += red[w][tt][e + 16];
+                    v += red_of(w)[tt * 256 + e];
+                    v2 += red_of(w)[tt * 256 + e + 16];
                 }
                 const int mo = row >> 1;
                 float out = (v + v2) * p.row_scale[mo];
@@ -370,7 +417,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_small_kernel(SmallParams p)
         if (row < p.M && n < p.N) {
             float v = 0.0f;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) v += red[w][tt][e];
+            for (int w = 0; w < kWaves; ++w) v += red_of(w)[tt * 256 + e];
             if (p.row_scale) {
                 const float rs = p.row_scale[row];
                 float o = rs != 0.0f ? v * rs : 0.0f;
