@@ -289,7 +289,12 @@ def test_small_m_workload_parity(mnb, small_m_workload, M):
 
 
 SMALL_CASES = [(2, 70, 384, 128, True), (3, 130, 160, 32, True), (7, 33, 4096, 64, False),
-               (16, 5, 48, 16, True), (9, 300, 640, 16, False), (5, 257, 896, 32, True)]
+               (16, 5, 48, 16, True), (9, 300, 640, 16, False), (5, 257, 896, 32, True),
+               # K not a multiple of 128 with two-chunk batches (groups of 64),
+               # M ending inside a row quad
+               (6, 100, 192, 64, True), (13, 40, 320, 64, False),
+               # several batches per wave (65 chunks) and a ragged last chunk
+               (4, 48, 8256, 64, True)]
 
 
 @pytest.mark.parametrize("M,N,K,g,zp", SMALL_CASES)
