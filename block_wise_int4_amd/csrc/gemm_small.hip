@@ -12,9 +12,12 @@
 // weight at most 16 times), so a workgroup owns a few 16-column tiles and its
 // waves split K.  Each wave streams one 16-byte code word per tile per
 // 128-k chunk, unpacks it in registers to the B operand of
-// v_mfma_f32_16x16x32_f16 and multiplies it with the A rows (rows >= M are
-// zero), loaded straight from global memory and reused across the tiles.
-// Waves then reduce through LDS in a fixed order.  The epilogue writes fp16
+// v_mfma_f32_16x16x32_f16 and multiplies it with the A rows, which reach a
+// slot of the wave's own in LDS by DMA and are reused across the tiles.  At
+// these sizes the kernel is bound by issued instructions, so every load is a
+// buffer load with the chunk in a scalar offset and the small per-chunk
+// records come through LDS too.  Waves then reduce through LDS in a fixed
+// order.  The epilogue writes fp16
 // (with an optional bias in either rounding) or, for int8 activation codes
 // as A (accuracy_level 4), fp32 times the row's activation scale plus an fp32
 // bias.
@@ -232,14 +235,13 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_small_kernel(SmallParams p)
     }
 
     for (int cb = wave; cb < C; cb += kWaves * kBatch) {
-        // Issue order: the A fragments of the batch, then its scales and
+        // Issue order: the batch's A slices (LDS DMAs), then its scales and
         // zero points, then its code words.  Waits count completions in
         // issue order, so the small loads never wait behind the code stream.
         // A chunk past K loads the last chunk's weights again and is not
-        // computed.
-        // row quads wholly past M are not fetched: those rows of the slot
-        // hold stale values, and MFMA output rows depend on their own A row
-        // only, so they reach no stored output
+        // computed.  Row quads wholly past M are not fetched: those rows of
+        // the slot hold stale values, and MFMA output rows depend on their
+        // own A row only, so they reach no stored output.
 #pragma unroll
         for (int u = 0; u < kBatch; ++u)
 #pragma unroll
