@@ -319,7 +319,9 @@ PREFILL_CASES = [(17, 70, 384, 128, True, "f16"), (130, 300, 512, 64, True, "f16
                  # 64-row tiles: groups of 32 or 16 k, and fp32 scales with
                  # zero points at 64 k; several row blocks and a ragged one
                  (200, 300, 1024, 32, True, "f16"), (65, 64, 256, 32, False, "f16"),
-                 (150, 130, 640, 64, True, "f32"), (130, 96, 512, 16, True, "f32")]
+                 (150, 130, 640, 64, True, "f32"), (130, 96, 512, 16, True, "f32"),
+                 # one chunk (every later DMA of the pipeline is for a chunk past K)
+                 (40, 48, 64, 32, True, "f16"), (24, 80, 128, 128, False, "f32")]
 
 
 @pytest.mark.parametrize("M,N,K,g,zp,sdt", PREFILL_CASES)
