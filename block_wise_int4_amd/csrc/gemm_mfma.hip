@@ -151,16 +151,16 @@ __device__ __forceinline__ h8_t as_h8(const h2_t q[4])
 // exactly nothing (NaN for infinite activations, as (c - z) * 0 * a does).
 // Both nibble halves use one packed fma, (x | magic) * m + a, with m = 1 or
 // 1/16 and a = -(1024 + z) or -(64 + z) for a live group and m = a = 0 for a
-// dead one: the same instruction count as unpack8.
+// dead one.  The two m and the two a sit in the halves of one register each
+// (a is zp_pair's), and each fma takes its pair from one half (op_sel).
 __device__ __forceinline__ void unpack8_scaled(uint32_t d, uint32_t zf, h2_t out[4])
 {
     const uint32_t lo = 0x000F000Fu, hi = 0x00F000F0u, magic = 0x64006400u;
     const bool dead = zf >= 16u;
-    const ZpConst zc = zp_const(zf & 15u);
-    const h2_t m_lo = as_h2(dead ? 0u : 0x3C003C00u);   // 1.0
-    const h2_t m_hi = as_h2(dead ? 0u : 0x2C002C00u);   // 1/16
-    const h2_t a_lo = as_h2(dead ? 0u : zc.neg1024z);
-    const h2_t a_hi = as_h2(dead ? 0u : zc.neg64z);
+    const h2_t m = as_h2(dead ? 0u : 0x2C003C00u);          // 1/16 (high half), 1.0 (low half)
+    const h2_t a = as_h2(dead ? 0u : zp_pair(zf & 15u));
+    const h2_t m_lo = {m[0], m[0]}, m_hi = {m[1], m[1]};
+    const h2_t a_lo = {a[0], a[0]}, a_hi = {a[1], a[1]};
     const uint32_t d8 = d >> 8;
     out[0] = as_h2(__builtin_amdgcn_bitop3_b32(d, lo, magic, 0xEA)) * m_lo + a_lo;
     out[1] = as_h2(__builtin_amdgcn_bitop3_b32(d, hi, magic, 0xEA)) * m_hi + a_hi;
