@@ -15,6 +15,13 @@
 //   blocks): their per-chunk rescale factors and zero points would push a
 //   96-row wave past 256 registers or its stages past half the LDS, one
 //   wave per SIMD, which measured twice as slow.
+// * Groups of 128 k also have a 128-row form (4 row blocks per wave): each
+//   unpacked B operand then feeds four MFMAs instead of three, and only two
+//   pipeline stages fit in the workgroup's half of the LDS.  The launcher
+//   picks the height per call from the number of workgroup rounds each
+//   leaves on the chip's CUs (a 128-row workgroup costs about 1.23 times a
+//   96-row one); both give the same bits, as every output adds the same
+//   products in the same order.
 // * A rows reach LDS by buffer_load ... lds (no VGPR round trip) into a ring
 //   of as many stages as the workgroup's share of LDS holds (three for the
 //   common record sizes); the DMAs of chunk c + stages - 1 are spread over the
@@ -48,6 +55,7 @@
 //   matmul_nbits.rs fold_bias_f16), or, for int8 activation codes as A
 //   (accuracy_level 4), fp32 outputs times the row's activation scale plus an
 //   fp32 bias.
+#include <atomic>
 #include <type_traits>
 
 #include "mnb_device.hpp"
@@ -68,7 +76,8 @@ constexpr int kWgPerCu = 8 / WAVES;          // two waves per SIMD
 constexpr int kLdsCu = 160 * 1024;
 constexpr int kLdsBudget = kLdsCu / kWgPerCu;   // this workgroup's share
 constexpr int kMaxStages = 6;
-constexpr int kMaxBM = 96;
+constexpr int kMaxBM = 96;         // rows of the three-stage form
+constexpr int kTallBM = 128;       // rows of the two-stage form (groups of 128 k)
 
 
 typedef float f16v_t __attribute__((ext_vector_type(16)));
@@ -99,11 +108,12 @@ struct GemmParams {
 };
 
 // Tile height and LDS geometry of one pipeline stage for (Q, scale bytes,
-// zero points).  Rows per workgroup: 96 when a 96-row stage leaves room for
-// three stages in the workgroup's half of the LDS and groups span 64 k or
-// more; else 64 (groups of 32 or 16 k, whose per-chunk rescale factors and
-// zero points would also push a 96-row wave past 256 registers).
-template <int Q, int SS, bool HAS_ZP> struct StageGeom {
+// zero points, tall).  Rows per workgroup: 128 for the tall form (groups of
+// 128 k, two stages); else 96 when a 96-row stage leaves room for three
+// stages in the workgroup's half of the LDS and groups span 64 k or more;
+// else 64 (groups of 32 or 16 k, whose per-chunk rescale factors and zero
+// points would also push a 96-row wave past 256 registers).
+template <int Q, int SS, bool HAS_ZP, bool TALL> struct StageGeom {
     static constexpr int kScaleDw = kTileN * Q * SS / 4;               // dwords per tile record
     static constexpr int kZpDw = HAS_ZP ? kTileN * Q / 8 : 0;          // 8Q bytes per tile record
     // per wave: the scale records of its tiles, then (from a 64-dword
@@ -114,8 +124,9 @@ template <int Q, int SS, bool HAS_ZP> struct StageGeom {
     static constexpr int kZpOffDw = kScaleInstr * 64;                  // zero points in the record
     static constexpr int kMetaDwPad = kMetaInstr * 64;
     static constexpr int kMeta = WAVES * kMetaDwPad * 4;
-    static constexpr bool kTall = Q < 4 && kLdsBudget / (kMaxBM * SEGS * 16 + kMeta) >= 3;
-    static constexpr int BM = kTall ? kMaxBM : 64;
+    static_assert(!TALL || Q == 1, "the two-stage form serves groups of 128 k");
+    static constexpr bool kFits96 = Q < 4 && kLdsBudget / (kMaxBM * SEGS * 16 + kMeta) >= 3;
+    static constexpr int BM = TALL ? kTallBM : kFits96 ? kMaxBM : 64;
     static constexpr int RB = BM / 32;                  // 32-row blocks per wave
     static constexpr int ROWS_PER_WAVE = BM / WAVES;    // A rows each wave copies per chunk
     static constexpr int A_DMA = ROWS_PER_WAVE / 4;     // 1 KiB (4-row) DMAs per wave per chunk
@@ -125,8 +136,10 @@ template <int Q, int SS, bool HAS_ZP> struct StageGeom {
     static constexpr int kBytes = kA + kB + kMeta;
     // as many pipeline stages as the workgroup's share of LDS holds (up to
     // kMaxStages); when that is fewer than three (large scale records), three
-    // or more in the whole LDS, leaving one workgroup per CU
-    static constexpr int kFit = kLdsBudget / kBytes >= 3 ? kLdsBudget / kBytes : kLdsCu / kBytes;
+    // or more in the whole LDS, leaving one workgroup per CU.  The tall form
+    // keeps two.
+    static constexpr int kMinStages = TALL ? 2 : 3;
+    static constexpr int kFit = kLdsBudget / kBytes >= kMinStages ? kLdsBudget / kBytes : kLdsCu / kBytes;
     static constexpr int kStages = kFit < kMaxStages ? kFit : kMaxStages;
     static constexpr int kDmaPerChunk = A_DMA + kMetaInstr;            // per wave
 };
@@ -203,20 +216,24 @@ __device__ __forceinline__ void tile_of(int bid, int num_m, int num_n, int& mb, 
     nb = r / gm;
 }
 
-template <typename ST, int Q, bool HAS_ZP> struct KernelLds {
-    typedef StageGeom<Q, (int)sizeof(ST), HAS_ZP> G;
-    static constexpr int kBytes = G::kStages * G::kBytes;
+// The pipeline's stages, or the epilogue's staging of the output block
+// (BM rows of 144 bytes per wave), whichever is larger.
+template <typename ST, int Q, bool HAS_ZP, bool TALL> struct KernelLds {
+    typedef StageGeom<Q, (int)sizeof(ST), HAS_ZP, TALL> G;
+    static constexpr int kPipe = G::kStages * G::kBytes;
+    static constexpr int kOut = WAVES * G::BM * 144;
+    static constexpr int kBytes = kPipe > kOut ? kPipe : kOut;
 };
 
 // F32OUT: the int8-activation epilogue (fp32 output, row scale, fp32 bias),
 // its own instantiation so that the fp16 kernel's code is not affected.
-template <typename ST, int Q, bool HAS_ZP, bool KTAIL, bool F32OUT>
+template <typename ST, int Q, bool HAS_ZP, bool KTAIL, bool F32OUT, bool TALL>
 __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmParams p)
 {
-    typedef StageGeom<Q, (int)sizeof(ST), HAS_ZP> G;
+    typedef StageGeom<Q, (int)sizeof(ST), HAS_ZP, TALL> G;
     constexpr int NST = G::kStages;
     constexpr int BM = G::BM, RB = G::RB, ROWS_PER_WAVE = G::ROWS_PER_WAVE, A_DMA = G::A_DMA;
-    __shared__ __align__(16) unsigned char lds[KernelLds<ST, Q, HAS_ZP>::kBytes];
+    __shared__ __align__(16) unsigned char lds[KernelLds<ST, Q, HAS_ZP, TALL>::kBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -238,15 +255,20 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
     };
 
     // ---- DMA sources ------------------------------------------------------
-    // Every buffer starts at this workgroup's first row or first tile, so
-    // offsets stay far inside 32 bits whatever the size of the operands, and
-    // rows, tiles and k outside the operand read as zero through the range
-    // check.  A: rows m0 .. m0+BM, ending at the last valid row; k >= K uses
-    // an offset past the range.
-    const int rows_here = (p.M - m0) < BM ? (p.M - m0) : BM;
-    const uint32_t a_bytes = (uint32_t)rows_here * (uint32_t)K * 2u;
-    const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(p.a + (int64_t)m0 * K), (short)0, (int)a_bytes, 0x00020000);
+    // Every buffer starts at this workgroup's (or wave's) first row or first
+    // tile, so offsets stay far inside 32 bits whatever the size of the
+    // operands, and rows, tiles and k outside the operand read as zero
+    // through the range check.  A: at most 32 rows from row r0 (the rows a
+    // wave copies, or one 32-row block), ending at the last valid row; k >= K
+    // uses an offset past the range.
+    auto a_rows = [&](int r0, int rows) {
+        int n = p.M - r0;
+        n = n < rows ? n : rows;
+        n = n > 0 ? n : 0;
+        return __builtin_amdgcn_make_buffer_rsrc((void*)(p.a + (n > 0 ? (int64_t)r0 * K : 0)), (short)0,
+                                                 (int)((uint32_t)n * (uint32_t)K * 2u), 0x00020000);
+    };
+    const __amdgpu_buffer_rsrc_t a_rsrc = a_rows(m0 + ROWS_PER_WAVE * wave, ROWS_PER_WAVE);
     const int t0 = nb * (BN / 16);                         // first tile of the workgroup
     const int tiles_here = (p.T - t0) < BN / 16 ? (p.T - t0) : BN / 16;
     const uint32_t code_bytes = (uint32_t)tiles_here * (uint32_t)C * 1024u;
@@ -278,9 +300,10 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
     uint32_t a_voff[A_DMA];
 #pragma unroll
     for (int idx = 0; idx < A_DMA; ++idx) {
-        const int r = ROWS_PER_WAVE * wave + 4 * idx + (lane >> 4);
+        const int rw = 4 * idx + (lane >> 4);          // row among the wave's
+        const int r = ROWS_PER_WAVE * wave + rw;       // row in the tile
         const int sg = (lane & 15) ^ (r & 15);         // logical segment at this slot
-        a_voff[idx] = ((uint32_t)r * (uint32_t)K + 8u * (uint32_t)sg) * 2u;
+        a_voff[idx] = ((uint32_t)rw * (uint32_t)K + 8u * (uint32_t)sg) * 2u;
     }
     uint32_t s_voff[G::kScaleInstr], z_voff[G::kZpInstr > 0 ? G::kZpInstr : 1];
 #pragma unroll
@@ -336,12 +359,15 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
     constexpr int HS_PER_GROUP = 8 / Q;          // 16-k steps per group (group = 128/Q)
     constexpr int NP = G::kDmaPerChunk;           // DMA pieces per chunk and wave
     constexpr int NP_STEP = (NP + 5) / 6;         // pieces issued per step (steps 0..5)
-    static_assert(NST >= 3, "the pipeline keeps at least three stages");
+    static_assert(NST >= 2, "the pipeline keeps at least two stages");
     static_assert((NST - 2) * NP + 2 * PAIRS < 64, "vmcnt range");
     // Wait until chunk j's DMAs (this wave's) have landed, with y later
     // chunks' DMAs and the next chunk's code words issued after them
-    // (y <= NST - 2; a smaller y than the truth only waits longer).
+    // (y <= NST - 2; a smaller y than the truth only waits longer).  With
+    // two stages, chunk j's DMAs and code words are issued in the same chunk,
+    // in no fixed order, and nothing later: wait for all of them.
     auto wait_landed = [&](int y) {
+        if constexpr (NST == 2) { wait_vm<0>(); return; }
         if constexpr (NST - 2 >= 4) { if (y >= 4) { wait_vm<4 * NP + 2 * PAIRS>(); return; } }
         if constexpr (NST - 2 >= 3) { if (y >= 3) { wait_vm<3 * NP + 2 * PAIRS>(); return; } }
         if constexpr (NST - 2 >= 2) { if (y >= 2) { wait_vm<2 * NP + 2 * PAIRS>(); return; } }
@@ -458,7 +484,8 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
                 f16v_t tot, grp;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) tot[e] = 0.f;
-                const uint32_t arow = (uint32_t)(rb * 32 + (lane & 31)) * (uint32_t)K * 2u;
+                const __amdgpu_buffer_rsrc_t ab_rsrc = a_rows(m0 + 64 * (rb >> 1), 64);
+                const uint32_t arow = (uint32_t)((rb & 1) * 32 + (lane & 31)) * (uint32_t)K * 2u;
                 for (int c = 0; c < C; ++c) {
                     u4_t bq[2];
 #pragma unroll
@@ -488,7 +515,7 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
                         h8_t a;
                         if (!KTAIL || k < K)
                             a = __builtin_bit_cast(h8_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                a_rsrc, arow + (uint32_t)k * 2u, 0, 0));
+                                ab_rsrc, arow + (uint32_t)k * 2u, 0, 0));
                         else
                             a = h8_t{};
                         h2_t u[4];
@@ -702,7 +729,7 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
             // row quads of one write instruction in different banks.  With
             // N % 4 == 0 a 16-byte segment is all inside or all outside.
             constexpr int RS = 288, HALF = BM / 2;
-            static_assert(WAVES * HALF * RS <= KernelLds<ST, Q, HAS_ZP>::kBytes, "half the fp32 block fits the LDS");
+            static_assert(WAVES * HALF * RS <= KernelLds<ST, Q, HAS_ZP, TALL>::kBytes, "half the fp32 block fits the LDS");
             block_sync_lds();   // every wave is past its last fragment reads
             unsigned char* ob = lds + wave * (HALF * RS);
             const int n = nb * BN + wave * 64 + (lane & 15) * 4;
@@ -756,7 +783,7 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
     auto store_f16 = [&](auto value) __attribute__((always_inline)) {
         if (p.vec_store) {
             constexpr int RS = 144;
-            static_assert(WAVES * BM * RS <= KernelLds<ST, Q, HAS_ZP>::kBytes, "the output block fits the LDS");
+            static_assert(WAVES * BM * RS <= KernelLds<ST, Q, HAS_ZP, TALL>::kBytes, "the output block fits the LDS");
             block_sync_lds();   // every wave is past its last fragment reads
             unsigned char* ob = lds + wave * (BM * RS);
 #pragma unroll
@@ -830,26 +857,72 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
     store_f16([&](int rb, int q, int e) { return __float2half_rn(acc[rb][q][e]); });
 }
 
-template <typename ST, int Q, bool HAS_ZP, bool F32OUT>
-void launch_k(const GemmParams& p, hipStream_t s)
+template <typename ST, int Q, bool HAS_ZP, bool F32OUT, bool TALL>
+void launch_k(GemmParams p, hipStream_t s)
 {
+    constexpr int BM = StageGeom<Q, (int)sizeof(ST), HAS_ZP, TALL>::BM;
+    p.num_m = (p.M + BM - 1) / BM;
     const int blocks = p.num_m * p.num_n;
-    if (p.K % kChunkK != 0)
-        gemm_mfma_kernel<ST, Q, HAS_ZP, true, F32OUT><<<dim3(blocks), dim3(WAVES * 64), 0, s>>>(p);
-    else
-        gemm_mfma_kernel<ST, Q, HAS_ZP, false, F32OUT><<<dim3(blocks), dim3(WAVES * 64), 0, s>>>(p);
+    if constexpr (TALL) {
+        // groups of 128 k: K is a multiple of the chunk
+        gemm_mfma_kernel<ST, Q, HAS_ZP, false, F32OUT, true><<<dim3(blocks), dim3(WAVES * 64), 0, s>>>(p);
+    } else if (p.K % kChunkK != 0) {
+        gemm_mfma_kernel<ST, Q, HAS_ZP, true, F32OUT, false><<<dim3(blocks), dim3(WAVES * 64), 0, s>>>(p);
+    } else {
+        gemm_mfma_kernel<ST, Q, HAS_ZP, false, F32OUT, false><<<dim3(blocks), dim3(WAVES * 64), 0, s>>>(p);
+    }
+}
+
+// Compute units of the current device (queried once per device).
+int device_cus()
+{
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+// A fixed tile height for groups of 128 k (96 or 128), or 0: per call.
+std::atomic<int> g_prefill_rows{0};
+
+// Tile height for groups of 128 k: the tall form when it leaves fewer
+// workgroup rounds, each weighted by its cost.  A round here is one
+// workgroup per CU (a CU holds two; one alone runs faster), and a 128-row
+// workgroup costs about 27/22 of a 96-row one (measured on MI355X at
+// M = 256 .. 4096, N = 14336, K = 4096).
+bool use_tall(const GemmParams& p)
+{
+    const int64_t cus = device_cus();
+    const int64_t rounds96 = ((int64_t)(p.M + kMaxBM - 1) / kMaxBM * p.num_n + cus - 1) / cus;
+    const int64_t rounds128 = ((int64_t)(p.M + kTallBM - 1) / kTallBM * p.num_n + cus - 1) / cus;
+    return 27 * rounds128 < 22 * rounds96;
+}
+
+template <typename ST, int Q, bool HAS_ZP, bool F32OUT>
+void launch_h(const GemmParams& p, hipStream_t s)
+{
+    if constexpr (Q == 1 && StageGeom<Q, (int)sizeof(ST), HAS_ZP, false>::BM == kMaxBM) {
+        const int rows = g_prefill_rows.load(std::memory_order_relaxed);
+        if (rows == kTallBM || (rows == 0 && use_tall(p))) {
+            launch_k<ST, Q, HAS_ZP, F32OUT, true>(p, s);
+            return;
+        }
+    }
+    launch_k<ST, Q, HAS_ZP, F32OUT, false>(p, s);
 }
 
 template <typename ST, int Q, bool HAS_ZP>
-hipError_t launch_t(const GemmParams& p0, hipStream_t s)
+hipError_t launch_t(const GemmParams& p, hipStream_t s)
 {
-    GemmParams p = p0;
-    constexpr int BM = StageGeom<Q, (int)sizeof(ST), HAS_ZP>::BM;
-    p.num_m = (p.M + BM - 1) / BM;
     if (p.row_scale)
-        launch_k<ST, Q, HAS_ZP, true>(p, s);
+        launch_h<ST, Q, HAS_ZP, true>(p, s);
     else
-        launch_k<ST, Q, HAS_ZP, false>(p, s);
+        launch_h<ST, Q, HAS_ZP, false>(p, s);
     return hipGetLastError();
 }
 
@@ -866,13 +939,20 @@ hipError_t launch_q(const Layout& L, const GemmParams& p, hipStream_t s)
 
 }  // namespace
 
-// Largest K the kernel's 32-bit buffer ranges and offsets cover: a
-// workgroup's rows of A (at most 96 * K * 2 bytes) and the code bytes of its
-// BN / 16 tiles (BN / 16 * C * 1024) each stay below 2^31.
+int set_prefill_rows(int rows)
+{
+    if (rows != 0 && rows != kMaxBM && rows != kTallBM) return -1;
+    return g_prefill_rows.exchange(rows);
+}
+
+// Largest K the kernel's 32-bit buffer ranges and offsets cover: the rows
+// of A behind one buffer resource (at most 32 * K * 2 bytes) and the code
+// bytes of a workgroup's BN / 16 tiles (BN / 16 * C * 1024) each stay below
+// 2^31.
 int64_t gemm_mfma_max_k()
 {
     const int64_t lim = (int64_t(1) << 31) - 1;
-    const int64_t by_a = lim / (2 * kMaxBM);
+    const int64_t by_a = lim / (2 * 32);
     const int64_t by_codes = lim / ((BN / 16) * 1024) * kChunkK;
     return by_a < by_codes ? by_a : by_codes;
 }

@@ -612,6 +612,8 @@ mnb_status mnb_unpack_debug(const mnb_weight_desc* w, const void* repacked, uint
                     "unpack_debug");
 }
 
+int32_t mnb_debug_prefill_rows(int32_t rows) { return mnb::set_prefill_rows(rows); }
+
 // Any value is accepted (an int at the boundary, not the enum type): unknown
 // ones give MNB_ERR_UNKNOWN.
 const char* mnb_status_string(int32_t status)

@@ -31,7 +31,7 @@ EXPORTS = ("mnb_repacked_bytes", "mnb_repacked_layout", "mnb_repack", "mnb_gemv"
            "mnb_act_order_permutation", "mnb_repack_act_order", "mnb_gemm_act_order_workspace_bytes",
            "mnb_gemm_act_order", "mnb_gemm_group_indices", "mnb_gemm_accuracy4_workspace_bytes", "mnb_gemm_accuracy4",
            "mnb_gemm_accuracy4_noalloc",
-           "mnb_unpack_debug", "mnb_status_string", "mnb_last_error", "mnb_last_variant")
+           "mnb_unpack_debug", "mnb_debug_prefill_rows", "mnb_status_string", "mnb_last_error", "mnb_last_variant")
 
 
 class MnbError(RuntimeError):
@@ -97,6 +97,7 @@ def _load():
         "mnb_gemm_accuracy4": (ctypes.c_int, [D, P, P, i64, P, P, P, sz, P]),
         "mnb_gemm_accuracy4_noalloc": (ctypes.c_int, [D, P, P, i64, P, P, P]),
         "mnb_unpack_debug": (ctypes.c_int, [D, P, P, P, P]),
+        "mnb_debug_prefill_rows": (ctypes.c_int32, [ctypes.c_int32]),
         "mnb_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "mnb_last_error": (ctypes.c_char_p, []),
         "mnb_last_variant": (ctypes.c_char_p, []),
@@ -289,6 +290,10 @@ def mnb_gemm_accuracy4_noalloc(w: mnb_weight_desc, repacked: Ptr, a, m: int, bia
 def mnb_unpack_debug(w: mnb_weight_desc, repacked: Ptr, codes: Ptr, w_f32: Ptr, stream=None) -> None:
     _check(lib.mnb_unpack_debug(ctypes.byref(w), _ptr(repacked), _ptr(codes), _ptr(w_f32),
                                 _stream(stream)))
+
+
+def mnb_debug_prefill_rows(rows: int) -> int:
+    return lib.mnb_debug_prefill_rows(rows)
 
 
 def mnb_status_string(s: int) -> str:

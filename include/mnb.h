@@ -187,7 +187,7 @@ size_t mnb_gemm_workspace_bytes_for(const mnb_weight_desc* w, int64_t m, int32_t
  * GEMV (its K limit applies); 2 <= M <= 16 a weight-streaming MFMA kernel
  * whose workgroups split K among their waves and reduce in a fixed order,
  * for K <= 33554432 (its 32-bit buffer ranges; else MNB_ERR_UNSUPPORTED);
- * larger M the MFMA prefill GEMM, for K <= 11184810 (its 32-bit buffer
+ * larger M the MFMA prefill GEMM, for K <= 16777088 (its 32-bit buffer
  * offsets; else MNB_ERR_UNSUPPORTED).  Products are fp16 x fp16 on the
  * matrix cores with fp32 accumulation; each group's partial sum is
  * multiplied by its scale after that group's accumulation.  fp32 A with
@@ -350,6 +350,14 @@ mnb_status mnb_gemm_accuracy4_noalloc(const mnb_weight_desc* w, const void* repa
  * output may be NULL. */
 mnb_status mnb_unpack_debug(const mnb_weight_desc* w, const void* repacked, uint8_t* codes,
                             float* w_f32, void* stream);
+
+/* Test-only: the tile height of the prefill GEMM (M > 16) for groups of
+ * 128 k.  rows = 0 (the default): chosen per call from the shape and the
+ * device's compute units; 96 or 128: that height for every later call in the
+ * process, from any thread.  Returns the previous setting; any other value
+ * changes nothing and returns -1.  Both heights give bit-identical results;
+ * this lets tests run either form at any size. */
+int32_t mnb_debug_prefill_rows(int32_t rows);
 
 /* Static string naming a status. */
 const char* mnb_status_string(int32_t status);

@@ -27,3 +27,14 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+@pytest.fixture(params=[0, 128], ids=["rows-auto", "rows128"])
+def prefill_rows(request):
+    """The prefill GEMM's tile height for groups of 128 k: chosen per call
+    (0; small shapes get 96 rows), or the 128-row form forced, so that small
+    shapes run it too.  Reset to per-call choice afterwards."""
+    from block_wise_int4_amd import mnb as m
+    m.mnb_debug_prefill_rows(request.param)
+    yield request.param
+    m.mnb_debug_prefill_rows(0)

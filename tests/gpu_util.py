@@ -1,6 +1,7 @@
 """Helpers shared by the GPU tests: upload seeded operands, run the C ABI,
 compare with the oracle under the per-element bound."""
 import numpy as np
+import pytest
 
 from block_wise_int4_amd import synth
 from oracle import oracle as o
@@ -83,3 +84,10 @@ def assert_within(y: np.ndarray, Y: np.ndarray, B: np.ndarray, what: str, bound=
         r = float(np.max(np.abs(y[fin] - Y[fin]) / tol[fin])) if fin.any() else 0.0
     print("%s: max |err|/bound = %.3g over %d outputs" % (what, r, y.size))
     return r
+
+
+def needs_tall_form(rows, g, M=None):
+    """Skip a forced 128-row run the case would not reach: the form serves
+    the prefill GEMM (M > 16) with groups of 128 k."""
+    if rows and (g != 128 or (M is not None and M <= 16)):
+        pytest.skip("the 128-row form serves the prefill GEMM with groups of 128 k")

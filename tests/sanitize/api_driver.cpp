@@ -20,6 +20,7 @@ int64_t gemv_max_k(bool, bool) { return int64_t(1) << 30; }
 int64_t acc4_gemv_max_k() { return int64_t(1) << 30; }
 int64_t gemm_mfma_max_k() { return int64_t(1) << 30; }
 int64_t gemm_small_max_k() { return int64_t(1) << 30; }
+int set_prefill_rows(int) { return 0; }
 size_t gemm_small_workspace(const Layout&, int64_t) { return 0; }
 hipError_t launch_repack(const Layout&, const uint8_t*, const void*, const uint8_t*, const int32_t*, void*,
                          hipStream_t) { std::abort(); }

@@ -172,12 +172,13 @@ def test_argument_validation():
 
 def test_prefill_k_limit():
     """M > 16 runs the prefill GEMM, whose buffer offsets are 32-bit: K up to
-    11184810 (96 rows of A below 2^31 bytes) is accepted (without a device
-    the call then stops at the device check), one group more is refused
-    before anything is enqueued, by every entry point that reaches it."""
+    16777088 (131071 chunks: the code bytes of a 256-column workgroup below
+    2^31) is accepted (without a device the call then stops at the device
+    check), one group more is refused before anything is enqueued, by every
+    entry point that reaches it."""
     lib = mnb.lib
     U, DEV = mnb.MNB_ERR_UNSUPPORTED, mnb.MNB_ERR_DEVICE
-    k_ok = 11184810 // 128 * 128
+    k_ok = 16777088
     ok, over = mnb.desc(16, k_ok, 128, False, mnb.MNB_F16), mnb.desc(16, k_ok + 128, 128, False, mnb.MNB_F16)
     assert lib.mnb_gemm(D(ok), FAKE, FAKE, 17, 1, FAKE, None, 0, None) == DEV
     assert "prefill GEMM limit" in _expect(U, lib.mnb_gemm, D(over), FAKE, FAKE, 17, 1, FAKE, None, 0, None)
@@ -345,3 +346,16 @@ def test_one_hip_runtime_in_the_process():
     # torch's HIP runtime and libmnb's must be the same library instance
     runtimes = mnb._hip_runtimes_mapped()
     assert len(runtimes) == 1, runtimes
+
+
+def test_prefill_rows_setting():
+    """The test-only tile-height setting of the prefill GEMM: 0, 96 and 128
+    are taken and each call returns the previous one; anything else changes
+    nothing and returns -1."""
+    set_rows = mnb.mnb_debug_prefill_rows
+    assert set_rows(96) == 0
+    assert set_rows(128) == 96
+    assert set_rows(64) == -1
+    assert set_rows(7) == -1
+    assert set_rows(0) == 128
+    assert set_rows(0) == 0

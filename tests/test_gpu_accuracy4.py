@@ -67,7 +67,7 @@ ACC4_CASES = [
     (2, 300, 512, 32, "f32", True, True), (5, 257, 896, 64, "f16", False, False),
     (16, 100, 1024, 16, "f32", True, True),
     (40, 300, 512, 64, "f32", True, True), (130, 70, 384, 128, "f16", False, False),
-    (200, 513, 1024, 32, "f32", True, True),
+    (200, 513, 1024, 32, "f32", True, True), (260, 300, 512, 128, "f32", True, True),
     # the prefill's 64-row tiles (groups of 32 or 16 k, fp32 scales with zero
     # points at 64 k) with 16-byte fp32 row stores (N % 4 == 0), ragged M
     (150, 256, 1024, 32, "f32", True, True), (97, 260, 512, 16, "f16", False, False),
@@ -79,7 +79,8 @@ ACC4_CASES = [
 
 
 @pytest.mark.parametrize("M,N,K,g,sdt,zp,with_bias", ACC4_CASES)
-def test_accuracy4_parity(mnb, M, N, K, g, sdt, zp, with_bias):
+def test_accuracy4_parity(mnb, prefill_rows, M, N, K, g, sdt, zp, with_bias):
+    G.needs_tall_form(prefill_rows, g, M)
     w = _weight(N, K, g, sdt, zp, seed=M)
     A = synth.activation(M, K, "f32", 1.0, (310, M, K))
     bias = synth.activation(1, N, "f32", 1.0, (311, N)).reshape(N) if with_bias else None

@@ -321,11 +321,16 @@ PREFILL_CASES = [(17, 70, 384, 128, True, "f16"), (130, 300, 512, 64, True, "f16
                  (200, 300, 1024, 32, True, "f16"), (65, 64, 256, 32, False, "f16"),
                  (150, 130, 640, 64, True, "f32"), (130, 96, 512, 16, True, "f32"),
                  # one chunk (every later DMA of the pipeline is for a chunk past K)
-                 (40, 48, 64, 32, True, "f16"), (24, 80, 128, 128, False, "f32")]
+                 (40, 48, 64, 32, True, "f16"), (24, 80, 128, 128, False, "f32"),
+                 # groups of 128 k with ragged row blocks of either height and a
+                 # ragged column block
+                 (200, 300, 512, 128, True, "f16"), (129, 48, 256, 128, False, "f32"),
+                 (260, 40, 384, 128, True, "f32")]
 
 
 @pytest.mark.parametrize("M,N,K,g,zp,sdt", PREFILL_CASES)
-def test_prefill_ragged_parity(mnb, M, N, K, g, zp, sdt):
+def test_prefill_ragged_parity(mnb, prefill_rows, M, N, K, g, zp, sdt):
+    G.needs_tall_form(prefill_rows, g)
     t = G.torch()
     w = _weight(N, K, g, sdt, zp, lo=0.002, hi=0.01)
     A = _act(M, K, sigma=0.5)
@@ -412,14 +417,16 @@ def test_prefill_mid_size_sampled_parity(mnb):
         assert t.equal(y, y2)
 
 
-def test_prefill_output_alignment_paths_agree(mnb):
+@pytest.mark.parametrize("g", [64, 128])
+def test_prefill_output_alignment_paths_agree(mnb, prefill_rows, g):
     """The prefill GEMM stores whole 16-byte row segments when N % 8 == 0 and
     Y is 16-byte aligned, and element by element otherwise: the same product
     into a Y shifted by one element (2-byte aligned only) gives the same bits,
     with and without a bias, and for the fp32 output of the int8-activation
     path (4-byte shift)."""
+    G.needs_tall_form(prefill_rows, g)
     t = G.torch()
-    M, N, K, g = 200, 520, 512, 64
+    M, N, K = 200, 520, 512
     w = _weight(N, K, g, "f16", True, seed=31)
     q = G.upload(w)
     a = G.to_dev(_act(M, K, seed=31))
@@ -462,36 +469,50 @@ def _sparse_row(K, seed):
 
 
 def test_prefill_at_maximum_k(mnb):
-    """The prefill GEMM at its largest K (11184768 = 87381 chunks): a full
-    96-row block of A is 2^31 bytes less 8 KiB, so the last row's offsets come
-    within 0.4% of the 32-bit limit.  One workgroup (M = 96, N = 32) runs
-    every chunk.  Every row is sparse (_sparse_row, the memory traffic is
-    that of a dense row); rows 0, 1, 47 and 95 are checked against the oracle
-    on every column."""
+    """The prefill GEMM at its largest K (16777088 = 131071 chunks): the 16
+    code tiles of a 256-column workgroup span 2^31 bytes less 16 KiB, so the
+    last tile's code offsets come within 0.001% of the 32-bit limit, and the
+    64 rows of A behind one buffer resource of the plain per-group path just
+    as close.  M = 128 in both tile heights (96: a full block and a partial
+    one; 128: one block), each on one column block (N = 256).  Rows are
+    sparse (_sparse_row, the memory traffic is that of a dense row); rows 0,
+    1, 95, 96 and 127 are checked against the oracle on the columns of the
+    first and the last tile, and the two heights give the same bits
+    everywhere."""
     t = G.torch()
-    M, N, g = 96, 32, 128
-    K = 11184810 // 128 * 128
+    M, N, g = 128, 256, 128
+    K = 16777088
     w = _weight(N, K, g, "f16", True, seed=21, lo=0.002, hi=0.01)
     q = G.upload(w)
     a = t.empty((M, K), dtype=t.float16, device="cuda")
-    rows = [0, 1, 47, 95]
+    rows = [0, 1, 95, 96, 127]
     kept = {}
     for m in range(M):
         r = _sparse_row(K, (210, m))
         a[m].copy_(t.from_numpy(r))
         if m in rows:
             kept[m] = r
-    y = t.empty((M, N), dtype=t.float16, device="cuda")
-    G.gemm(q, a, M, y)
-    assert mnb.mnb_last_variant() == "gemm_mfma_32x32x16"
-    yh = G.host(y)
+    outs = {}
+    try:
+        for bm in (96, 128):
+            mnb.mnb_debug_prefill_rows(bm)
+            y = t.empty((M, N), dtype=t.float16, device="cuda")
+            G.gemm(q, a, M, y)
+            assert mnb.mnb_last_variant() == "gemm_mfma_32x32x16"
+            outs[bm] = G.host(y)
+            del y
+    finally:
+        mnb.mnb_debug_prefill_rows(0)
     del a
     t.cuda.empty_cache()
+    assert np.array_equal(outs[96].view(np.uint16), outs[128].view(np.uint16))
+    cols = np.r_[0:16, N - 16:N]
     A = np.stack([kept[m] for m in rows])
-    ms = np.repeat(np.arange(len(rows)), N)
-    ns = np.tile(np.arange(N), len(rows))
+    ms = np.repeat(np.arange(len(rows)), len(cols))
+    ns = np.tile(cols, len(rows))
     Y, B = o.matmul_nbits_at(A, w.packed, w.scales, w.zero_points, N, K, g, ms, ns)
-    G.assert_within(yh[np.array(rows)[ms], ns], Y, B, "prefill at K=%d" % K)
+    for bm in (96, 128):
+        G.assert_within(outs[bm][np.array(rows)[ms], ns], Y, B, "prefill (%d rows) at K=%d" % (bm, K))
 
 
 def test_small_m_at_maximum_k(mnb):
@@ -534,13 +555,14 @@ BIAS_CASES = [
 
 
 @pytest.mark.parametrize("M,N,K,g,adt,zp", BIAS_CASES)
-def test_bias_epilogue_parity(mnb, M, N, K, g, adt, zp):
+def test_bias_epilogue_parity(mnb, prefill_rows, M, N, K, g, adt, zp):
     """The bias epilogue on every path, one bias vector for all rows (stride
     0) and a per-row residual (stride N + 5).  After-round mode must equal,
     bit for bit, the oracle's epilogue applied to the unbiased output (the
     two-operator path); fused mode is checked against Y + b (fp64) under the
     accumulator's bound plus one fp32 add and one fp16 rounding; a zero bias
     changes nothing.  fp32 outputs add once in both modes."""
+    G.needs_tall_form(prefill_rows, g, M)
     t = G.torch()
     w = _weight(N, K, g, "f16", zp, seed=M)
     A = _act(M, K, adt, seed=M + 1)
@@ -603,11 +625,12 @@ ACT_ORDER_CASES = [
 
 
 @pytest.mark.parametrize("M,N,K,g,adt,zp", ACT_ORDER_CASES)
-def test_act_order_parity(mnb, M, N, K, g, adt, zp):
+def test_act_order_parity(mnb, prefill_rows, M, N, K, g, adt, zp):
     """Act-order weights (random g_idx, every group of exactly g positions):
     the repack in permuted order and the GEMM on permuted activation columns,
     against the oracle's act-order dequant (scale and zero point of group
     g_idx[k]) and fp64 matmul, on every path."""
+    G.needs_tall_form(prefill_rows, g, M)
     t = G.torch()
     w = _weight(N, K, g, "f16", zp, seed=M + 3)
     rng = np.random.default_rng(M * 31 + K)
@@ -812,7 +835,7 @@ def test_nan_and_inf_propagate(mnb):
         G.assert_within(G.host(y), Y, B, "nan/inf M=%d" % M)
 
 
-def test_zero_and_non_finite_scales(mnb):
+def test_zero_and_non_finite_scales(mnb, prefill_rows):
     """Groups whose scale is 0 add exactly nothing, and a NaN scale makes
     its column NaN, on every path: GEMV, small M, MFMA.  The same weights are
     checked at several group sizes and both scale dtypes (the dequantized
@@ -869,12 +892,13 @@ def _f32_rows(M, K, seed):
 
 
 @pytest.mark.parametrize("M,N,K,g,sdt,zp", F32_CASES)
-def test_f32_activations_gemm_parity(mnb, M, N, K, g, sdt, zp):
+def test_f32_activations_gemm_parity(mnb, prefill_rows, M, N, K, g, sdt, zp):
     """fp32 activations with M > 1: rows split into fp16 (hi, lo) pairs under
     a power-of-two row scale, the fp16 GEMM on the 2M rows, the pairs summed
     and scaled back in fp32.  Against the oracle on the fp32 values (exact in
     fp64), with huge, tiny, subnormal, NaN and infinite rows, and with an fp32
     bias vector and a per-row bias."""
+    G.needs_tall_form(prefill_rows, g, 2 * M)
     t = G.torch()
     w = _weight(N, K, g, sdt, zp, seed=M + 21)
     q = G.upload(w)
@@ -944,13 +968,14 @@ def _extreme_scales(N, kb, base, big=False):
 
 
 @pytest.mark.parametrize("K,g", [(512, 128), (512, 32), (400, 16)])
-def test_extreme_scale_ranges(mnb, K, g):
+def test_extreme_scale_ranges(mnb, prefill_rows, K, g):
     """fp32 scales whose magnitudes within a column differ by up to 2^121, or
     are subnormal, on every path: the GEMV and small-M kernels apply each
     group's scale to a fresh partial; the prefill GEMM keeps one rescaled
     accumulator for tiles in its range class (recorded by the repack, checked
     here against the host model) and computes the other tiles with fresh
     partials.  Outputs within the bound everywhere."""
+    G.needs_tall_form(prefill_rows, g)
     t = G.torch()
     N = 96
     kb = K // g
@@ -971,9 +996,10 @@ def test_extreme_scale_ranges(mnb, K, g):
 
 
 @pytest.mark.parametrize("K,g", [(512, 128), (400, 16)])
-def test_extreme_scale_ranges_int8_activations(mnb, K, g):
+def test_extreme_scale_ranges_int8_activations(mnb, prefill_rows, K, g):
     """The same extreme scales, plus a 1e30 scale beside a 1e-30 one, through
     the int8-activation product (fp32 outputs hold the large values)."""
+    G.needs_tall_form(prefill_rows, g)
     t = G.torch()
     N = 96
     kb = K // g
