@@ -36,7 +36,10 @@ DEVICE_FLAGS = [
 
 # per-source extras: the prefill GEMM keeps its MFMA accumulators in VGPRs, so
 # the per-group scaling reads them without v_accvgpr_read copies
-EXTRA_FLAGS = {"gemm_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+EXTRA_FLAGS = {"gemm_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+               # the first 16 argument dwords of the memory-bound kernels arrive in SGPRs
+               "gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"],
+               "gemm_small.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
 
 
 def _compile(src: str) -> str:

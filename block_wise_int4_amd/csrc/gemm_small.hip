@@ -152,9 +152,37 @@ template <typename ST, int Q> constexpr int batch_of() { return sizeof(ST) == 2 
 // buffer ranges, a lane's part of each offset is fixed, and the chunk's part
 // is wave-uniform (a scalar offset), so addressing costs no vector
 // instructions.  Activation rows >= M read zero through the range check.
+//
+// The arguments are scalars, those the first loads need first (the codes,
+// scales and zero points, A, M, K, C and the tile count): built with kernarg
+// preloading (-amdgpu-kernarg-preload-count), the first 16 dwords arrive in
+// SGPRs when the wave starts instead of through a scalar load of the
+// argument block.
 template <typename ST, int Q, bool HAS_ZP, int TPW, bool KTAIL>
-__global__ __launch_bounds__(kWaves * 64) void gemm_small_kernel(SmallParams p)
+__global__ __launch_bounds__(kWaves * 64) void gemm_small_kernel(
+    const u4_t* codes, const void* scales, const uint8_t* zp, const _Float16* a, int M_, int K_, int C_, int64_t T_,
+    int N_, __half* y, const __half* bias, int64_t bias_stride, int bias_after_round, float* y32,
+    const float* row_scale, const float* bias32, int64_t bias32_stride, int pair_rows)
 {
+    SmallParams p;
+    p.codes = codes;
+    p.scales = scales;
+    p.zp = zp;
+    p.a = a;
+    p.y = y;
+    p.bias = bias;
+    p.bias_stride = bias_stride;
+    p.bias_after_round = bias_after_round;
+    p.y32 = y32;
+    p.row_scale = row_scale;
+    p.bias32 = bias32;
+    p.bias32_stride = bias32_stride;
+    p.pair_rows = pair_rows;
+    p.M = M_;
+    p.N = N_;
+    p.K = K_;
+    p.C = C_;
+    p.T = T_;
     constexpr int kBatch = batch_of<ST, Q>();
     // Each wave's slices of A (its chunks' 128 k of all 16 rows, 4 KiB per
     // chunk) reach a slot of its own by 16-byte LDS DMAs; the 16-byte
@@ -438,9 +466,13 @@ hipError_t launch_t(const SmallParams& p, hipStream_t s)
 {
     const int64_t blocks = (p.T + TPW - 1) / TPW;
     if (p.K % kChunkK != 0)
-        gemm_small_kernel<ST, Q, HAS_ZP, TPW, true><<<dim3((unsigned)blocks), dim3(kWaves * 64), 0, s>>>(p);
+        gemm_small_kernel<ST, Q, HAS_ZP, TPW, true><<<dim3((unsigned)blocks), dim3(kWaves * 64), 0, s>>>(
+            p.codes, p.scales, p.zp, p.a, p.M, p.K, p.C, p.T, p.N, p.y, p.bias, p.bias_stride, p.bias_after_round, p.y32,
+            p.row_scale, p.bias32, p.bias32_stride, p.pair_rows);
     else
-        gemm_small_kernel<ST, Q, HAS_ZP, TPW, false><<<dim3((unsigned)blocks), dim3(kWaves * 64), 0, s>>>(p);
+        gemm_small_kernel<ST, Q, HAS_ZP, TPW, false><<<dim3((unsigned)blocks), dim3(kWaves * 64), 0, s>>>(
+            p.codes, p.scales, p.zp, p.a, p.M, p.K, p.C, p.T, p.N, p.y, p.bias, p.bias_stride, p.bias_after_round, p.y32,
+            p.row_scale, p.bias32, p.bias32_stride, p.pair_rows);
     return hipGetLastError();
 }
 

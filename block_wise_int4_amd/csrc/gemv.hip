@@ -291,8 +291,29 @@ __host__ __device__ inline size_t stage_bytes(int waves, int C)
 // straight-line code holding one register set; LOOP = true: batches alternate
 // between two register sets.
 template <typename AT, typename ST, int Q, bool HAS_ZP, bool FUSED, int kBatch, bool PERM, bool LOOP>
-__global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
+//
+// The arguments are scalars in the order the kernel first needs them (the
+// weight's codes, scales and zero points, A, Y, the sizes and the wave
+// count), not one structure: built with kernarg preloading
+// (-amdgpu-kernarg-preload-count), the first 16 dwords arrive in SGPRs when
+// the wave starts, so the first loads are issued without waiting on a
+// scalar load of the argument block.  The rest are loaded when used.
+__global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
+    const u4_t* codes0, const void* scales0, const uint8_t* zp0, const void* a, void* y, int N, int K, int C,
+    int nw, const u4_t* codes1, const void* scales1, const uint8_t* zp1, const void* bias, int bias_after_round,
+    const int32_t* perm)
 {
+    GemvParams p;
+    p.w[0] = GemvWeight{codes0, scales0, zp0};
+    p.w[1] = GemvWeight{codes1, scales1, zp1};
+    p.a = a;
+    p.y = y;
+    p.bias = bias;
+    p.bias_after_round = bias_after_round;
+    p.perm = perm;
+    p.N = N;
+    p.K = K;
+    p.C = C;
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr bool F16 = sizeof(AT) == 2;
     constexpr bool WAVE_STAGE = !LOOP && !PERM;
@@ -302,10 +323,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = uniform(tid >> 6);
-    const int nw = blockDim.x >> 6;
     const int h = lane >> 4;
     const int64_t t = blockIdx.x;
-    const int C = p.C;
     const int64_t kpad = (int64_t)C * kChunkK;
 
     // Issue order of a wave: its first activation vector, then the scales
@@ -323,9 +342,9 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
     if constexpr (PERM) {
 #pragma unroll
         for (int j = 0; j < kPermPre; ++j) {
-            const int v = tid + j * (int)blockDim.x;
+            const int v = tid + j * (nw * 64);
             // workgroup-uniform test: only the vectors that exist are requested
-            pidx[j] = (j == 0 || j * (int)blockDim.x < nq) ? perm_vec[v < nq ? v : 0] : u4_t{0u, 0u, 0u, 0u};
+            pidx[j] = (j == 0 || j * (nw * 64) < nq) ? perm_vec[v < nq ? v : 0] : u4_t{0u, 0u, 0u, 0u};
         }
     }
 
@@ -405,7 +424,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
         act = reinterpret_cast<const unsigned char*>(slot);
     } else {
         if (tid < nvec) s_vec[tid] = tid < nvec_valid ? first : u4_t{0u, 0u, 0u, 0u};
-        for (int v = tid + blockDim.x; v < nvec; v += blockDim.x)
+        for (int v = tid + nw * 64; v < nvec; v += nw * 64)
             s_vec[v] = v < nvec_valid ? a_vec[v] : u4_t{0u, 0u, 0u, 0u};
         block_sync_lds();
     }
@@ -431,10 +450,10 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(GemvParams p)
         };
 #pragma unroll
         for (int j = 0; j < kPermPre; ++j) {
-            const int v = tid + j * (int)blockDim.x;
+            const int v = tid + j * (nw * 64);
             if (v < nq_pad) gather4(v, pidx[j]);
         }
-        for (int v = tid + kPermPre * (int)blockDim.x; v < nq_pad; v += blockDim.x)
+        for (int v = tid + kPermPre * (nw * 64); v < nq_pad; v += nw * 64)
             gather4(v, perm_vec[v < nq ? v : 0]);
         block_sync_lds();
         act = dst;
@@ -538,7 +557,9 @@ void launch_k(const GemvParams& p, int waves, int64_t tiles, hipStream_t s)
     constexpr bool WAVE_STAGE = !LOOP && !PERM;
     const size_t stage = stage_bytes<AT, B, WAVE_STAGE>(waves, p.C);
     const size_t smem = stage + kRedBytes + (PERM ? stage : 0);
-    gemv_kernel<AT, ST, Q, HAS_ZP, FUSED, B, PERM, LOOP><<<dim3((unsigned)tiles), dim3(waves * 64), smem, s>>>(p);
+    gemv_kernel<AT, ST, Q, HAS_ZP, FUSED, B, PERM, LOOP><<<dim3((unsigned)tiles), dim3(waves * 64), smem, s>>>(
+        p.w[0].codes, p.w[0].scales, p.w[0].zp, p.a, p.y, p.N, p.K, p.C, waves, p.w[1].codes, p.w[1].scales,
+        p.w[1].zp, p.bias, p.bias_after_round, p.perm);
 }
 
 template <typename AT, typename ST, int Q, bool HAS_ZP, bool FUSED, bool PERM>
