@@ -39,7 +39,10 @@ DEVICE_FLAGS = [
 EXTRA_FLAGS = {"gemm_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
                # the first 16 argument dwords of the memory-bound kernels arrive in SGPRs
                "gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"],
-               "gemm_small.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
+               "gemm_small.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"],
+               "acc4.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"],
+               "act_order.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"],
+               "f32_split.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
 
 
 def _compile(src: str) -> str:
