@@ -37,12 +37,11 @@ DEVICE_FLAGS = [
 # per-source extras: the prefill GEMM keeps its MFMA accumulators in VGPRs, so
 # the per-group scaling reads them without v_accvgpr_read copies
 EXTRA_FLAGS = {"gemm_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-               # the first 16 argument dwords of the memory-bound kernels arrive in SGPRs
+               # the first 16 argument dwords of the fp16 GEMV and the small-M kernel
+               # arrive in SGPRs (measured faster; the int8-activation GEMV measured
+               # slower with it)
                "gemv.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"],
-               "gemm_small.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"],
-               "acc4.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"],
-               "act_order.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"],
-               "f32_split.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
+               "gemm_small.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=16"]}
 
 
 def _compile(src: str) -> str:

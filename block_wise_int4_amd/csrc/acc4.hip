@@ -154,36 +154,21 @@ __device__ __forceinline__ float chunk_acc4(const Chunk<ST, Q>& r, const unsigne
     return acc;
 }
 
-// The arguments are scalars, those the first loads need first: built with
-// kernarg preloading (-amdgpu-kernarg-preload-count), the first 16 dwords
-// arrive in SGPRs when the wave starts.  nw is the workgroup's wave count.
 template <typename ST, int Q, bool HAS_ZP, int kBatch>
-__global__ __launch_bounds__(kMaxWaves * 64) void acc4_gemv_kernel(
-    const u4_t* codes, const void* scales, const uint8_t* zp, const float* a, int N, int K, int C, int nw,
-    float* y, const float* bias, _Float16* q_out, float* s_out)
+__global__ __launch_bounds__(kMaxWaves * 64) void acc4_gemv_kernel(Acc4Params p)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     typedef Chunk<ST, Q> Regs;
     constexpr int G = kChunkK / Q;
-    Acc4Params p;
-    p.codes = codes;
-    p.scales = scales;
-    p.zp = zp;
-    p.a = a;
-    p.bias = bias;
-    p.y = y;
-    p.q_out = q_out;
-    p.s_out = s_out;
-    p.N = N;
-    p.K = K;
-    p.C = C;
 
     const int tid = threadIdx.x;
-    const int bd = nw * 64;
+    const int bd = blockDim.x;
     const int lane = tid & 63;
     const int wave = uniform(tid >> 6);
+    const int nw = bd >> 6;
     const int h = lane >> 4;
     const int64_t t = blockIdx.x;
+    const int C = p.C;
     const int kpad = C * kChunkK;
     const int nv = kpad / 4;      // 4-activation vectors, padding included
     const int nvk = p.K / 4;      // valid ones (K is a multiple of the group size)
@@ -405,11 +390,9 @@ template <typename ST, int Q, bool HAS_ZP>
 hipError_t launch_t(const Acc4Params& p, int waves, size_t smem, int64_t tiles, hipStream_t s)
 {
     if (waves > kMaxWaves / 2)
-        acc4_gemv_kernel<ST, Q, HAS_ZP, 2><<<dim3((unsigned)tiles), dim3(waves * 64), smem, s>>>(
-            p.codes, p.scales, p.zp, p.a, p.N, p.K, p.C, waves, p.y, p.bias, p.q_out, p.s_out);
+        acc4_gemv_kernel<ST, Q, HAS_ZP, 2><<<dim3((unsigned)tiles), dim3(waves * 64), smem, s>>>(p);
     else
-        acc4_gemv_kernel<ST, Q, HAS_ZP, 4><<<dim3((unsigned)tiles), dim3(waves * 64), smem, s>>>(
-            p.codes, p.scales, p.zp, p.a, p.N, p.K, p.C, waves, p.y, p.bias, p.q_out, p.s_out);
+        acc4_gemv_kernel<ST, Q, HAS_ZP, 4><<<dim3((unsigned)tiles), dim3(waves * 64), smem, s>>>(p);
     return hipGetLastError();
 }
 
