@@ -579,10 +579,13 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
     // loop below runs two chunks per trip), so nothing is copied between
     // chunks.  st: pipeline stage of chunk c (wave-uniform).
     int st = 0;
-    auto chunk = [&](int c, const u4_t (&bq)[PAIRS][2], u4_t (&bq_n)[PAIRS][2],
+    auto chunk = [&](auto par, int c, const u4_t (&bq)[PAIRS][2], u4_t (&bq_n)[PAIRS][2],
                      const float (&ratio)[PAIRS][Q], float (&ratio_n)[PAIRS][Q],
                      const uint32_t (&zc)[PAIRS][Q], uint32_t (&zc_n)[PAIRS][Q])
         __attribute__((always_inline)) {
+        // two stages: the first chunk of a trip is always in stage 0, the
+        // second in stage 1, so the stage offsets are constants
+        if constexpr (NST == 2) st = decltype(par)::value;
         const int nst = st == NST - 1 ? 0 : st + 1;
         const int dst = st == 0 ? NST - 1 : st - 1;   // stage of chunk c + NST - 1
         const bool more = c + 1 < C;        // wave-uniform
@@ -659,8 +662,8 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
         st = nst;
     };
     for (int c = 0; c < C; c += 2) {
-        chunk(c, bqA, bqB, ratioA, ratioB, zcA, zcB);
-        if (c + 1 < C) chunk(c + 1, bqB, bqA, ratioB, ratioA, zcB, zcA);
+        chunk(std::integral_constant<int, 0>(), c, bqA, bqB, ratioA, ratioB, zcA, zcB);
+        if (c + 1 < C) chunk(std::integral_constant<int, 1>(), c + 1, bqB, bqA, ratioB, ratioA, zcB, zcA);
     }
 
     // the DMAs of the chunks past the last are not waited for in the loop;
