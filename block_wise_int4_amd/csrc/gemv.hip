@@ -526,7 +526,22 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
 #pragma unroll
         for (int x = 0; x < NW; ++x) {
             r[x] = 0.0f;
-            for (int ww = 0; ww < nw; ++ww) r[x] += red[(x * kMaxWaves + ww) * 16 + lane];
+            // the common wave counts unrolled: every read in flight at once,
+            // then the same sum in the same order
+            auto sum_all = [&](auto n_c) __attribute__((always_inline)) {
+                constexpr int NWV = decltype(n_c)::value;
+                float pv[NWV];
+#pragma unroll
+                for (int ww = 0; ww < NWV; ++ww) pv[ww] = red[(x * kMaxWaves + ww) * 16 + lane];
+#pragma unroll
+                for (int ww = 0; ww < NWV; ++ww) r[x] += pv[ww];
+            };
+            if (nw == kMaxWaves)
+                sum_all(std::integral_constant<int, kMaxWaves>());
+            else if (nw == kMaxWaves / 2)
+                sum_all(std::integral_constant<int, kMaxWaves / 2>());
+            else
+                for (int ww = 0; ww < nw; ++ww) r[x] += red[(x * kMaxWaves + ww) * 16 + lane];
         }
         const int64_t n = t * kTileN + lane;
         if (n < p.N) {
