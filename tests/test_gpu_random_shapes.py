@@ -30,6 +30,22 @@ def _draw(i):
     return M, N, K, g, sdt, zp, kind, rng
 
 
+N_PREFILL_CASES = 16
+
+
+def _draw_prefill(i):
+    """Prefill shapes with groups of 128 k, the ones both tile heights serve."""
+    rng = np.random.default_rng((510, i))
+    g = 128
+    K = g * int(rng.integers(1, 13))
+    N = int(rng.integers(1, 400))
+    M = int(rng.integers(17, 300))
+    sdt = str(rng.choice(["f16", "f32"]))
+    zp = bool(rng.integers(0, 2))
+    kind = str(rng.choice(["plain", "bias", "act_order", "accuracy4"]))
+    return M, N, K, g, sdt, zp, kind, rng
+
+
 @pytest.fixture(scope="module")
 def mnb():
     from block_wise_int4_amd import mnb as m
@@ -38,14 +54,35 @@ def mnb():
 
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_shape(mnb, i):
+    _run_case(mnb, i, *_draw(i), seed=500)
+
+
+@pytest.mark.parametrize("i", range(N_PREFILL_CASES))
+def test_random_prefill_shape_in_both_tile_heights(mnb, i):
+    """The prefill GEMM's two tile heights (96 and 128 rows, forced) on seeded
+    shapes with groups of 128 k: each within the bound against the oracle,
+    and the two bit for bit the same."""
+    outs = []
+    try:
+        for rows in (96, 128):
+            assert mnb.mnb_debug_prefill_rows(rows) in (0, 96, 128)
+            outs.append(_run_case(mnb, i, *_draw_prefill(i), seed=510))
+    finally:
+        mnb.mnb_debug_prefill_rows(0)
+    assert outs[0].dtype == outs[1].dtype
+    assert np.array_equal(outs[0].view(np.uint8), outs[1].view(np.uint8)), "case %d: the heights differ" % i
+
+
+def _run_case(mnb, i, M, N, K, g, sdt, zp, kind, rng, seed):
+    """One drawn case through its call, checked against the oracle; returns
+    the output on the host."""
     t = G.torch()
-    M, N, K, g, sdt, zp, kind, rng = _draw(i)
-    what = "case %d: %s M=%d N=%d K=%d g=%d %s zp=%s" % (i, kind, M, N, K, g, sdt, zp)
+    what = "case %d/%d: %s M=%d N=%d K=%d g=%d %s zp=%s" % (seed, i, kind, M, N, K, g, sdt, zp)
     print(what, flush=True)
-    w = synth.weight(N, K, g, sdt, (0.005, 0.02), zp, (501, i))
+    w = synth.weight(N, K, g, sdt, (0.005, 0.02), zp, (seed + 1, i))
     if kind == "accuracy4":
-        A = synth.activation(M, K, "f32", 1.0, (502, i))
-        bias = synth.activation(1, N, "f32", 1.0, (503, i)).reshape(N) if rng.integers(0, 2) else None
+        A = synth.activation(M, K, "f32", 1.0, (seed + 2, i))
+        bias = synth.activation(1, N, "f32", 1.0, (seed + 3, i)).reshape(N) if rng.integers(0, 2) else None
         q = G.upload(w)
         n_ws = mnb.mnb_gemm_accuracy4_workspace_bytes(q.desc, M)
         ws = t.zeros(n_ws, dtype=t.uint8, device="cuda")
@@ -58,11 +95,12 @@ def test_random_shape(mnb, i):
         codes = raw[off:off + 2 * M * K].view(np.float16).reshape(M, K).astype(np.float64)
         assert (codes == qc).all(), what
         assert (raw[:4 * M].view(np.uint32) == sc.view(np.uint32)).all(), what
-        G.assert_within(G.host(y), Y, B, what, bound=o.acc4_bound(B, K, g))
-        return
+        yh = G.host(y)
+        G.assert_within(yh, Y, B, what, bound=o.acc4_bound(B, K, g))
+        return yh
     # fp16 activations for every GEMM; fp32 only at M = 1
     adt = "f32" if (M == 1 and rng.integers(0, 3) == 0) else "f16"
-    A = synth.activation(M, K, adt, 1.0, (504, i))
+    A = synth.activation(M, K, adt, 1.0, (seed + 4, i))
     odt = t.float16 if adt == "f16" else t.float32
     y = t.empty((M, N), dtype=odt, device="cuda")
     if kind == "act_order":
@@ -79,13 +117,14 @@ def test_random_shape(mnb, i):
         mnb.mnb_gemm_act_order(d, rep, G.to_dev(A), M, perm, y, ws, n_ws)
         W = o.dequant_gidx(w.packed, w.scales, w.zero_points, g_idx, N, K, g)
         Y, B = o.matmul(o.decode(A.reshape(-1, K)), W)
-        G.assert_within(G.host(y), Y, B, what)
-        return
+        yh = G.host(y)
+        G.assert_within(yh, Y, B, what)
+        return yh
     q = G.upload(w)
     ws, n = G.workspace(q, M)
     if kind == "bias":
         after = bool(rng.integers(0, 2))
-        bias = synth.activation(1, N, adt, 1.0, (505, i)).reshape(N)
+        bias = synth.activation(1, N, adt, 1.0, (seed + 5, i)).reshape(N)
         mnb.mnb_gemm_bias(q.desc, q.repacked, G.to_dev(A), M, G.to_dev(bias), 0,
                           mnb.MNB_BIAS_AFTER_ROUND if after else mnb.MNB_BIAS_FUSED, y, ws, n)
         Y, B = o.matmul_nbits(A, w.packed, w.scales, w.zero_points, N, K, g)
@@ -94,8 +133,11 @@ def test_random_shape(mnb, i):
             bound = o.bias_bound(Y, B, b64)
         else:
             bound = o.REL_TOL * B + o.ABS_TOL + 2.0 ** -24 * np.abs(Y + b64)
-        G.assert_within(G.host(y), Y + b64, B, what, bound=bound)
-        return
+        yh = G.host(y)
+        G.assert_within(yh, Y + b64, B, what, bound=bound)
+        return yh
     mnb.mnb_gemm(q.desc, q.repacked, G.to_dev(A), M, y, ws, n)
     Y, B = o.matmul_nbits(A, w.packed, w.scales, w.zero_points, N, K, g)
-    G.assert_within(G.host(y), Y, B, what)
+    yh = G.host(y)
+    G.assert_within(yh, Y, B, what)
+    return yh
