@@ -17,11 +17,13 @@
 //   wave per SIMD, which measured twice as slow.
 // * Groups of 128 k also have a 128-row form (4 row blocks per wave): each
 //   unpacked B operand then feeds four MFMAs instead of three, and only two
-//   pipeline stages fit in the workgroup's half of the LDS.  The launcher
-//   picks the height per call from the number of workgroup rounds each
-//   leaves on the chip's CUs (a 128-row workgroup costs about 1.23 times a
-//   96-row one); both give the same bits, as every output adds the same
-//   products in the same order.
+//   pipeline stages fit in the workgroup's half of the LDS; and a 64-row
+//   form, faster where every workgroup fits on the chip at once.  The
+//   launcher picks the height per call from the number of workgroup rounds
+//   each leaves on the chip's CUs, weighted by its cost (a 64-row workgroup
+//   about 0.82 times a 96-row one, a 128-row one about 1.23 times); all give
+//   the same bits, as every output adds the same products in the same
+//   order.
 // * A rows reach LDS by buffer_load ... lds (no VGPR round trip) into a ring
 //   of as many stages as the workgroup's share of LDS holds (three for the
 //   common record sizes); the DMAs of chunk c + stages - 1 are spread over the
@@ -78,6 +80,7 @@ constexpr int kLdsBudget = kLdsCu / kWgPerCu;   // this workgroup's share
 constexpr int kMaxStages = 6;
 constexpr int kMaxBM = 96;         // rows of the three-stage form
 constexpr int kTallBM = 128;       // rows of the two-stage form (groups of 128 k)
+constexpr int kShortBM = 64;       // rows of the short form
 
 
 typedef float f16v_t __attribute__((ext_vector_type(16)));
@@ -108,12 +111,13 @@ struct GemmParams {
 };
 
 // Tile height and LDS geometry of one pipeline stage for (Q, scale bytes,
-// zero points, tall).  Rows per workgroup: 128 for the tall form (groups of
-// 128 k, two stages); else 96 when a 96-row stage leaves room for three
-// stages in the workgroup's half of the LDS and groups span 64 k or more;
-// else 64 (groups of 32 or 16 k, whose per-chunk rescale factors and zero
-// points would also push a 96-row wave past 256 registers).
-template <int Q, int SS, bool HAS_ZP, bool TALL> struct StageGeom {
+// zero points, requested height H).  Rows per workgroup: H when given (128:
+// the two-stage form for groups of 128 k; 64: the short form); else 96 when
+// a 96-row stage leaves room for three stages in the workgroup's half of the
+// LDS and groups span 64 k or more; else 64 (groups of 32 or 16 k, whose
+// per-chunk rescale factors and zero points would also push a 96-row wave
+// past 256 registers).
+template <int Q, int SS, bool HAS_ZP, int H> struct StageGeom {
     static constexpr int kScaleDw = kTileN * Q * SS / 4;               // dwords per tile record
     static constexpr int kZpDw = HAS_ZP ? kTileN * Q / 8 : 0;          // 8Q bytes per tile record
     // per wave: the scale records of its tiles, then (from a 64-dword
@@ -124,9 +128,10 @@ template <int Q, int SS, bool HAS_ZP, bool TALL> struct StageGeom {
     static constexpr int kZpOffDw = kScaleInstr * 64;                  // zero points in the record
     static constexpr int kMetaDwPad = kMetaInstr * 64;
     static constexpr int kMeta = WAVES * kMetaDwPad * 4;
-    static_assert(!TALL || Q == 1, "the two-stage form serves groups of 128 k");
+    static_assert(H == 0 || H == kShortBM || (H == kTallBM && Q == 1),
+                  "the two-stage form serves groups of 128 k");
     static constexpr bool kFits96 = Q < 4 && kLdsBudget / (kMaxBM * SEGS * 16 + kMeta) >= 3;
-    static constexpr int BM = TALL ? kTallBM : kFits96 ? kMaxBM : 64;
+    static constexpr int BM = H ? H : kFits96 ? kMaxBM : kShortBM;
     static constexpr int RB = BM / 32;                  // 32-row blocks per wave
     static constexpr int ROWS_PER_WAVE = BM / WAVES;    // A rows each wave copies per chunk
     static constexpr int A_DMA = ROWS_PER_WAVE / 4;     // 1 KiB (4-row) DMAs per wave per chunk
@@ -136,9 +141,9 @@ template <int Q, int SS, bool HAS_ZP, bool TALL> struct StageGeom {
     static constexpr int kBytes = kA + kB + kMeta;
     // as many pipeline stages as the workgroup's share of LDS holds (up to
     // kMaxStages); when that is fewer than three (large scale records), three
-    // or more in the whole LDS, leaving one workgroup per CU.  The tall form
-    // keeps two.
-    static constexpr int kMinStages = TALL ? 2 : 3;
+    // or more in the whole LDS, leaving one workgroup per CU.  The 128-row
+    // form keeps two.
+    static constexpr int kMinStages = BM == kTallBM ? 2 : 3;
     static constexpr int kFit = kLdsBudget / kBytes >= kMinStages ? kLdsBudget / kBytes : kLdsCu / kBytes;
     static constexpr int kStages = kFit < kMaxStages ? kFit : kMaxStages;
     static constexpr int kDmaPerChunk = A_DMA + kMetaInstr;            // per wave
@@ -218,8 +223,8 @@ __device__ __forceinline__ void tile_of(int bid, int num_m, int num_n, int& mb, 
 
 // The pipeline's stages, or the epilogue's staging of the output block
 // (BM rows of 144 bytes per wave), whichever is larger.
-template <typename ST, int Q, bool HAS_ZP, bool TALL> struct KernelLds {
-    typedef StageGeom<Q, (int)sizeof(ST), HAS_ZP, TALL> G;
+template <typename ST, int Q, bool HAS_ZP, int H> struct KernelLds {
+    typedef StageGeom<Q, (int)sizeof(ST), HAS_ZP, H> G;
     static constexpr int kPipe = G::kStages * G::kBytes;
     static constexpr int kOut = WAVES * G::BM * 144;
     static constexpr int kBytes = kPipe > kOut ? kPipe : kOut;
@@ -227,13 +232,13 @@ template <typename ST, int Q, bool HAS_ZP, bool TALL> struct KernelLds {
 
 // F32OUT: the int8-activation epilogue (fp32 output, row scale, fp32 bias),
 // its own instantiation so that the fp16 kernel's code is not affected.
-template <typename ST, int Q, bool HAS_ZP, bool KTAIL, bool F32OUT, bool TALL>
+template <typename ST, int Q, bool HAS_ZP, bool KTAIL, bool F32OUT, int H>
 __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmParams p)
 {
-    typedef StageGeom<Q, (int)sizeof(ST), HAS_ZP, TALL> G;
+    typedef StageGeom<Q, (int)sizeof(ST), HAS_ZP, H> G;
     constexpr int NST = G::kStages;
     constexpr int BM = G::BM, RB = G::RB, ROWS_PER_WAVE = G::ROWS_PER_WAVE, A_DMA = G::A_DMA;
-    __shared__ __align__(16) unsigned char lds[KernelLds<ST, Q, HAS_ZP, TALL>::kBytes];
+    __shared__ __align__(16) unsigned char lds[KernelLds<ST, Q, HAS_ZP, H>::kBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -732,7 +737,7 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
             // row quads of one write instruction in different banks.  With
             // N % 4 == 0 a 16-byte segment is all inside or all outside.
             constexpr int RS = 288, HALF = BM / 2;
-            static_assert(WAVES * HALF * RS <= KernelLds<ST, Q, HAS_ZP, TALL>::kBytes, "half the fp32 block fits the LDS");
+            static_assert(WAVES * HALF * RS <= KernelLds<ST, Q, HAS_ZP, H>::kBytes, "half the fp32 block fits the LDS");
             block_sync_lds();   // every wave is past its last fragment reads
             unsigned char* ob = lds + wave * (HALF * RS);
             const int n = nb * BN + wave * 64 + (lane & 15) * 4;
@@ -786,7 +791,7 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
     auto store_f16 = [&](auto value) __attribute__((always_inline)) {
         if (p.vec_store) {
             constexpr int RS = 144;
-            static_assert(WAVES * BM * RS <= KernelLds<ST, Q, HAS_ZP, TALL>::kBytes, "the output block fits the LDS");
+            static_assert(WAVES * BM * RS <= KernelLds<ST, Q, HAS_ZP, H>::kBytes, "the output block fits the LDS");
             block_sync_lds();   // every wave is past its last fragment reads
             unsigned char* ob = lds + wave * (BM * RS);
 #pragma unroll
@@ -860,19 +865,18 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
     store_f16([&](int rb, int q, int e) { return __float2half_rn(acc[rb][q][e]); });
 }
 
-template <typename ST, int Q, bool HAS_ZP, bool F32OUT, bool TALL>
+template <typename ST, int Q, bool HAS_ZP, bool F32OUT, int H>
 void launch_k(GemmParams p, hipStream_t s)
 {
-    constexpr int BM = StageGeom<Q, (int)sizeof(ST), HAS_ZP, TALL>::BM;
+    constexpr int BM = StageGeom<Q, (int)sizeof(ST), HAS_ZP, H>::BM;
     p.num_m = (p.M + BM - 1) / BM;
     const int blocks = p.num_m * p.num_n;
-    if constexpr (TALL) {
+    if (Q == 1 || p.K % kChunkK == 0) {
         // groups of 128 k: K is a multiple of the chunk
-        gemm_mfma_kernel<ST, Q, HAS_ZP, false, F32OUT, true><<<dim3(blocks), dim3(WAVES * 64), 0, s>>>(p);
-    } else if (p.K % kChunkK != 0) {
-        gemm_mfma_kernel<ST, Q, HAS_ZP, true, F32OUT, false><<<dim3(blocks), dim3(WAVES * 64), 0, s>>>(p);
+        gemm_mfma_kernel<ST, Q, HAS_ZP, false, F32OUT, H><<<dim3(blocks), dim3(WAVES * 64), 0, s>>>(p);
     } else {
-        gemm_mfma_kernel<ST, Q, HAS_ZP, false, F32OUT, false><<<dim3(blocks), dim3(WAVES * 64), 0, s>>>(p);
+        if constexpr (Q != 1)
+            gemm_mfma_kernel<ST, Q, HAS_ZP, true, F32OUT, H><<<dim3(blocks), dim3(WAVES * 64), 0, s>>>(p);
     }
 }
 
@@ -890,33 +894,35 @@ int device_cus()
     return n;
 }
 
-// A fixed tile height for groups of 128 k (96 or 128), or 0: per call.
+// A fixed tile height for groups of 128 k (64, 96 or 128), or 0: per call.
 std::atomic<int> g_prefill_rows{0};
 
-// Tile height for groups of 128 k: the tall form when it leaves fewer
-// workgroup rounds, each weighted by its cost.  A round here is one
-// workgroup per CU (a CU holds two; one alone runs faster), and a 128-row
-// workgroup costs about 27/22 of a 96-row one (measured on MI355X at
-// M = 256 .. 4096, N = 14336, K = 4096).
-bool use_tall(const GemmParams& p)
+// Tile height for groups of 128 k: the one whose workgroup rounds, weighted
+// by its cost, are fewest.  A round here is one workgroup per CU (a CU holds
+// two; one alone runs faster).  Costs relative to a 96-row workgroup: 64
+// rows 18/22, 128 rows 27/22 (measured on MI355X at M = 32 .. 4096,
+// N = 14336, K = 4096).  Ties go to the taller tile.
+int pick_rows(const GemmParams& p)
 {
     const int64_t cus = device_cus();
-    const int64_t rounds96 = ((int64_t)(p.M + kMaxBM - 1) / kMaxBM * p.num_n + cus - 1) / cus;
-    const int64_t rounds128 = ((int64_t)(p.M + kTallBM - 1) / kTallBM * p.num_n + cus - 1) / cus;
-    return 27 * rounds128 < 22 * rounds96;
+    auto cost = [&](int bm, int64_t w) { return w * ((((int64_t)p.M + bm - 1) / bm * p.num_n + cus - 1) / cus); };
+    int best = kTallBM;
+    int64_t c = cost(kTallBM, 27);
+    if (cost(kMaxBM, 22) < c) { best = kMaxBM; c = cost(kMaxBM, 22); }
+    if (cost(kShortBM, 18) < c) best = kShortBM;
+    return best;
 }
 
 template <typename ST, int Q, bool HAS_ZP, bool F32OUT>
 void launch_h(const GemmParams& p, hipStream_t s)
 {
-    if constexpr (Q == 1 && StageGeom<Q, (int)sizeof(ST), HAS_ZP, false>::BM == kMaxBM) {
-        const int rows = g_prefill_rows.load(std::memory_order_relaxed);
-        if (rows == kTallBM || (rows == 0 && use_tall(p))) {
-            launch_k<ST, Q, HAS_ZP, F32OUT, true>(p, s);
-            return;
-        }
+    if constexpr (Q == 1 && StageGeom<Q, (int)sizeof(ST), HAS_ZP, 0>::BM == kMaxBM) {
+        int rows = g_prefill_rows.load(std::memory_order_relaxed);
+        if (rows == 0) rows = pick_rows(p);
+        if (rows == kTallBM) { launch_k<ST, Q, HAS_ZP, F32OUT, kTallBM>(p, s); return; }
+        if (rows == kShortBM) { launch_k<ST, Q, HAS_ZP, F32OUT, kShortBM>(p, s); return; }
     }
-    launch_k<ST, Q, HAS_ZP, F32OUT, false>(p, s);
+    launch_k<ST, Q, HAS_ZP, F32OUT, 0>(p, s);
 }
 
 template <typename ST, int Q, bool HAS_ZP>
@@ -944,7 +950,7 @@ hipError_t launch_q(const Layout& L, const GemmParams& p, hipStream_t s)
 
 int set_prefill_rows(int rows)
 {
-    if (rows != 0 && rows != kMaxBM && rows != kTallBM) return -1;
+    if (rows != 0 && rows != kShortBM && rows != kMaxBM && rows != kTallBM) return -1;
     return g_prefill_rows.exchange(rows);
 }
 

@@ -29,11 +29,11 @@ def pytest_collection_modifyitems(config, items):
             item.add_marker(skip)
 
 
-@pytest.fixture(params=[0, 128], ids=["rows-auto", "rows128"])
+@pytest.fixture(params=[0, 64, 128], ids=["rows-auto", "rows64", "rows128"])
 def prefill_rows(request):
     """The prefill GEMM's tile height for groups of 128 k: chosen per call
-    (0; small shapes get 96 rows), or the 128-row form forced, so that small
-    shapes run it too.  Reset to per-call choice afterwards."""
+    (0), or the 64- or 128-row form forced, so that every shape runs each
+    form.  Reset to per-call choice afterwards."""
     from block_wise_int4_amd import mnb as m
     m.mnb_debug_prefill_rows(request.param)
     yield request.param

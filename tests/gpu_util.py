@@ -87,7 +87,7 @@ def assert_within(y: np.ndarray, Y: np.ndarray, B: np.ndarray, what: str, bound=
 
 
 def needs_tall_form(rows, g, M=None):
-    """Skip a forced 128-row run the case would not reach: the form serves
-    the prefill GEMM (M > 16) with groups of 128 k."""
+    """Skip a forced tile height the case would not reach: the forced
+    heights serve the prefill GEMM (M > 16) with groups of 128 k."""
     if rows and (g != 128 or (M is not None and M <= 16)):
-        pytest.skip("the 128-row form serves the prefill GEMM with groups of 128 k")
+        pytest.skip("forced tile heights serve the prefill GEMM with groups of 128 k")

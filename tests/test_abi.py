@@ -349,13 +349,14 @@ def test_one_hip_runtime_in_the_process():
 
 
 def test_prefill_rows_setting():
-    """The test-only tile-height setting of the prefill GEMM: 0, 96 and 128
-    are taken and each call returns the previous one; anything else changes
-    nothing and returns -1."""
+    """The test-only tile-height setting of the prefill GEMM: 0, 64, 96 and
+    128 are taken and each call returns the previous one; anything else
+    changes nothing and returns -1."""
     set_rows = mnb.mnb_debug_prefill_rows
     assert set_rows(96) == 0
     assert set_rows(128) == 96
-    assert set_rows(64) == -1
+    assert set_rows(64) == 128
+    assert set_rows(32) == -1
     assert set_rows(7) == -1
-    assert set_rows(0) == 128
+    assert set_rows(0) == 64
     assert set_rows(0) == 0

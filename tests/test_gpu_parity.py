@@ -473,8 +473,8 @@ def test_prefill_at_maximum_k(mnb):
     code tiles of a 256-column workgroup span 2^31 bytes less 16 KiB, so the
     last tile's code offsets come within 0.001% of the 32-bit limit, and the
     64 rows of A behind one buffer resource of the plain per-group path just
-    as close.  M = 128 in both tile heights (96: a full block and a partial
-    one; 128: one block), each on one column block (N = 256).  Rows are
+    as close.  M = 128 in each tile height (64: two blocks; 96: a full block
+    and a partial one; 128: one block), each on one column block (N = 256).  Rows are
     sparse (_sparse_row, the memory traffic is that of a dense row); rows 0,
     1, 95, 96 and 127 are checked against the oracle on the columns of the
     first and the last tile, and the two heights give the same bits
@@ -494,7 +494,7 @@ def test_prefill_at_maximum_k(mnb):
             kept[m] = r
     outs = {}
     try:
-        for bm in (96, 128):
+        for bm in (64, 96, 128):
             mnb.mnb_debug_prefill_rows(bm)
             y = t.empty((M, N), dtype=t.float16, device="cuda")
             G.gemm(q, a, M, y)
@@ -506,12 +506,13 @@ def test_prefill_at_maximum_k(mnb):
     del a
     t.cuda.empty_cache()
     assert np.array_equal(outs[96].view(np.uint16), outs[128].view(np.uint16))
+    assert np.array_equal(outs[96].view(np.uint16), outs[64].view(np.uint16))
     cols = np.r_[0:16, N - 16:N]
     A = np.stack([kept[m] for m in rows])
     ms = np.repeat(np.arange(len(rows)), len(cols))
     ns = np.tile(cols, len(rows))
     Y, B = o.matmul_nbits_at(A, w.packed, w.scales, w.zero_points, N, K, g, ms, ns)
-    for bm in (96, 128):
+    for bm in (64, 96, 128):
         G.assert_within(outs[bm][np.array(rows)[ms], ns], Y, B, "prefill (%d rows) at K=%d" % (bm, K))
 
 

@@ -34,7 +34,7 @@ N_PREFILL_CASES = 16
 
 
 def _draw_prefill(i):
-    """Prefill shapes with groups of 128 k, the ones both tile heights serve."""
+    """Prefill shapes with groups of 128 k, the ones every tile height serves."""
     rng = np.random.default_rng((510, i))
     g = 128
     K = g * int(rng.integers(1, 13))
@@ -58,19 +58,20 @@ def test_random_shape(mnb, i):
 
 
 @pytest.mark.parametrize("i", range(N_PREFILL_CASES))
-def test_random_prefill_shape_in_both_tile_heights(mnb, i):
-    """The prefill GEMM's two tile heights (96 and 128 rows, forced) on seeded
-    shapes with groups of 128 k: each within the bound against the oracle,
-    and the two bit for bit the same."""
+def test_random_prefill_shape_in_every_tile_height(mnb, i):
+    """The prefill GEMM's tile heights (64, 96 and 128 rows, forced) on
+    seeded shapes with groups of 128 k: each within the bound against the
+    oracle, and all bit for bit the same."""
     outs = []
     try:
-        for rows in (96, 128):
-            assert mnb.mnb_debug_prefill_rows(rows) in (0, 96, 128)
+        for rows in (64, 96, 128):
+            assert mnb.mnb_debug_prefill_rows(rows) in (0, 64, 96, 128)
             outs.append(_run_case(mnb, i, *_draw_prefill(i), seed=510))
     finally:
         mnb.mnb_debug_prefill_rows(0)
-    assert outs[0].dtype == outs[1].dtype
-    assert np.array_equal(outs[0].view(np.uint8), outs[1].view(np.uint8)), "case %d: the heights differ" % i
+    for o_ in outs[1:]:
+        assert o_.dtype == outs[0].dtype
+        assert np.array_equal(outs[0].view(np.uint8), o_.view(np.uint8)), "case %d: the heights differ" % i
 
 
 def _run_case(mnb, i, M, N, K, g, sdt, zp, kind, rng, seed):
