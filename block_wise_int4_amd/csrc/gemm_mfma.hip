@@ -17,13 +17,13 @@
 //   wave per SIMD, which measured twice as slow.
 // * Groups of 128 k also have a 128-row form (4 row blocks per wave): each
 //   unpacked B operand then feeds four MFMAs instead of three, and only two
-//   pipeline stages fit in the workgroup's half of the LDS; and a 64-row
-//   form, faster where every workgroup fits on the chip at once.  The
-//   launcher picks the height per call from the number of workgroup rounds
-//   each leaves on the chip's CUs, weighted by its cost (a 64-row workgroup
-//   about 0.82 times a 96-row one, a 128-row one about 1.23 times); all give
-//   the same bits, as every output adds the same products in the same
-//   order.
+//   pipeline stages fit in the workgroup's half of the LDS.  Groups of 128
+//   and 64 k also have a 64-row form, faster where every workgroup fits on
+//   the chip at once.  The launcher picks the height per call from the
+//   number of workgroup rounds each leaves on the chip's CUs, weighted by its
+//   cost (a 64-row workgroup about 0.82 times a 96-row one, a 128-row one
+//   about 1.23 times); all give the same bits, as every output adds the same
+//   products in the same order.
 // * A rows reach LDS by buffer_load ... lds (no VGPR round trip) into a ring
 //   of as many stages as the workgroup's share of LDS holds (three for the
 //   common record sizes); the DMAs of chunk c + stages - 1 are spread over the
@@ -894,21 +894,23 @@ int device_cus()
     return n;
 }
 
-// A fixed tile height for groups of 128 k (64, 96 or 128), or 0: per call.
+// A fixed tile height where the group size offers several (64, 96 or 128;
+// one the group size does not offer leaves the default), or 0: per call.
 std::atomic<int> g_prefill_rows{0};
 
-// Tile height for groups of 128 k: the one whose workgroup rounds, weighted
-// by its cost, are fewest.  A round here is one workgroup per CU (a CU holds
-// two; one alone runs faster).  Costs relative to a 96-row workgroup: 64
-// rows 18/22, 128 rows 27/22 (measured on MI355X at M = 32 .. 4096,
-// N = 14336, K = 4096).  Ties go to the taller tile.
-int pick_rows(const GemmParams& p)
+// Tile height for groups of 128 or 64 k: the one whose workgroup rounds,
+// weighted by its cost, are fewest (128 rows only for groups of 128 k).  A
+// round here is one workgroup per CU (a CU holds two; one alone runs
+// faster).  Costs relative to a 96-row workgroup: 64 rows 18/22, 128 rows
+// 27/22 (measured on MI355X at M = 32 .. 4096, N = 14336, K = 4096, groups
+// of 128 and 64 k).  Ties go to the taller tile.
+int pick_rows(const GemmParams& p, bool tall)
 {
     const int64_t cus = device_cus();
     auto cost = [&](int bm, int64_t w) { return w * ((((int64_t)p.M + bm - 1) / bm * p.num_n + cus - 1) / cus); };
-    int best = kTallBM;
-    int64_t c = cost(kTallBM, 27);
-    if (cost(kMaxBM, 22) < c) { best = kMaxBM; c = cost(kMaxBM, 22); }
+    int best = kMaxBM;
+    int64_t c = cost(kMaxBM, 22);
+    if (tall && cost(kTallBM, 27) <= c) { best = kTallBM; c = cost(kTallBM, 27); }
     if (cost(kShortBM, 18) < c) best = kShortBM;
     return best;
 }
@@ -916,10 +918,12 @@ int pick_rows(const GemmParams& p)
 template <typename ST, int Q, bool HAS_ZP, bool F32OUT>
 void launch_h(const GemmParams& p, hipStream_t s)
 {
-    if constexpr (Q == 1 && StageGeom<Q, (int)sizeof(ST), HAS_ZP, 0>::BM == kMaxBM) {
+    if constexpr (Q <= 2 && StageGeom<Q, (int)sizeof(ST), HAS_ZP, 0>::BM == kMaxBM) {
         int rows = g_prefill_rows.load(std::memory_order_relaxed);
-        if (rows == 0) rows = pick_rows(p);
-        if (rows == kTallBM) { launch_k<ST, Q, HAS_ZP, F32OUT, kTallBM>(p, s); return; }
+        if (rows == 0) rows = pick_rows(p, Q == 1);
+        if constexpr (Q == 1) {
+            if (rows == kTallBM) { launch_k<ST, Q, HAS_ZP, F32OUT, kTallBM>(p, s); return; }
+        }
         if (rows == kShortBM) { launch_k<ST, Q, HAS_ZP, F32OUT, kShortBM>(p, s); return; }
     }
     launch_k<ST, Q, HAS_ZP, F32OUT, 0>(p, s);

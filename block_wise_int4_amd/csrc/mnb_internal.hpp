@@ -60,9 +60,9 @@ hipError_t launch_gemm_small(const Layout& L, const WeightView& w, const void* a
 
 // M > 16, fp16 activations, K up to gemm_mfma_max_k().
 int64_t gemm_mfma_max_k();
-// Tile height of the prefill GEMM for groups of 128 k: 64, 96 or 128 for
-// every later call, 0 to choose per call; returns the previous value (-1:
-// invalid).
+// Tile height of the prefill GEMM where the group size offers several: 64,
+// 96 or 128 for every later call, 0 to choose per call; returns the
+// previous value (-1: invalid).
 int set_prefill_rows(int rows);
 hipError_t launch_gemm_mfma(const Layout& L, const WeightView& w, const void* a, int64_t m,
                             const Bias& bias, void* y, hipStream_t stream, const char** variant);

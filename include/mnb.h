@@ -352,11 +352,13 @@ mnb_status mnb_unpack_debug(const mnb_weight_desc* w, const void* repacked, uint
                             float* w_f32, void* stream);
 
 /* Test-only: the tile height of the prefill GEMM (M > 16) for groups of
- * 128 k.  rows = 0 (the default): chosen per call from the shape and the
- * device's compute units; 64, 96 or 128: that height for every later call in
- * the process, from any thread.  Returns the previous setting; any other
- * value changes nothing and returns -1.  All heights give bit-identical
- * results; this lets tests run each form at any size. */
+ * 128 or 64 k.  rows = 0 (the default): chosen per call from the shape and
+ * the device's compute units; 64, 96 or 128: that height for every later
+ * call in the process, from any thread (128 only for groups of 128 k; a
+ * height the group size does not offer leaves its default).  Returns the
+ * previous setting; any other value changes nothing and returns -1.  All
+ * heights give bit-identical results; this lets tests run each form at any
+ * size. */
 int32_t mnb_debug_prefill_rows(int32_t rows);
 
 /* Static string naming a status. */

@@ -31,9 +31,9 @@ def pytest_collection_modifyitems(config, items):
 
 @pytest.fixture(params=[0, 64, 128], ids=["rows-auto", "rows64", "rows128"])
 def prefill_rows(request):
-    """The prefill GEMM's tile height for groups of 128 k: chosen per call
-    (0), or the 64- or 128-row form forced, so that every shape runs each
-    form.  Reset to per-call choice afterwards."""
+    """The prefill GEMM's tile height: chosen per call (0), or the 64-row
+    (groups of 128 or 64 k) or 128-row form (groups of 128 k) forced, so that
+    every shape runs each form.  Reset to per-call choice afterwards."""
     from block_wise_int4_amd import mnb as m
     m.mnb_debug_prefill_rows(request.param)
     yield request.param

@@ -86,8 +86,13 @@ def assert_within(y: np.ndarray, Y: np.ndarray, B: np.ndarray, what: str, bound=
     return r
 
 
-def needs_tall_form(rows, g, M=None):
-    """Skip a forced tile height the case would not reach: the forced
-    heights serve the prefill GEMM (M > 16) with groups of 128 k."""
-    if rows and (g != 128 or (M is not None and M <= 16)):
-        pytest.skip("forced tile heights serve the prefill GEMM with groups of 128 k")
+def needs_forced_height(rows, g, M=None):
+    """Skip a forced tile height the case would not reach: forced heights
+    serve the prefill GEMM (M > 16), 64 rows with groups of 128 or 64 k, 128
+    rows with groups of 128 k."""
+    if not rows:
+        return
+    if M is not None and M <= 16:
+        pytest.skip("forced tile heights serve the prefill GEMM (M > 16)")
+    if (rows == 128 and g != 128) or (rows == 64 and g not in (64, 128)):
+        pytest.skip("the group size offers no %d-row form" % rows)

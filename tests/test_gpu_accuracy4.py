@@ -80,7 +80,7 @@ ACC4_CASES = [
 
 @pytest.mark.parametrize("M,N,K,g,sdt,zp,with_bias", ACC4_CASES)
 def test_accuracy4_parity(mnb, prefill_rows, M, N, K, g, sdt, zp, with_bias):
-    G.needs_tall_form(prefill_rows, g, M)
+    G.needs_forced_height(prefill_rows, g, M)
     w = _weight(N, K, g, sdt, zp, seed=M)
     A = synth.activation(M, K, "f32", 1.0, (310, M, K))
     bias = synth.activation(1, N, "f32", 1.0, (311, N)).reshape(N) if with_bias else None

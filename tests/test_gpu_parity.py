@@ -330,7 +330,7 @@ PREFILL_CASES = [(17, 70, 384, 128, True, "f16"), (130, 300, 512, 64, True, "f16
 
 @pytest.mark.parametrize("M,N,K,g,zp,sdt", PREFILL_CASES)
 def test_prefill_ragged_parity(mnb, prefill_rows, M, N, K, g, zp, sdt):
-    G.needs_tall_form(prefill_rows, g)
+    G.needs_forced_height(prefill_rows, g)
     t = G.torch()
     w = _weight(N, K, g, sdt, zp, lo=0.002, hi=0.01)
     A = _act(M, K, sigma=0.5)
@@ -424,7 +424,7 @@ def test_prefill_output_alignment_paths_agree(mnb, prefill_rows, g):
     into a Y shifted by one element (2-byte aligned only) gives the same bits,
     with and without a bias, and for the fp32 output of the int8-activation
     path (4-byte shift)."""
-    G.needs_tall_form(prefill_rows, g)
+    G.needs_forced_height(prefill_rows, g)
     t = G.torch()
     M, N, K = 200, 520, 512
     w = _weight(N, K, g, "f16", True, seed=31)
@@ -563,7 +563,7 @@ def test_bias_epilogue_parity(mnb, prefill_rows, M, N, K, g, adt, zp):
     two-operator path); fused mode is checked against Y + b (fp64) under the
     accumulator's bound plus one fp32 add and one fp16 rounding; a zero bias
     changes nothing.  fp32 outputs add once in both modes."""
-    G.needs_tall_form(prefill_rows, g, M)
+    G.needs_forced_height(prefill_rows, g, M)
     t = G.torch()
     w = _weight(N, K, g, "f16", zp, seed=M)
     A = _act(M, K, adt, seed=M + 1)
@@ -631,7 +631,7 @@ def test_act_order_parity(mnb, prefill_rows, M, N, K, g, adt, zp):
     the repack in permuted order and the GEMM on permuted activation columns,
     against the oracle's act-order dequant (scale and zero point of group
     g_idx[k]) and fp64 matmul, on every path."""
-    G.needs_tall_form(prefill_rows, g, M)
+    G.needs_forced_height(prefill_rows, g, M)
     t = G.torch()
     w = _weight(N, K, g, "f16", zp, seed=M + 3)
     rng = np.random.default_rng(M * 31 + K)
@@ -899,7 +899,7 @@ def test_f32_activations_gemm_parity(mnb, prefill_rows, M, N, K, g, sdt, zp):
     and scaled back in fp32.  Against the oracle on the fp32 values (exact in
     fp64), with huge, tiny, subnormal, NaN and infinite rows, and with an fp32
     bias vector and a per-row bias."""
-    G.needs_tall_form(prefill_rows, g, 2 * M)
+    G.needs_forced_height(prefill_rows, g, 2 * M)
     t = G.torch()
     w = _weight(N, K, g, sdt, zp, seed=M + 21)
     q = G.upload(w)
@@ -976,7 +976,7 @@ def test_extreme_scale_ranges(mnb, prefill_rows, K, g):
     accumulator for tiles in its range class (recorded by the repack, checked
     here against the host model) and computes the other tiles with fresh
     partials.  Outputs within the bound everywhere."""
-    G.needs_tall_form(prefill_rows, g)
+    G.needs_forced_height(prefill_rows, g)
     t = G.torch()
     N = 96
     kb = K // g
@@ -1000,7 +1000,7 @@ def test_extreme_scale_ranges(mnb, prefill_rows, K, g):
 def test_extreme_scale_ranges_int8_activations(mnb, prefill_rows, K, g):
     """The same extreme scales, plus a 1e30 scale beside a 1e-30 one, through
     the int8-activation product (fp32 outputs hold the large values)."""
-    G.needs_tall_form(prefill_rows, g)
+    G.needs_forced_height(prefill_rows, g)
     t = G.torch()
     N = 96
     kb = K // g

@@ -34,9 +34,10 @@ N_PREFILL_CASES = 16
 
 
 def _draw_prefill(i):
-    """Prefill shapes with groups of 128 k, the ones every tile height serves."""
+    """Prefill shapes with groups of 128 or 64 k, the ones with several tile
+    heights."""
     rng = np.random.default_rng((510, i))
-    g = 128
+    g = int(rng.choice([64, 128]))
     K = g * int(rng.integers(1, 13))
     N = int(rng.integers(1, 400))
     M = int(rng.integers(17, 300))
@@ -59,9 +60,9 @@ def test_random_shape(mnb, i):
 
 @pytest.mark.parametrize("i", range(N_PREFILL_CASES))
 def test_random_prefill_shape_in_every_tile_height(mnb, i):
-    """The prefill GEMM's tile heights (64, 96 and 128 rows, forced) on
-    seeded shapes with groups of 128 k: each within the bound against the
-    oracle, and all bit for bit the same."""
+    """The prefill GEMM's tile heights (64, 96 and 128 rows, forced; 128 only
+    for groups of 128 k) on seeded shapes with groups of 128 or 64 k: each
+    within the bound against the oracle, and all bit for bit the same."""
     outs = []
     try:
         for rows in (64, 96, 128):
