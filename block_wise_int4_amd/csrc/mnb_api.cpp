@@ -303,15 +303,22 @@ size_t mnb_gemm_workspace_bytes_for(const mnb_weight_desc* w, int64_t m, int32_t
     return workspace_for(L, m, a_dtype);
 }
 
-// M > 16 runs the prefill GEMM, whose buffer offsets are 32-bit.
-static mnb_status check_gemm_k(const Layout& L, int64_t m)
+// fp16 activations with 16 < M <= kSliceMaxM run the small-M kernel on
+// 16-row slices, one launch each: above 16 rows the prefill GEMM's grid
+// covers too few CUs at these heights (N = 14336, K = 4096: 35-40 us at
+// M = 17..32 against 16.3-17.4 us in two slices, about 25 us in three).
+constexpr int64_t kSliceMaxM = 48;
+
+// rows (2..small_max) run the small-M kernel, more the prefill GEMM; both
+// have 32-bit buffer offsets.
+static mnb_status check_gemm_k(const Layout& L, int64_t rows, int64_t small_max)
 {
-    if (m >= 2 && m <= 16 && L.K > mnb::gemm_small_max_k())
-        return fail(MNB_ERR_UNSUPPORTED, "K=%lld exceeds the small-M GEMM limit %lld (2 <= M <= 16)",
-                    (long long)L.K, (long long)mnb::gemm_small_max_k());
-    if (m > 16 && L.K > mnb::gemm_mfma_max_k())
-        return fail(MNB_ERR_UNSUPPORTED, "K=%lld exceeds the prefill GEMM limit %lld (M > 16)", (long long)L.K,
-                    (long long)mnb::gemm_mfma_max_k());
+    if (rows >= 2 && rows <= small_max && L.K > mnb::gemm_small_max_k())
+        return fail(MNB_ERR_UNSUPPORTED, "K=%lld exceeds the small-M GEMM limit %lld (2 <= M <= %lld)",
+                    (long long)L.K, (long long)mnb::gemm_small_max_k(), (long long)small_max);
+    if (rows > small_max && L.K > mnb::gemm_mfma_max_k())
+        return fail(MNB_ERR_UNSUPPORTED, "K=%lld exceeds the prefill GEMM limit %lld (M > %lld)", (long long)L.K,
+                    (long long)mnb::gemm_mfma_max_k(), (long long)small_max);
     return MNB_OK;
 }
 
@@ -325,7 +332,7 @@ static mnb_status gemm_f32_rows(const mnb_weight_desc* w, const Layout& L, const
     if (m > INT64_MAX / 8 / L.K) return fail(MNB_ERR_INVALID_ARGUMENT, "M*K overflows");
     if (2 * m > INT32_MAX) return fail(MNB_ERR_INVALID_ARGUMENT, "2M must fit in 32 bits");
     if (L.N == 0) return ok("noop");
-    MNB_TRY(check_gemm_k(L, 2 * m));
+    MNB_TRY(check_gemm_k(L, 2 * m, 16));
     const size_t need = workspace_for(L, m, MNB_F32);
     if (workspace_bytes < need)
         return fail(MNB_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed (fp32 activations, "
@@ -366,7 +373,7 @@ static mnb_status gemm_common(const mnb_weight_desc* w, const void* repacked, co
     if (m > 1 && a_dtype == MNB_F32) return gemm_f32_rows(w, L, repacked, a, m, bias, y, workspace, workspace_bytes, stream);
     const size_t need = workspace_for(L, m);
     if (m == 0 || L.N == 0) return ok("noop");
-    MNB_TRY(check_gemm_k(L, m));
+    MNB_TRY(check_gemm_k(L, m, kSliceMaxM));
     if (workspace_bytes < need)
         return fail(MNB_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed",
                     workspace_bytes, need);
@@ -379,10 +386,20 @@ static mnb_status gemm_common(const mnb_weight_desc* w, const void* repacked, co
     const mnb::WeightView v = mnb::view_of(L, repacked);
     const char* variant = "";
     hipError_t e;
-    if (m <= 16)
-        e = mnb::launch_gemm_small(L, v, a, m, bias, y, workspace, static_cast<hipStream_t>(stream), &variant);
-    else
+    if (m <= kSliceMaxM) {
+        // 16-row slices of A, Y and a per-row bias, one small-M launch each
+        // (the small-M kernel needs no workspace)
+        e = hipSuccess;
+        for (int64_t r0 = 0; r0 < m && e == hipSuccess; r0 += 16) {
+            mnb::Bias b = bias;
+            if (b.ptr && b.row_stride) b.ptr = static_cast<const uint16_t*>(b.ptr) + r0 * b.row_stride;
+            e = mnb::launch_gemm_small(L, v, static_cast<const uint16_t*>(a) + r0 * L.K, m - r0 < 16 ? m - r0 : 16, b,
+                                       static_cast<uint16_t*>(y) + r0 * L.N, workspace,
+                                       static_cast<hipStream_t>(stream), &variant);
+        }
+    } else {
         e = mnb::launch_gemm_mfma(L, v, a, m, bias, y, static_cast<hipStream_t>(stream), &variant);
+    }
     return launched(e, variant);
 }
 
@@ -442,7 +459,7 @@ mnb_status mnb_gemm_act_order(const mnb_weight_desc* w, const void* repacked, co
     if (m == 0 || L.N == 0) return ok("noop");
     if (m > INT32_MAX) return fail(MNB_ERR_INVALID_ARGUMENT, "M must fit in 32 bits");
     if (L.K > 0 && m > INT64_MAX / 16 / L.K) return fail(MNB_ERR_INVALID_ARGUMENT, "M*K overflows");
-    MNB_TRY(check_gemm_k(L, a_dtype == MNB_F32 ? 2 * m : m));
+    MNB_TRY(check_gemm_k(L, a_dtype == MNB_F32 ? 2 * m : m, a_dtype == MNB_F32 ? 16 : kSliceMaxM));
     const size_t a_bytes = act_order_a_bytes(L, m, a_dtype);
     const size_t need = a_bytes + workspace_for(L, m, a_dtype);
     if (workspace_bytes < need)
@@ -533,7 +550,7 @@ static mnb_status accuracy4_common(const mnb_weight_desc* w, const void* repacke
     if (m == 1 && L.K > mnb::acc4_gemv_max_k())
         return fail(MNB_ERR_UNSUPPORTED, "K=%lld exceeds the int8-activation decode limit %lld",
                     (long long)L.K, (long long)mnb::acc4_gemv_max_k());
-    MNB_TRY(check_gemm_k(L, m));
+    MNB_TRY(check_gemm_k(L, m, 16));
     const size_t need = acc4_scale_bytes(m) + acc4_codes_bytes(L, m) + workspace_for(L, m);
     // the decode GEMV needs no workspace; given one, it receives the codes
     if ((m > 1 || workspace) && workspace_bytes < need)

@@ -186,7 +186,8 @@ size_t mnb_gemm_workspace_bytes_for(const mnb_weight_desc* w, int64_t m, int32_t
  * A (device, [M,K]) and Y (device, [M,N]) of a_dtype.  M = 1 runs the decode
  * GEMV (its K limit applies); 2 <= M <= 16 a weight-streaming MFMA kernel
  * whose workgroups split K among their waves and reduce in a fixed order,
- * for K <= 33554432 (its 32-bit buffer ranges; else MNB_ERR_UNSUPPORTED);
+ * for K <= 33554432 (its 32-bit buffer ranges; else MNB_ERR_UNSUPPORTED),
+ * and with fp16 A the same kernel up to M = 48, once per 16-row slice;
  * larger M the MFMA prefill GEMM, for K <= 16777088 (its 32-bit buffer
  * offsets; else MNB_ERR_UNSUPPORTED).  Products are fp16 x fp16 on the
  * matrix cores with fp32 accumulation; each group's partial sum is

@@ -294,7 +294,11 @@ SMALL_CASES = [(2, 70, 384, 128, True), (3, 130, 160, 32, True), (7, 33, 4096, 6
                # M ending inside a row quad
                (6, 100, 192, 64, True), (13, 40, 320, 64, False),
                # several batches per wave (65 chunks) and a ragged last chunk
-               (4, 48, 8256, 64, True)]
+               (4, 48, 8256, 64, True),
+               # 16 < M <= 48 (fp16 A): one launch per 16-row slice, the last
+               # ragged; every group size
+               (17, 70, 384, 128, True), (32, 257, 512, 64, False), (33, 40, 160, 16, True),
+               (48, 300, 640, 32, True), (41, 16, 8256, 64, False)]
 
 
 @pytest.mark.parametrize("M,N,K,g,zp", SMALL_CASES)
@@ -307,21 +311,22 @@ def test_small_m_ragged_parity(mnb, M, N, K, g, zp):
     ws_n = mnb.mnb_gemm_workspace_bytes(q.desc, M)
     ws = t.empty(max(ws_n, 16), dtype=t.uint8, device="cuda")
     mnb.mnb_gemm(q.desc, q.repacked, G.to_dev(A), M, y, ws, ws_n)
+    assert mnb.mnb_last_variant() == "gemm_small_m"
     Y, B, _ = G.oracle_dense(A, w)
     G.assert_within(G.host(y), Y, B, "small-M M=%d N=%d K=%d g=%d" % (M, N, K, g))
 
 
 # --------------------------------------------------------------- prefill ----
 
-PREFILL_CASES = [(17, 70, 384, 128, True, "f16"), (130, 300, 512, 64, True, "f16"),
-                 (64, 257, 256, 32, False, "f32"), (33, 40, 160, 16, True, "f16"),
+PREFILL_CASES = [(49, 70, 384, 128, True, "f16"), (130, 300, 512, 64, True, "f16"),
+                 (64, 257, 256, 32, False, "f32"), (57, 40, 160, 16, True, "f16"),
                  (300, 512, 1024, 128, False, "f16"), (129, 16, 4096, 128, True, "f16"),
                  # 64-row tiles: groups of 32 or 16 k, and fp32 scales with
                  # zero points at 64 k; several row blocks and a ragged one
                  (200, 300, 1024, 32, True, "f16"), (65, 64, 256, 32, False, "f16"),
                  (150, 130, 640, 64, True, "f32"), (130, 96, 512, 16, True, "f32"),
                  # one chunk (every later DMA of the pipeline is for a chunk past K)
-                 (40, 48, 64, 32, True, "f16"), (24, 80, 128, 128, False, "f32"),
+                 (70, 48, 64, 32, True, "f16"), (88, 80, 128, 128, False, "f32"),
                  # groups of 128 k with ragged row blocks of either height and a
                  # ragged column block
                  (200, 300, 512, 128, True, "f16"), (129, 48, 256, 128, False, "f32"),

@@ -40,7 +40,7 @@ def _draw_prefill(i):
     g = int(rng.choice([64, 128]))
     K = g * int(rng.integers(1, 13))
     N = int(rng.integers(1, 400))
-    M = int(rng.integers(17, 300))
+    M = int(rng.integers(49, 300))
     sdt = str(rng.choice(["f16", "f32"]))
     zp = bool(rng.integers(0, 2))
     kind = str(rng.choice(["plain", "bias", "act_order", "accuracy4"]))
