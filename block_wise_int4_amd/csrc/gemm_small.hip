@@ -396,12 +396,14 @@ __global__ __launch_bounds__(kWaves * 64) void gemm_small_kernel(
                         const h8_t b = make_b(q);
                         // group 16: a 32-k step spans groups 2j (octets 0,1) and
                         // 2j+1 (octets 2,3); one MFMA per group with the other
-                        // group's octets zeroed
+                        // group's activation octets zeroed (not its weights:
+                        // an infinite activation times a zeroed weight would
+                        // put a NaN into the other group)
                         const h8_t zero = zero_h8();
-                        const h8_t be = (h < 2) ? b : zero;
-                        const h8_t bo = (h < 2) ? zero : b;
-                        const f4_t ge = mfma16(afr[u][j], be, f4_t{0.f, 0.f, 0.f, 0.f});
-                        const f4_t go = mfma16(afr[u][j], bo, f4_t{0.f, 0.f, 0.f, 0.f});
+                        const h8_t ae = (h < 2) ? afr[u][j] : zero;
+                        const h8_t ao = (h < 2) ? zero : afr[u][j];
+                        const f4_t ge = mfma16(ae, b, f4_t{0.f, 0.f, 0.f, 0.f});
+                        const f4_t go = mfma16(ao, b, f4_t{0.f, 0.f, 0.f, 0.f});
                         const float se = raw_scale<ST, NS>(sr[u][tt][0], j);
                         const float so = raw_scale<ST, NS>(sr[u][tt][NL - 1], j);
 #pragma unroll

@@ -223,14 +223,17 @@ __device__ __forceinline__ float chunk_dot_f16(const ChunkRegs<ST, Q, HAS_ZP>& r
         const h8_t a = *reinterpret_cast<const h8_t*>(as + c * kChunkK + 32 * j + 8 * h);
         {
             // group 16: octets 0,1 of the step are group 2j, octets 2,3 group
-            // 2j+1.  A lane's scale vector holds the groups of its own octet
-            // half (h >> 1), so the other half's scale comes from the lane 32
-            // positions away.
+            // 2j+1; one MFMA per group with the other group's activation
+            // octets zeroed (not its weights: an infinite activation times a
+            // zeroed weight would put a NaN into the other group).  A lane's
+            // scale vector holds the groups of its own octet half (h >> 1),
+            // so the other half's scale comes from the lane 32 positions
+            // away.
             h8_t zh;
 #pragma unroll
             for (int e = 0; e < 8; ++e) zh[e] = (_Float16)0.0f;
-            const f4_t ge = mfma16(a, (h < 2) ? b : zh, zero);
-            const f4_t go = mfma16(a, (h < 2) ? zh : b, zero);
+            const f4_t ge = mfma16((h < 2) ? a : zh, b, zero);
+            const f4_t go = mfma16((h < 2) ? zh : a, b, zero);
             const float s_own = scale_at<ST, NS>(r.s, sj);
             const float s_other = __shfl_xor(s_own, 32);
             const float se = (h < 2) ? s_own : s_other;

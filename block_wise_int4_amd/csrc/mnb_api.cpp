@@ -263,9 +263,16 @@ mnb_status mnb_gemv_gate_up_swiglu(const mnb_weight_desc* w, const void* gate_re
     return gemv_common(w, gate_repacked, up_repacked, a, a_dtype, mnb::Bias(), y, stream);
 }
 
+// Up to kSliceMaxM fp16 rows (M for fp16 and int8 activations, 2M for fp32
+// ones) run the small-M kernel, once per slice of at most 16 rows: above 16
+// rows the prefill GEMM's grid covers too few CUs at these heights
+// (N = 14336, K = 4096: 35-40 us at M = 17..32 against 16.3-17.4 us in two
+// slices, about 25 us in three).  More rows run the prefill GEMM.
+constexpr int64_t kSliceMaxM = 48;
+
 static size_t workspace_for(const Layout& L, int64_t m)
 {
-    if (m >= 2 && m <= 16) return mnb::gemm_small_workspace(L, m);
+    if (m >= 2 && m <= kSliceMaxM) return mnb::gemm_small_workspace(L, m < 16 ? m : 16);
     return 0;
 }
 
@@ -303,22 +310,16 @@ size_t mnb_gemm_workspace_bytes_for(const mnb_weight_desc* w, int64_t m, int32_t
     return workspace_for(L, m, a_dtype);
 }
 
-// fp16 activations with 16 < M <= kSliceMaxM run the small-M kernel on
-// 16-row slices, one launch each: above 16 rows the prefill GEMM's grid
-// covers too few CUs at these heights (N = 14336, K = 4096: 35-40 us at
-// M = 17..32 against 16.3-17.4 us in two slices, about 25 us in three).
-constexpr int64_t kSliceMaxM = 48;
 
-// rows (2..small_max) run the small-M kernel, more the prefill GEMM; both
-// have 32-bit buffer offsets.
-static mnb_status check_gemm_k(const Layout& L, int64_t rows, int64_t small_max)
+// Both GEMMs have 32-bit buffer offsets.
+static mnb_status check_gemm_k(const Layout& L, int64_t rows)
 {
-    if (rows >= 2 && rows <= small_max && L.K > mnb::gemm_small_max_k())
-        return fail(MNB_ERR_UNSUPPORTED, "K=%lld exceeds the small-M GEMM limit %lld (2 <= M <= %lld)",
-                    (long long)L.K, (long long)mnb::gemm_small_max_k(), (long long)small_max);
-    if (rows > small_max && L.K > mnb::gemm_mfma_max_k())
-        return fail(MNB_ERR_UNSUPPORTED, "K=%lld exceeds the prefill GEMM limit %lld (M > %lld)", (long long)L.K,
-                    (long long)mnb::gemm_mfma_max_k(), (long long)small_max);
+    if (rows >= 2 && rows <= kSliceMaxM && L.K > mnb::gemm_small_max_k())
+        return fail(MNB_ERR_UNSUPPORTED, "K=%lld exceeds the small-M GEMM limit %lld (2 <= rows <= %lld)",
+                    (long long)L.K, (long long)mnb::gemm_small_max_k(), (long long)kSliceMaxM);
+    if (rows > kSliceMaxM && L.K > mnb::gemm_mfma_max_k())
+        return fail(MNB_ERR_UNSUPPORTED, "K=%lld exceeds the prefill GEMM limit %lld (rows > %lld)", (long long)L.K,
+                    (long long)mnb::gemm_mfma_max_k(), (long long)kSliceMaxM);
     return MNB_OK;
 }
 
@@ -332,7 +333,7 @@ static mnb_status gemm_f32_rows(const mnb_weight_desc* w, const Layout& L, const
     if (m > INT64_MAX / 8 / L.K) return fail(MNB_ERR_INVALID_ARGUMENT, "M*K overflows");
     if (2 * m > INT32_MAX) return fail(MNB_ERR_INVALID_ARGUMENT, "2M must fit in 32 bits");
     if (L.N == 0) return ok("noop");
-    MNB_TRY(check_gemm_k(L, 2 * m, 16));
+    MNB_TRY(check_gemm_k(L, 2 * m));
     const size_t need = workspace_for(L, m, MNB_F32);
     if (workspace_bytes < need)
         return fail(MNB_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed (fp32 activations, "
@@ -352,10 +353,18 @@ static mnb_status gemm_f32_rows(const mnb_weight_desc* w, const Layout& L, const
     if (e != hipSuccess) return launched(e, "f32_split");
     const char* variant = "";
     const float* b = static_cast<const float*>(bias.ptr);
-    if (2 * m <= 16)
-        e = mnb::launch_gemm_small_f32(L, v, hl, 2 * m, rs, b, static_cast<float*>(y),
-                                       ws + f32_scale_bytes(m) + f32_rows_bytes(L, m), s, &variant, 1, bias.row_stride);
-    else
+    if (2 * m <= kSliceMaxM) {
+        // slices of 8 rows: their 16 (hi, lo) fp16 rows, row scales, outputs
+        // and per-row bias
+        e = hipSuccess;
+        for (int64_t r0 = 0; r0 < m && e == hipSuccess; r0 += 8) {
+            const int64_t rows = m - r0 < 8 ? m - r0 : 8;
+            e = mnb::launch_gemm_small_f32(L, v, hl + 2 * r0 * L.K, 2 * rows, rs + r0, b ? b + r0 * bias.row_stride : b,
+                                           static_cast<float*>(y) + r0 * L.N,
+                                           ws + f32_scale_bytes(m) + f32_rows_bytes(L, m), s, &variant, 1,
+                                           bias.row_stride);
+        }
+    } else
         e = mnb::launch_gemm_mfma_f32(L, v, hl, 2 * m, rs, b, static_cast<float*>(y), s, &variant, 1, bias.row_stride);
     return launched(e, variant);
 }
@@ -373,7 +382,7 @@ static mnb_status gemm_common(const mnb_weight_desc* w, const void* repacked, co
     if (m > 1 && a_dtype == MNB_F32) return gemm_f32_rows(w, L, repacked, a, m, bias, y, workspace, workspace_bytes, stream);
     const size_t need = workspace_for(L, m);
     if (m == 0 || L.N == 0) return ok("noop");
-    MNB_TRY(check_gemm_k(L, m, kSliceMaxM));
+    MNB_TRY(check_gemm_k(L, m));
     if (workspace_bytes < need)
         return fail(MNB_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed",
                     workspace_bytes, need);
@@ -459,7 +468,7 @@ mnb_status mnb_gemm_act_order(const mnb_weight_desc* w, const void* repacked, co
     if (m == 0 || L.N == 0) return ok("noop");
     if (m > INT32_MAX) return fail(MNB_ERR_INVALID_ARGUMENT, "M must fit in 32 bits");
     if (L.K > 0 && m > INT64_MAX / 16 / L.K) return fail(MNB_ERR_INVALID_ARGUMENT, "M*K overflows");
-    MNB_TRY(check_gemm_k(L, a_dtype == MNB_F32 ? 2 * m : m, a_dtype == MNB_F32 ? 16 : kSliceMaxM));
+    MNB_TRY(check_gemm_k(L, a_dtype == MNB_F32 ? 2 * m : m));
     const size_t a_bytes = act_order_a_bytes(L, m, a_dtype);
     const size_t need = a_bytes + workspace_for(L, m, a_dtype);
     if (workspace_bytes < need)
@@ -550,7 +559,7 @@ static mnb_status accuracy4_common(const mnb_weight_desc* w, const void* repacke
     if (m == 1 && L.K > mnb::acc4_gemv_max_k())
         return fail(MNB_ERR_UNSUPPORTED, "K=%lld exceeds the int8-activation decode limit %lld",
                     (long long)L.K, (long long)mnb::acc4_gemv_max_k());
-    MNB_TRY(check_gemm_k(L, m, 16));
+    MNB_TRY(check_gemm_k(L, m));
     const size_t need = acc4_scale_bytes(m) + acc4_codes_bytes(L, m) + workspace_for(L, m);
     // the decode GEMV needs no workspace; given one, it receives the codes
     if ((m > 1 || workspace) && workspace_bytes < need)
@@ -571,10 +580,12 @@ static mnb_status accuracy4_common(const mnb_weight_desc* w, const void* repacke
     if (m == 1) return launched(mnb::launch_acc4_gemv(L, v, a, bias, y, q, sc, s, &variant), variant);
     hipError_t e = mnb::launch_acc4_quantize(a, m, L.K, q, sc, s);
     if (e != hipSuccess) return launched(e, "accuracy4_quantize");
-    if (m <= 16)
-        e = mnb::launch_gemm_small_f32(L, v, q, m, sc, bias, y, ws + acc4_scale_bytes(m) + acc4_codes_bytes(L, m),
-                                       s, &variant);
-    else
+    if (m <= kSliceMaxM) {
+        // slices of 16 rows: their codes, row scales and outputs
+        for (int64_t r0 = 0; r0 < m && e == hipSuccess; r0 += 16)
+            e = mnb::launch_gemm_small_f32(L, v, q + r0 * L.K, m - r0 < 16 ? m - r0 : 16, sc + r0, bias, y + r0 * L.N,
+                                           ws + acc4_scale_bytes(m) + acc4_codes_bytes(L, m), s, &variant);
+    } else
         e = mnb::launch_gemm_mfma_f32(L, v, q, m, sc, bias, y, s, &variant);
     return launched(e, variant);
 }

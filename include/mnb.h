@@ -187,7 +187,8 @@ size_t mnb_gemm_workspace_bytes_for(const mnb_weight_desc* w, int64_t m, int32_t
  * GEMV (its K limit applies); 2 <= M <= 16 a weight-streaming MFMA kernel
  * whose workgroups split K among their waves and reduce in a fixed order,
  * for K <= 33554432 (its 32-bit buffer ranges; else MNB_ERR_UNSUPPORTED),
- * and with fp16 A the same kernel up to M = 48, once per 16-row slice;
+ * and the same kernel up to 48 fp16 rows (M with fp16 A), once per slice
+ * of at most 16 rows;
  * larger M the MFMA prefill GEMM, for K <= 16777088 (its 32-bit buffer
  * offsets; else MNB_ERR_UNSUPPORTED).  Products are fp16 x fp16 on the
  * matrix cores with fp32 accumulation; each group's partial sum is
@@ -196,8 +197,8 @@ size_t mnb_gemm_workspace_bytes_for(const mnb_weight_desc* w, int64_t m, int32_t
  * any M): each row m is scaled by a power of two 2^-e_m that puts its largest
  * finite magnitude in [2^14, 2^15) and written as two fp16 rows, hi =
  * fp16(a 2^-e_m) and lo = fp16(a 2^-e_m - hi); the fp16 GEMM runs on the 2M
- * rows (the small-M kernel for 2M <= 16, else the prefill kernel, whose K
- * limit then applies) and y[m,n] = 2^e_m * (acc[2m,n] + acc[2m+1,n]) in fp32.
+ * rows (the small-M kernel for 2M <= 48, in slices of 8 rows of A, else
+ * the prefill kernel, whose K limit then applies) and y[m,n] = 2^e_m * (acc[2m,n] + acc[2m+1,n]) in fp32.
  * The split errs by at most 2^-22 |a| + 2^-39 max|a| per element; NaN and
  * infinities pass whole.  `workspace` (device) must hold
  * mnb_gemm_workspace_bytes_for(w, m, a_dtype) bytes: none for fp16 (it may be

@@ -189,20 +189,23 @@ def test_prefill_k_limit():
                                            None, 0, None)
     assert "prefill GEMM limit" in _expect(U, lib.mnb_gemm_act_order, D(over), FAKE, FAKE, 49, 1, FAKE, FAKE,
                                            FAKE, 1 << 40, None)
-    # fp32 A (2M fp16 rows) and int8 activations leave the small-M kernel above 16 rows
-    assert "prefill GEMM limit" in _expect(U, lib.mnb_gemm, D(over), FAKE, FAKE, 9, mnb.MNB_F32, FAKE, FAKE,
+    # fp32 A (2M fp16 rows) leaves the small-M kernel above 48 fp16 rows
+    for m in (8, 24):
+        assert lib.mnb_gemm(D(over), FAKE, FAKE, m, mnb.MNB_F32, FAKE, FAKE, 1 << 40, None) == DEV
+    assert "prefill GEMM limit" in _expect(U, lib.mnb_gemm, D(over), FAKE, FAKE, 25, mnb.MNB_F32, FAKE, FAKE,
                                            1 << 40, None)
     over32 = mnb.desc(16, k_ok + 128, 128, False, mnb.MNB_F32)
-    assert "prefill GEMM limit" in _expect(U, lib.mnb_gemm_accuracy4, D(over32), FAKE, FAKE, 17, None, FAKE,
+    assert "prefill GEMM limit" in _expect(U, lib.mnb_gemm_accuracy4, D(over32), FAKE, FAKE, 49, None, FAKE,
                                            FAKE, 1 << 40, None)
+    assert lib.mnb_gemm_accuracy4(D(over32), FAKE, FAKE, 48, None, FAKE, FAKE, 1 << 40, None) == DEV
 
 
 def test_small_m_k_limit():
-    """2 <= M <= 16 (fp16 A: up to 48, in 16-row slices) runs the small-M
-    kernel, whose buffer ranges are 32-bit: K up to 2^25 is accepted (without
-    a device the call then stops at the device check), one group more is
-    refused before anything is enqueued, also for fp32 activations (2M fp16
-    rows) and int8 activations."""
+    """Up to 48 fp16 rows (M for fp16 and int8 activations, 2M for fp32 ones)
+    run the small-M kernel in slices of 16 rows, whose buffer ranges are
+    32-bit: K up to 2^25 is accepted (without a device the call then stops at
+    the device check), one group more is refused before anything is
+    enqueued."""
     lib = mnb.lib
     U, DEV = mnb.MNB_ERR_UNSUPPORTED, mnb.MNB_ERR_DEVICE
     k_ok = 1 << 25
@@ -210,11 +213,13 @@ def test_small_m_k_limit():
     for m in (2, 16, 17, 48):
         assert lib.mnb_gemm(D(ok), FAKE, FAKE, m, 1, FAKE, None, 0, None) == DEV
         assert "small-M GEMM limit" in _expect(U, lib.mnb_gemm, D(over), FAKE, FAKE, m, 1, FAKE, None, 0, None)
-    assert "small-M GEMM limit" in _expect(U, lib.mnb_gemm, D(over), FAKE, FAKE, 8, mnb.MNB_F32, FAKE, FAKE,
-                                           1 << 40, None)
+    for m in (8, 24):
+        assert "small-M GEMM limit" in _expect(U, lib.mnb_gemm, D(over), FAKE, FAKE, m, mnb.MNB_F32, FAKE, FAKE,
+                                               1 << 40, None)
     over32 = mnb.desc(16, k_ok + 128, 128, False, mnb.MNB_F32)
-    assert "small-M GEMM limit" in _expect(U, lib.mnb_gemm_accuracy4, D(over32), FAKE, FAKE, 4, None, FAKE,
-                                           FAKE, 1 << 40, None)
+    for m in (4, 48):
+        assert "small-M GEMM limit" in _expect(U, lib.mnb_gemm_accuracy4, D(over32), FAKE, FAKE, m, None, FAKE,
+                                               FAKE, 1 << 40, None)
 
 
 def test_bias_argument_validation():

@@ -68,6 +68,8 @@ ACC4_CASES = [
     (16, 100, 1024, 16, "f32", True, True),
     (40, 300, 512, 64, "f32", True, True), (130, 70, 384, 128, "f16", False, False),
     (200, 513, 1024, 32, "f32", True, True), (260, 300, 512, 128, "f32", True, True),
+    # 16 < M <= 48: the small-M kernel on 16-row slices (the last ragged)
+    (48, 96, 640, 32, "f16", True, True), (17, 130, 384, 128, "f32", False, True),
     # the prefill's 64-row tiles (groups of 32 or 16 k, fp32 scales with zero
     # points at 64 k) with 16-byte fp32 row stores (N % 4 == 0), ragged M
     (150, 256, 1024, 32, "f32", True, True), (97, 260, 512, 16, "f16", False, False),
@@ -85,7 +87,7 @@ def test_accuracy4_parity(mnb, prefill_rows, M, N, K, g, sdt, zp, with_bias):
     A = synth.activation(M, K, "f32", 1.0, (310, M, K))
     bias = synth.activation(1, N, "f32", 1.0, (311, N)).reshape(N) if with_bias else None
     y, variant = _check(mnb, w, A, bias, "accuracy4 M=%d N=%d K=%d g=%d %s zp=%s" % (M, N, K, g, sdt, zp))
-    expect = "gemv_accuracy4_i8" if M == 1 else ("gemm_small_m_accuracy4" if M <= 16
+    expect = "gemv_accuracy4_i8" if M == 1 else ("gemm_small_m_accuracy4" if M <= 48
                                                  else "gemm_mfma_32x32x16_accuracy4")
     assert variant == expect
 

@@ -827,8 +827,12 @@ def test_code_equal_to_zero_point_gives_zero(mnb):
 
 
 def test_nan_and_inf_propagate(mnb):
+    """A NaN and an infinite activation on every path (GEMV, small M, its
+    16-row slices, prefill), also with groups of 16 k, where one 32-k MFMA
+    step holds two groups: the infinity reaches only its own group's weight."""
     t = G.torch()
-    for (M, N, K, g) in ((1, 40, 256, 32), (3, 40, 256, 32), (20, 40, 256, 32)):
+    for (M, N, K, g) in ((1, 40, 256, 32), (3, 40, 256, 32), (20, 40, 256, 32), (1, 40, 256, 16),
+                         (3, 40, 256, 16), (20, 40, 256, 16), (60, 40, 256, 16)):
         w = _weight(N, K, g)
         A = _act(M, K)
         A[0, 7] = np.nan
@@ -878,7 +882,9 @@ F32_CASES = [
     (2, 200, 512, 32, "f16", True), (5, 257, 896, 64, "f32", False), (8, 130, 384, 128, "f16", True),
     (9, 96, 1024, 16, "f16", True), (16, 300, 512, 64, "f32", True), (40, 513, 1024, 32, "f16", True),
     (200, 300, 384, 128, "f16", False), (33, 70, 400, 16, "f32", True), (3, 70, 352, 32, "f16", True),
-    (70, 256, 512, 32, "f16", True)]
+    (70, 256, 512, 32, "f16", True),
+    # 2M <= 48: the small-M kernel on slices of 8 rows (16 fp16 rows), the last ragged
+    (24, 130, 384, 128, "f16", False), (13, 257, 640, 64, "f32", True)]
 
 
 def _f32_rows(M, K, seed):
@@ -912,7 +918,7 @@ def test_f32_activations_gemm_parity(mnb, prefill_rows, M, N, K, g, sdt, zp):
     a = G.to_dev(A)
     y = t.empty((M, N), dtype=t.float32, device="cuda")
     G.gemm(q, a, M, y)
-    expect = "gemm_small_m_f32act" if 2 * M <= 16 else "gemm_mfma_32x32x16_f32act"
+    expect = "gemm_small_m_f32act" if 2 * M <= 48 else "gemm_mfma_32x32x16_f32act"
     assert mnb.mnb_last_variant() == expect
     Y, B, W64 = G.oracle_dense(A, w)
     G.assert_within(G.host(y), Y, B, "fp32 activations M=%d N=%d K=%d g=%d" % (M, N, K, g))
