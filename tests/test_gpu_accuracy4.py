@@ -132,6 +132,7 @@ def test_accuracy4_special_rows(mnb):
     for m in range(A.shape[0]):
         _check(mnb, w, A[m:m + 1], bias, "accuracy4 special row %d (GEMV)" % m)
     _check(mnb, w, A, bias, "accuracy4 special rows (small-M GEMM)")
+    _check(mnb, w, np.tile(A, (13, 1))[:64], bias, "accuracy4 special rows (prefill GEMM)")
     big = np.concatenate([A] * 5)
     _check(mnb, w, big, bias, "accuracy4 special rows (prefill GEMM)")
 

@@ -798,7 +798,7 @@ def test_results_are_deterministic(mnb):
 
 def test_absent_zero_points_equal_explicit_eights(mnb):
     t = G.torch()
-    for (M, N, K, g) in ((1, 200, 512, 32), (4, 96, 1024, 64), (40, 64, 256, 128)):
+    for (M, N, K, g) in ((1, 200, 512, 32), (4, 96, 1024, 64), (40, 64, 256, 128), (64, 64, 256, 128)):
         w = _weight(N, K, g, zp=False)
         kb = K // g
         w8 = synth.Weight(N, K, g, w.packed, w.scales, np.full((N, (kb + 1) // 2), 0x88, np.uint8))
@@ -866,7 +866,7 @@ def test_zero_and_non_finite_scales(mnb, prefill_rows):
         s[9, 0] = np.nan
         w2 = synth.Weight(N, K, g, w.packed, s.astype(w.scales.dtype), w.zero_points)
         q = G.upload(w2)
-        for M in (1, 4, 40):
+        for M in (1, 4, 40, 64):
             A = _act(M, K, seed=M)
             y = t.empty((M, N), dtype=t.float16, device="cuda")
             G.gemm(q, G.to_dev(A), M, y)
