@@ -521,18 +521,20 @@ def test_prefill_at_maximum_k(mnb):
         G.assert_within(outs[bm][np.array(rows)[ms], ns], Y, B, "prefill (%d rows) at K=%d" % (bm, K))
 
 
-def test_small_m_at_maximum_k(mnb):
+@pytest.mark.parametrize("M", [16, 20])
+def test_small_m_at_maximum_k(mnb, M):
     """The small-M kernel at its largest K (2^25 = 262144 chunks): 16 rows of
-    fp16 A are 2^30 bytes, so the activation offsets reach 2^30.  One
-    workgroup (N = 16) runs every chunk.  Rows are sparse (_sparse_row); rows
-    0, 1, 7 and 15 are checked against the oracle on every column."""
+    fp16 A are 2^30 bytes, so the activation offsets reach 2^30; at M = 20 the
+    second 16-row slice starts 2^30 bytes into A.  One workgroup (N = 16) runs
+    every chunk.  Rows are sparse (_sparse_row); rows 0, 1, 7 and 15 (and 16
+    and 19 at M = 20) are checked against the oracle on every column."""
     t = G.torch()
-    M, N, g = 16, 16, 128
+    N, g = 16, 128
     K = 1 << 25
     w = _weight(N, K, g, "f16", True, seed=22, lo=0.002, hi=0.01)
     q = G.upload(w)
     a = t.empty((M, K), dtype=t.float16, device="cuda")
-    rows = [0, 1, 7, 15]
+    rows = [0, 1, 7, 15] + ([16, M - 1] if M > 16 else [])
     kept = {}
     for m in range(M):
         r = _sparse_row(K, (220, m))
