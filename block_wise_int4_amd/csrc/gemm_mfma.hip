@@ -303,29 +303,32 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
     // range, so they read zero.
     constexpr uint32_t kFar = 0x80000000u;
     uint32_t a_voff[A_DMA];
-#pragma unroll
-    for (int idx = 0; idx < A_DMA; ++idx) {
-        const int rw = 4 * idx + (lane >> 4);          // row among the wave's
-        const int r = ROWS_PER_WAVE * wave + rw;       // row in the tile
-        const int sg = (lane & 15) ^ (r & 15);         // logical segment at this slot
-        a_voff[idx] = ((uint32_t)rw * (uint32_t)K + 8u * (uint32_t)sg) * 2u;
-    }
     uint32_t s_voff[G::kScaleInstr], z_voff[G::kZpInstr > 0 ? G::kZpInstr : 1];
+    auto set_offsets = [&](int ln) __attribute__((always_inline)) {
 #pragma unroll
-    for (int m = 0; m < G::kScaleInstr; ++m) {
-        const int d = m * 64 + lane;
-        const int tt = d / G::kScaleDw, o = d % G::kScaleDw;
-        s_voff[m] = d < TPW * G::kScaleDw
-            ? (uint32_t)(wave * TPW + tt) * (uint32_t)C * (uint32_t)(G::kScaleDw * 4) + (uint32_t)o * 4u : kFar;
-    }
+        for (int idx = 0; idx < A_DMA; ++idx) {
+            const int rw = 4 * idx + (ln >> 4);            // row among the wave's
+            const int r = ROWS_PER_WAVE * wave + rw;       // row in the tile
+            const int sg = (ln & 15) ^ (r & 15);           // logical segment at this slot
+            a_voff[idx] = ((uint32_t)rw * (uint32_t)K + 8u * (uint32_t)sg) * 2u;
+        }
 #pragma unroll
-    for (int m = 0; m < G::kZpInstr; ++m) {
-        constexpr int ZD = G::kZpDw > 0 ? G::kZpDw : 1;
-        const int d = m * 64 + lane;
-        const int tt = d / ZD, o = d % ZD;
-        z_voff[m] = d < TPW * G::kZpDw
-            ? (uint32_t)(wave * TPW + tt) * (uint32_t)C * (uint32_t)(ZD * 4) + (uint32_t)o * 4u : kFar;
-    }
+        for (int m = 0; m < G::kScaleInstr; ++m) {
+            const int d = m * 64 + ln;
+            const int tt = d / G::kScaleDw, o = d % G::kScaleDw;
+            s_voff[m] = d < TPW * G::kScaleDw
+                ? (uint32_t)(wave * TPW + tt) * (uint32_t)C * (uint32_t)(G::kScaleDw * 4) + (uint32_t)o * 4u : kFar;
+        }
+#pragma unroll
+        for (int m = 0; m < G::kZpInstr; ++m) {
+            constexpr int ZD = G::kZpDw > 0 ? G::kZpDw : 1;
+            const int d = m * 64 + ln;
+            const int tt = d / ZD, o = d % ZD;
+            z_voff[m] = d < TPW * G::kZpDw
+                ? (uint32_t)(wave * TPW + tt) * (uint32_t)C * (uint32_t)(ZD * 4) + (uint32_t)o * 4u : kFar;
+        }
+    };
+    set_offsets(lane);
     auto issue_piece = [&](int c, int st, int idx) {
         if (idx < A_DMA) {
             // A rows [ROWS_PER_WAVE*wave + 4*idx, +4); a chunk reaching past K
@@ -571,6 +574,14 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
         wait_vm<0>();
         fallback_tile();
     } else {
+    // The DMA offsets once more, from an opaque copy of the lane: the
+    // prologue's copies then end with the prologue's DMAs instead of living
+    // across the fallback branch, which spilled them to scratch memory
+    {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        set_offsets(ln);
+    }
     read_meta(0, ratioA, zcA, true);
     load_afr(0, afr[0], 0);
     {
@@ -709,40 +720,38 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
             }
             return;
         }
-        // fp32 outputs: the row's activation scale, then the bias; the
-        // lane's row scales are loaded before any is used
-        float rs[RB][16];
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                int m = m0 + rb * 32 + 8 * (e >> 2) + 4 * oct + (e & 3);
-                m = m < p.M ? m : p.M - 1;
-                rs[rb][e] = p.row_scale[m];
-            }
-        float bq[PAIRS];
-#pragma unroll
-        for (int q = 0; q < PAIRS; ++q) {
-            const int n = nb * BN + wave * 64 + q * 32 + (lane & 31);
-            bq[q] = p.bias32 ? p.bias32[n < p.N ? n : p.N - 1] : 0.0f;
-        }
-        auto value = [&](int rb, int q, int e) __attribute__((always_inline)) {
-            float v = rs[rb][e] != 0.0f ? acc[rb][q][e] * rs[rb][e] : 0.0f;
-            if (p.bias32) v = v + bq[q];
+        // fp32 outputs: the accumulator times its row's activation scale (0
+        // where that scale is 0), then the bias.  Each row scale is loaded
+        // for the store of its row, so the lane's 64 row scales are never
+        // live beside its 128 accumulators (held all at once they spilled)
+        auto finish32 = [&](float a, float sc, float b) __attribute__((always_inline)) {
+            float v = sc != 0.0f ? a * sc : 0.0f;
+            if (p.bias32) v = v + b;
             return v;
         };
         if (p.vec_store) {
-            // as the fp16 output below, in two passes of 48 rows (the fp32
-            // block of a wave is twice the size); 288-byte rows put the two
-            // row quads of one write instruction in different banks.  With
-            // N % 4 == 0 a 16-byte segment is all inside or all outside.
-            constexpr int RS = 288, HALF = BM / 2;
+            // the raw accumulators staged as the fp16 output below, in two
+            // passes of BM/2 rows (the fp32 block of a wave is twice the
+            // size); 288-byte rows put the two row quads of one write
+            // instruction in different banks.  With N % 4 == 0 a 16-byte
+            // segment is all inside or all outside.  A lane then finishes
+            // and stores 4 columns of one row at a time.
+            constexpr int RS = 288, HALF = BM / 2, ROWS = HALF / 4;
             static_assert(WAVES * HALF * RS <= KernelLds<ST, Q, HAS_ZP, H>::kBytes, "half the fp32 block fits the LDS");
+            const int n = nb * BN + wave * 64 + (lane & 15) * 4;
+            float b4[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b4[j] = p.bias32 ? p.bias32[n + j < p.N ? n + j : p.N - 1] : 0.0f;
             block_sync_lds();   // every wave is past its last fragment reads
             unsigned char* ob = lds + wave * (HALF * RS);
-            const int n = nb * BN + wave * 64 + (lane & 15) * 4;
 #pragma unroll
             for (int hp = 0; hp < 2; ++hp) {
+                float rsv[ROWS];
+#pragma unroll
+                for (int i = 0; i < ROWS; ++i) {
+                    const int m = m0 + hp * HALF + (lane >> 4) + 4 * i;
+                    rsv[i] = p.row_scale[m < p.M ? m : p.M - 1];
+                }
                 // 8-row block rb*4 + e/4 of the wave's BM rows is in pass (rb*4 + e/4) / (HALF/8)
 #pragma unroll
                 for (int q = 0; q < PAIRS; ++q)
@@ -752,15 +761,17 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
                         for (int e = 0; e < 16; ++e) {
                             if ((rb * 4 + (e >> 2)) / (HALF / 8) != hp) continue;
                             const int row = rb * 32 + 8 * (e >> 2) + 4 * oct + (e & 3) - hp * HALF;
-                            *reinterpret_cast<float*>(ob + row * RS + (q * 32 + (lane & 31)) * 4) = value(rb, q, e);
+                            *reinterpret_cast<float*>(ob + row * RS + (q * 32 + (lane & 31)) * 4) = acc[rb][q][e];
                         }
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
-                for (int i = 0; i < HALF / 4; ++i) {
+                for (int i = 0; i < ROWS; ++i) {
                     const int row = (lane >> 4) + 4 * i;
                     const int m = m0 + hp * HALF + row;
-                    const u4_t v = *reinterpret_cast<const u4_t*>(ob + row * RS + (lane & 15) * 16);
-                    if (m < p.M && n < p.N) *reinterpret_cast<u4_t*>(p.y32 + (int64_t)m * p.N + n) = v;
+                    f4_t v = __builtin_bit_cast(f4_t, *reinterpret_cast<const u4_t*>(ob + row * RS + (lane & 15) * 16));
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) v[j] = finish32(v[j], rsv[i], b4[j]);
+                    if (m < p.M && n < p.N) *reinterpret_cast<u4_t*>(p.y32 + (int64_t)m * p.N + n) = __builtin_bit_cast(u4_t, v);
                 }
                 // the reads are done before the next pass writes
                 asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -771,12 +782,13 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
         for (int q = 0; q < PAIRS; ++q) {
             const int n = nb * BN + wave * 64 + q * 32 + (lane & 31);
             if (n >= p.N) continue;
+            const float bn = p.bias32 ? p.bias32[n] : 0.0f;
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
                     const int m = m0 + rb * 32 + 8 * (e >> 2) + 4 * oct + (e & 3);
-                    if (m < p.M) p.y32[(int64_t)m * p.N + n] = value(rb, q, e);
+                    if (m < p.M) p.y32[(int64_t)m * p.N + n] = finish32(acc[rb][q][e], p.row_scale[m], bn);
                 }
         }
         return;
