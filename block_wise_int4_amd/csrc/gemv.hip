@@ -563,7 +563,11 @@ __global__ __launch_bounds__(kMaxWaves * 64) void gemv_kernel(
 // Chunks per wave: when the tile's C chunks fit in one batch of at most
 // kMaxBatch per wave, the smallest batch size of {1, 2, 4} that covers them
 // (every load of the wave in flight before its first wait, one register set);
-// else the two-set loop with batches of 2 (16 waves) or 4 (8 waves).  Larger
+// else the two-set loop with batches of 2 (16 waves, or the fused pair) or 4
+// (a single weight on 8 waves).  The fused pair's two weights in batches of 4
+// outgrow the 128 registers the 16-wave launch bound leaves a wave and spill
+// inside the loop; in batches of 2 it is 9-13% faster (K = 5120, N = 13824
+// and K = 8192, N = 28672, same bits).  Larger
 // single batches (6 or 8 chunks in flight per wave) measured slower: the
 // loads finish sooner, but every chunk of a wave then lands near the end of
 // the stream and the unpack work runs after it instead of beside it.
@@ -590,9 +594,9 @@ hipError_t launch_b(const GemvParams& p, int waves, int64_t tiles, hipStream_t s
         launch_k<AT, ST, Q, HAS_ZP, FUSED, 2, PERM, false>(p, waves, tiles, s);
     else if (per_wave <= kMaxBatch)
         launch_k<AT, ST, Q, HAS_ZP, FUSED, kMaxBatch, PERM, false>(p, waves, tiles, s);
-    else if (waves > kMaxWaves / 2)
+    else if (waves > kMaxWaves / 2 || FUSED)
         launch_k<AT, ST, Q, HAS_ZP, FUSED, 2, PERM, true>(p, waves, tiles, s);
-    else
+    else if constexpr (!FUSED)
         launch_k<AT, ST, Q, HAS_ZP, FUSED, 4, PERM, true>(p, waves, tiles, s);
     return hipGetLastError();
 }

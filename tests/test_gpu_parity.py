@@ -233,7 +233,10 @@ def ctypes_byref(x):
 # ------------------------------------------------------- gate/up SwiGLU ----
 
 GATE_UP_CASES = [(11008, 4096, 128, "f16"), (4864, 896, 32, "f16"), (70, 384, 64, "f16"),
-                 (133, 512, 16, "f32")]
+                 (133, 512, 16, "f32"),
+                 # more than 512 tiles (8-wave workgroups) and more than 4
+                 # chunks per wave: the two-set loop of the fused pair
+                 (13824, 5120, 128, "f16"), (9000, 4608, 64, "f32")]
 
 
 @pytest.mark.parametrize("N,K,g,adt", GATE_UP_CASES)
