@@ -562,6 +562,9 @@ BIAS_CASES = [
     (1, 300, 512, 32, "f16", True), (1, 200, 640, 64, "f32", False),
     (4, 257, 896, 32, "f16", True), (40, 300, 512, 64, "f16", True),
     (130, 70, 384, 128, "f16", False),
+    # the prefill with N % 8 == 0: outputs staged in LDS and stored 16 bytes
+    # per lane, the bias read per output element (ragged M)
+    (130, 264, 384, 128, "f16", True), (75, 512, 640, 64, "f16", False),
 ]
 
 
