@@ -852,26 +852,73 @@ __global__ __launch_bounds__(WAVES * 64, kWgPerCu) void gemm_mfma_kernel(GemmPar
         return;
     }
     if (p.bias) {
-        // a per-row bias: all of the lane's bias elements are loaded before
-        // any is used (rows and columns outside the output read an element
-        // inside it)
-        __half bv[PAIRS][RB][16];
+        // a per-row bias.  With 16-byte stores the raw accumulators are
+        // staged in LDS as fp32, in two passes of BM/2 rows as for the fp32
+        // output, and a lane finishes 4 columns of one row at a time; a
+        // pass's bias elements are requested before its staging, so their
+        // latency hides behind it, and only that pass's 64 are live (all 128
+        // of a lane held at once spilled).  Rows and columns outside the
+        // output read an element inside it.  Otherwise each output element
+        // reads its own bias element.
+        if (p.vec_store) {
+            constexpr int RS = 288, HALF = BM / 2, ROWS = HALF / 4;
+            static_assert(WAVES * HALF * RS <= KernelLds<ST, Q, HAS_ZP, H>::kBytes, "half the fp32 block fits the LDS");
+            const int n = nb * BN + wave * 64 + (lane & 15) * 4;
+            const int nc = n < p.N ? n : p.N - 4;     // N % 8 == 0 here
+            block_sync_lds();   // every wave is past its last fragment reads
+            unsigned char* ob = lds + wave * (HALF * RS);
+#pragma unroll
+            for (int hp = 0; hp < 2; ++hp) {
+                __half bb[ROWS][4];
+#pragma unroll
+                for (int i = 0; i < ROWS; ++i) {
+                    int m = m0 + hp * HALF + (lane >> 4) + 4 * i;
+                    m = m < p.M ? m : p.M - 1;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) bb[i][j] = p.bias[(int64_t)m * p.bias_stride + nc + j];
+                }
+#pragma unroll
+                for (int q = 0; q < PAIRS; ++q)
+#pragma unroll
+                    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) {
+                            if ((rb * 4 + (e >> 2)) / (HALF / 8) != hp) continue;
+                            const int row = rb * 32 + 8 * (e >> 2) + 4 * oct + (e & 3) - hp * HALF;
+                            *reinterpret_cast<float*>(ob + row * RS + (q * 32 + (lane & 31)) * 4) = acc[rb][q][e];
+                        }
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+                for (int i = 0; i < ROWS; ++i) {
+                    const int row = (lane >> 4) + 4 * i;
+                    const int m = m0 + hp * HALF + row;
+                    const f4_t v = __builtin_bit_cast(f4_t, *reinterpret_cast<const u4_t*>(ob + row * RS + (lane & 15) * 16));
+                    uint32_t h[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        h[j] = __half_as_ushort(finish_value(v[j], __half2float(bb[i][j]), p.bias_after_round));
+                    if (m < p.M && n < p.N)
+                        *reinterpret_cast<uint2*>(p.y + (int64_t)m * p.N + n) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+                }
+                // the reads are done before the next pass writes
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            }
+            return;
+        }
 #pragma unroll
         for (int q = 0; q < PAIRS; ++q) {
-            int n = nb * BN + wave * 64 + q * 32 + (lane & 31);
-            n = n < p.N ? n : p.N - 1;
+            const int n = nb * BN + wave * 64 + q * 32 + (lane & 31);
+            if (n >= p.N) continue;
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    int m = m0 + rb * 32 + 8 * (e >> 2) + 4 * oct + (e & 3);
-                    m = m < p.M ? m : p.M - 1;
-                    bv[q][rb][e] = p.bias[(int64_t)m * p.bias_stride + n];
+                    const int m = m0 + rb * 32 + 8 * (e >> 2) + 4 * oct + (e & 3);
+                    if (m < p.M)
+                        p.y[(int64_t)m * p.N + n] = finish_value(
+                            acc[rb][q][e], __half2float(p.bias[(int64_t)m * p.bias_stride + n]), p.bias_after_round);
                 }
         }
-        store_f16([&](int rb, int q, int e) {
-            return finish_value(acc[rb][q][e], __half2float(bv[q][rb][e]), p.bias_after_round);
-        });
         return;
     }
     store_f16([&](int rb, int q, int e) { return __float2half_rn(acc[rb][q][e]); });
